@@ -1,0 +1,162 @@
+/* mpnn.h -- C ABI of the REANN-style message-passing interatomic potential on MI355X (gfx950).
+ *
+ * The library evaluates the energy and forces of the model described in "Efficient
+ * Parallelization of Message Passing Neural Network Potentials for Large-Scale Molecular
+ * Dynamics" (Xia & Jiang), section "REANN Architecture", Eq. 1 (embedded-atom density from
+ * Gaussian-type orbital sums), Eq. 2 (messages c^t from atomic networks) and Fig. 1, with
+ * forces from the reverse pass of section "Parallelization Algorithm", Eq. 3-5, on one GPU's
+ * subdomain: the local atoms plus a ghost shell of periodic images, refreshed per layer
+ * (Fig. 4a) and folded back to the owners in the reverse pass (Fig. 4b).
+ *
+ * Model (the readings this library implements):
+ *   R_k(d)  = exp(-(d - mu_k)^2 / (2 sigma^2))             k = 0..K-1
+ *   f_c(d)  = (1 + cos(pi d / rc)) / 2 for d < rc, else 0
+ *   A_m(r)  = (x/rc)^lx (y/rc)^ly (z/rc)^lz, lx+ly+lz = l <= L, ordered by l, then lx
+ *             descending, then ly descending; w_m = l! / (lx! ly! lz!)
+ *   O_i[k,m] = sum_{j in N_c(i)} c_j[k] R_k(d_ij) f_c(d_ij) A_m(r_ij),  r_ij = r_j - r_i
+ *   rho_i[(a,b),l] = sum_{|m|=l} w_m O_i[a,m] O_i[b,m], 0 <= a <= b < K, index
+ *             l*K(K+1)/2 + (row-major rank of (a,b) in the upper triangle)
+ *   c^0_i = C0[species_i]; c^{t+1}_i = MLP^t_{s_i}(rho^t_i / s_t) for t < T-1;
+ *   E_i = e_scale * MLP^{T-1}_{s_i}(rho^{T-1}_i / s_{T-1}); E = sum_i E_i (fp64)
+ *   MLP(x) = W3 silu(W2 silu(W1 x + b1) + b2) + b3, silu(x) = x / (1 + exp(-x))
+ *   F_i = -dE/dr_i.
+ *
+ * Units: A, eV, fs, amu.  Arithmetic: positions, velocities and forces fp64; edge basis,
+ * aggregation and networks fp32 (matrix cores); energy accumulated in fp64.
+ *
+ * Conventions for every call:
+ *   - Array arguments are DEVICE pointers (e.g. torch tensors on the same GPU), read or
+ *     written on the context's stream; scalars and `box` are host values.
+ *   - The caller owns every array it passes; the library never frees caller memory.  The
+ *     context owns its device scratch (hipMalloc) and releases it in mpnn_destroy.
+ *   - Atom arrays are in the caller's order; the library keeps its own locality (cell) order
+ *     internally and converts on the way in and out.
+ *   - Every call returns mpnn_status; on error mpnn_last_error() describes it and the
+ *     context stays usable (a failed build leaves no neighbour list).
+ *   - One context must not be used from two threads at once.  Results are deterministic:
+ *     no floating-point atomics are used anywhere.
+ */
+#ifndef MPNN_H
+#define MPNN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mpnn_ctx mpnn_ctx;
+
+typedef enum {
+    MPNN_OK = 0,
+    MPNN_E_INVALID_ARG = -1, /* null pointer, bad size, unsupported (K, L, H) combination */
+    MPNN_E_OOM = -2,         /* device allocation failed */
+    MPNN_E_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    MPNN_E_CAPACITY = -4,    /* more than 2^31-1 neighbour entries or nodes */
+    MPNN_E_SKIN = -5,        /* positions moved more than skin/2 and auto-rebuild is off */
+    MPNN_E_NONFINITE = -6,   /* non-finite position or energy */
+    MPNN_E_STATE = -7,       /* call order (e.g. energy before mpnn_build_neighbors) */
+    MPNN_E_BOX = -8          /* box edge not larger than rc + skin */
+} mpnn_status;
+
+/* Model parameters, all host arrays, copied by mpnn_create (the caller keeps ownership).
+ * Supported shapes: (K, L) in {(2,1), (4,2), (8,2), (12,3)}, hidden in {64, 128},
+ * 1 <= T <= 8, 1 <= n_species <= 16. */
+typedef struct {
+    int32_t n_species;
+    int32_t K;                  /* radial primitives (N_phi in the paper) */
+    int32_t L;                  /* maximum angular momentum */
+    int32_t T;                  /* message-passing layers */
+    int32_t hidden;             /* width H of both hidden layers */
+    int32_t reserved;           /* must be 0 */
+    double rc;                  /* cutoff radius, A */
+    double sigma;               /* Gaussian standard deviation, A */
+    const double *mu;           /* [K] radial centres, A */
+    const double *c0;           /* [n_species][K] layer-0 orbital coefficients */
+    const double *mlp;          /* for t in 0..T-1, for s in 0..S-1: W1[H][D], b1[H], W2[H][H],
+                                   b2[H], W3[out][H], b3[out]; out = K for t < T-1, 1 for t = T-1;
+                                   D = K(K+1)(L+1)/2 */
+    const double *layer_scale;  /* [T] s_t */
+    double e_scale;
+    const double *mass;         /* [n_species] amu */
+} mpnn_params;
+
+typedef struct {
+    double epot;                /* potential energy after the last step, eV */
+    double ekin;                /* kinetic energy, eV */
+    double temp;                /* 2 ekin / ((3N-3) kB), K */
+    int64_t rebuilds;           /* neighbour-list rebuilds during the call */
+    double max_disp;            /* largest displacement since a build seen in the call, A */
+    int64_t steps;              /* total steps taken by this context */
+} mpnn_md_stats;
+
+typedef struct {
+    int64_t n_local;            /* atoms */
+    int64_t n_ghost;            /* periodic-image ghosts in the shell of width rc + skin */
+    int64_t n_edges;            /* Verlet-list entries (d < rc + skin), receivers local */
+    int64_t cells[3];           /* interior cells per axis (side >= rc + skin) */
+    int64_t bytes_device;       /* device memory held by the context */
+} mpnn_info;
+
+/* Validates and copies the parameters, uploads the weights in the matrix-core layout.
+ * No kernel runs.  *out receives the context (NULL on error). */
+mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out);
+void mpnn_destroy(mpnn_ctx *ctx);
+
+/* Stream for every later call (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream);
+ * NULL selects the null stream. */
+mpnn_status mpnn_set_stream(mpnn_ctx *ctx, void *hip_stream);
+
+/* Neighbour build for n atoms at `pos` ([n][3] fp64, device) with species `types` ([n] int32,
+ * device) in the orthorhombic periodic box `box` (host, A).  Wraps positions into the box,
+ * orders atoms by a Morton curve over cells of side >= rc + skin, builds the periodic-image
+ * ghost shell of width rc + skin (paper: local and ghost atoms, Fig. 3a), the receiver-major
+ * Verlet list of every pair with d^2 < (rc + skin)^2 evaluated in fp64 as
+ * (dx*dx + dy*dy) + dz*dz, its sender-major transpose, and the per-species atom groups.
+ * rc must equal the model's rc.  Velocities are reset to zero (see mpnn_set_state).
+ * Errors: E_INVALID_ARG, E_BOX (box edge <= rc + skin), E_CAPACITY, E_OOM, E_HIP. */
+mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t *types,
+                                 int64_t n, const double box[3], double rc, double skin);
+
+/* Energy and forces.  pos: NULL uses the context's current positions; otherwise new positions
+ * ([n][3] fp64, device, caller order) replace them (if any atom moved more than skin/2 from
+ * the last build the list is rebuilt first).  energy: host out (eV) or NULL; forces: device
+ * out [n][3] fp64 (eV/A, caller order) or NULL; atom_energy: device out [n] fp64 or NULL.
+ * Synchronizes the stream when `energy` is requested. */
+mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
+                               double *atom_energy);
+
+/* n_steps velocity-Verlet steps of dt_fs (NVE).  The list is rebuilt every rebuild_every steps
+ * (0: never by count) and whenever an atom has moved more than skin/2 since the last build.
+ * stats: host out or NULL. */
+mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t rebuild_every,
+                         mpnn_md_stats *stats);
+
+/* Replace positions and/or velocities ([n][3] fp64, device, caller order; either may be NULL).
+ * New positions trigger a rebuild. */
+mpnn_status mpnn_set_state(mpnn_ctx *ctx, const double *pos, const double *vel);
+
+/* Current positions/velocities ([n][3] fp64 device out, caller order; either may be NULL) and
+ * the step counter (host out or NULL). */
+mpnn_status mpnn_get_state(mpnn_ctx *ctx, double *pos, double *vel, int64_t *step);
+
+/* The Verlet list as canonical tuples in caller ids: receiver i, sender j and image shift S
+ * (r_ij = r_j + S*box - r_i for the wrapped positions of the last build).  Device outputs
+ * i[cap], j[cap], shift[cap][3] (int32); *n_pairs (host) receives the total count; at most cap
+ * entries are written. */
+mpnn_status mpnn_get_pairs(mpnn_ctx *ctx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j,
+                           int32_t *shift);
+
+/* Per-atom intermediates of the last evaluation, fp64 device out in caller order:
+ * which = 0: c^t [n][K]; 1: O^t [n][K*M]; 2: dE/dO^t [n][K*M]; 3: E_i [n] (t ignored). */
+mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, double *out);
+
+mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info);
+
+/* Text of the last error on this context ("" if none); valid until the next call. */
+const char *mpnn_last_error(const mpnn_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPNN_H */

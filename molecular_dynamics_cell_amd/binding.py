@@ -1,0 +1,196 @@
+"""Thin ctypes binding of libmpnn.so (include/mpnn.h).  Argument marshalling only: every step of
+the energy/force/MD path runs in the library's HIP kernels.  torch supplies device memory and
+the stream.  There is no fallback: if the library is missing, calls raise."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import torch
+
+from . import inputs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmpnn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mpnn.h")
+
+STATUS = {0: "MPNN_OK", -1: "MPNN_E_INVALID_ARG", -2: "MPNN_E_OOM", -3: "MPNN_E_HIP",
+          -4: "MPNN_E_CAPACITY", -5: "MPNN_E_SKIN", -6: "MPNN_E_NONFINITE", -7: "MPNN_E_STATE",
+          -8: "MPNN_E_BOX"}
+
+
+class MPNNError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Params(C.Structure):
+    _fields_ = [("n_species", C.c_int32), ("K", C.c_int32), ("L", C.c_int32), ("T", C.c_int32),
+                ("hidden", C.c_int32), ("reserved", C.c_int32), ("rc", C.c_double),
+                ("sigma", C.c_double), ("mu", C.POINTER(C.c_double)), ("c0", C.POINTER(C.c_double)),
+                ("mlp", C.POINTER(C.c_double)), ("layer_scale", C.POINTER(C.c_double)),
+                ("e_scale", C.c_double), ("mass", C.POINTER(C.c_double))]
+
+
+class MDStats(C.Structure):
+    _fields_ = [("epot", C.c_double), ("ekin", C.c_double), ("temp", C.c_double),
+                ("rebuilds", C.c_int64), ("max_disp", C.c_double), ("steps", C.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class Info(C.Structure):
+    _fields_ = [("n_local", C.c_int64), ("n_ghost", C.c_int64), ("n_edges", C.c_int64),
+                ("cells", C.c_int64 * 3), ("bytes_device", C.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmpnn.so (torch is imported first so one HIP runtime serves both)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m molecular_dynamics_cell_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64, d = C.c_void_p, C.c_int32, C.c_int64, C.c_double
+        st = C.c_int
+        sig = {
+            "mpnn_create": ([C.POINTER(_Params), C.POINTER(p)], st),
+            "mpnn_destroy": ([p], None),
+            "mpnn_set_stream": ([p, p], st),
+            "mpnn_build_neighbors": ([p, p, p, i64, C.POINTER(C.c_double), d, d], st),
+            "mpnn_energy_forces": ([p, p, C.POINTER(C.c_double), p, p], st),
+            "mpnn_md_step": ([p, d, i32, i32, C.POINTER(MDStats)], st),
+            "mpnn_set_state": ([p, p, p], st),
+            "mpnn_get_state": ([p, p, p, C.POINTER(C.c_int64)], st),
+            "mpnn_get_pairs": ([p, i64, C.POINTER(C.c_int64), p, p, p], st),
+            "mpnn_get_intermediate": ([p, i32, i32, p], st),
+            "mpnn_get_info": ([p, C.POINTER(Info)], st),
+            "mpnn_last_error": ([p], C.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/mpnn.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mpnn_[a-z_]+)\s*\(", text)))
+
+
+def _dptr(t: torch.Tensor):
+    return C.c_void_p(t.data_ptr()) if t is not None else None
+
+
+class MPNN:
+    """One library context: model parameters plus one system's neighbour list and state."""
+
+    def __init__(self, params: inputs.Params, device="cuda"):
+        self.params = params
+        self.device = torch.device(device)
+        s = params.spec
+        self.T, self.K, self.L = s.T, s.K, s.L
+        self.M = (s.L + 1) * (s.L + 2) * (s.L + 3) // 6
+        self._keep = [np.ascontiguousarray(a, np.float64) for a in
+                      (params.mu, params.c0, params.packed_mlp(), params.layer_scale, params.masses)]
+        dp = C.POINTER(C.c_double)
+        mu, c0, mlp, sc, ms = (a.ctypes.data_as(dp) for a in self._keep)
+        self._p = _Params(s.n_species, s.K, s.L, s.T, s.H, 0, s.rc, s.sigma, mu, c0, mlp, sc,
+                          float(params.e_scale), ms)
+        h = C.c_void_p()
+        self._check(lib().mpnn_create(C.byref(self._p), C.byref(h)), None)
+        self.h = h
+        self.n = 0
+        self.set_stream(torch.cuda.current_stream(self.device))
+
+    def _check(self, code, h="self"):
+        if code != 0:
+            hh = self.h if h == "self" else h
+            msg = lib().mpnn_last_error(hh).decode() if hh else ""
+            raise MPNNError(code, msg)
+
+    def close(self):
+        if getattr(self, "h", None):
+            lib().mpnn_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_stream(self, stream: torch.cuda.Stream):
+        self._check(lib().mpnn_set_stream(self.h, C.c_void_p(stream.cuda_stream)))
+
+    def build_neighbors(self, pos: torch.Tensor, types: torch.Tensor, box, rc=None, skin=None):
+        pos = pos.to(self.device, torch.float64).contiguous()
+        types = types.to(self.device, torch.int32).contiguous()
+        b = (C.c_double * 3)(*[float(x) for x in box])
+        rc = self.params.spec.rc if rc is None else rc
+        skin = self.params.spec.skin if skin is None else skin
+        self.n = pos.shape[0]
+        self._check(lib().mpnn_build_neighbors(self.h, _dptr(pos), _dptr(types), self.n, b,
+                                               float(rc), float(skin)))
+
+    def energy_forces(self, pos: torch.Tensor = None, forces=True, atom_energy=False, energy=True):
+        F = torch.empty((self.n, 3), dtype=torch.float64, device=self.device) if forces else None
+        Ei = torch.empty(self.n, dtype=torch.float64, device=self.device) if atom_energy else None
+        E = C.c_double(0.0)
+        if pos is not None:
+            pos = pos.to(self.device, torch.float64).contiguous()
+        self._check(lib().mpnn_energy_forces(self.h, _dptr(pos), C.byref(E) if energy else None,
+                                             _dptr(F), _dptr(Ei)))
+        return E.value if energy else None, F, Ei
+
+    def md_step(self, dt, n_steps, rebuild_every=0, stats=True):
+        st = MDStats()
+        self._check(lib().mpnn_md_step(self.h, float(dt), int(n_steps), int(rebuild_every),
+                                       C.byref(st) if stats else None))
+        return st.as_dict() if stats else None
+
+    def set_state(self, pos=None, vel=None):
+        pos = pos.to(self.device, torch.float64).contiguous() if pos is not None else None
+        vel = vel.to(self.device, torch.float64).contiguous() if vel is not None else None
+        self._check(lib().mpnn_set_state(self.h, _dptr(pos), _dptr(vel)))
+
+    def get_state(self):
+        pos = torch.empty((self.n, 3), dtype=torch.float64, device=self.device)
+        vel = torch.empty((self.n, 3), dtype=torch.float64, device=self.device)
+        step = C.c_int64(0)
+        self._check(lib().mpnn_get_state(self.h, _dptr(pos), _dptr(vel), C.byref(step)))
+        return pos, vel, step.value
+
+    def get_pairs(self):
+        cnt = C.c_int64(0)
+        self._check(lib().mpnn_get_pairs(self.h, 0, C.byref(cnt), None, None, None))
+        n = cnt.value
+        i = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)
+        j = torch.empty(max(n, 1), dtype=torch.int32, device=self.device)
+        s = torch.empty((max(n, 1), 3), dtype=torch.int32, device=self.device)
+        self._check(lib().mpnn_get_pairs(self.h, n, C.byref(cnt), _dptr(i), _dptr(j), _dptr(s)))
+        return i[:n], j[:n], s[:n]
+
+    def get_intermediate(self, which: int, t: int = 0):
+        width = {0: self.K, 1: self.K * self.M, 2: self.K * self.M, 3: 1}[which]
+        out = torch.empty((self.n, width), dtype=torch.float64, device=self.device)
+        self._check(lib().mpnn_get_intermediate(self.h, int(which), int(t), _dptr(out)))
+        return out
+
+    def info(self):
+        inf = Info()
+        self._check(lib().mpnn_get_info(self.h, C.byref(inf)))
+        return dict(n_local=inf.n_local, n_ghost=inf.n_ghost, n_edges=inf.n_edges,
+                    cells=list(inf.cells), bytes_device=inf.bytes_device)

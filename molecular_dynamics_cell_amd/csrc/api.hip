@@ -1,0 +1,378 @@
+// C ABI entry points (include/mpnn.h): validation, buffer management and the call sequence
+// of one energy/force evaluation and of the velocity-Verlet loop.
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "impl.h"
+
+struct mpnn_ctx {
+    mpnn::Context cx;
+};
+
+namespace mpnn {
+
+Status Context::grow(Buf &b, size_t bytes) {
+    if (bytes == 0) bytes = 16;
+    if (b.bytes >= bytes) return Status::ok();
+    if (b.p) {
+        MPNN_HIP(hipStreamSynchronize(stream));
+        release(b);
+    }
+    size_t want = bytes + bytes / 8;
+    void *p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) {
+        (void)hipGetLastError();
+        return Status::err(MPNN_E_OOM, "hipMalloc of " + std::to_string(want) + " bytes failed");
+    }
+    b.p = p;
+    b.bytes = want;
+    device_bytes += want;
+    return Status::ok();
+}
+
+Status Context::grow_keep(Buf &b, size_t bytes, size_t keep) {
+    if (b.bytes >= bytes) return Status::ok();
+    Buf nb;
+    MPNN_TRY(grow(nb, bytes));
+    if (b.p && keep) MPNN_HIP(hipMemcpyAsync(nb.p, b.p, keep < b.bytes ? keep : b.bytes, hipMemcpyDeviceToDevice, stream));
+    MPNN_HIP(hipStreamSynchronize(stream));
+    release(b);
+    b = nb;
+    return Status::ok();
+}
+
+void Context::release(Buf &b) {
+    if (b.p) {
+        (void)hipFree(b.p);
+        device_bytes -= b.bytes;
+    }
+    b.p = nullptr;
+    b.bytes = 0;
+}
+
+Context::~Context() {
+    if (stream) (void)hipStreamSynchronize(stream);
+    Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
+                  &ghost_off, &row_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &GO, &Gc,
+                  &gedge, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c, &tmp_d, &tmp_scan,
+                  &types_caller, &stage_pos, &stage_vel};
+    for (Buf *b : all) release(*b);
+}
+
+namespace {
+
+bool supported(int K, int L, int H) {
+    const bool kl = (K == 8 && L == 2) || (K == 12 && L == 3) || (K == 2 && L == 1) || (K == 4 && L == 2);
+    return kl && (H == 64 || H == 128);
+}
+
+// One energy/force evaluation on the current (sorted) state: paper Eq. 1-2 forward with the
+// per-layer ghost refresh, then Eq. 3-5 backward with the ghost->owner folds.
+Status evaluate(Context &cx, double *F_caller) {
+    MPNN_TRY(refresh_ghost_positions(cx));
+    for (int t = 0; t < cx.T; ++t) {
+        MPNN_TRY(aggregate(cx, t));
+        if (t < cx.T - 1) {
+            MPNN_TRY(mlp_forward(cx, t));
+            MPNN_TRY(refresh_ghost_features(cx, t + 1));
+        } else {
+            MPNN_TRY(mlp_energy(cx));
+        }
+    }
+    for (int t = cx.T - 1; t >= 1; --t) {
+        MPNN_TRY(backward_messages(cx, t));
+        MPNN_TRY(mlp_backward(cx, t - 1));
+    }
+    MPNN_TRY(force_edges(cx));
+    MPNN_TRY(force_gather(cx, F_caller));
+    cx.forces_valid = true;
+    return Status::ok();
+}
+
+// Rebuild from the context's own state (positions and velocities carried over).
+Status rebuild_from_state(Context &cx) {
+    const int64_t n1 = cx.n > 0 ? cx.n : 1;
+    MPNN_TRY(cx.grow(cx.stage_pos, sizeof(double) * 3 * n1));
+    MPNN_TRY(cx.grow(cx.stage_vel, sizeof(double) * 3 * n1));
+    MPNN_TRY(unpermute_vec3(cx, cx.pos.as<double>(), cx.stage_pos.as<double>()));
+    MPNN_TRY(unpermute_vec3(cx, cx.vel.as<double>(), cx.stage_vel.as<double>()));
+    double box[3] = {cx.box[0], cx.box[1], cx.box[2]};
+    return build_neighbors(cx, cx.stage_pos.as<double>(), cx.types_caller.as<int32_t>(), cx.n, box, cx.skin,
+                           cx.stage_vel.as<double>());
+}
+
+mpnn_status finish(mpnn_ctx *ctx, const Status &s) {
+    if (ctx) ctx->cx.last_error = s.msg;
+    return s.code;
+}
+
+}  // namespace
+}  // namespace mpnn
+
+using mpnn::Status;
+
+extern "C" {
+
+mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
+    if (!out) return MPNN_E_INVALID_ARG;
+    *out = nullptr;
+    if (!p || !p->mu || !p->c0 || !p->mlp || !p->layer_scale || !p->mass) return MPNN_E_INVALID_ARG;
+    if (p->reserved != 0 || p->n_species < 1 || p->n_species > 16 || p->T < 1 || p->T > 8 ||
+        !mpnn::supported(p->K, p->L, p->hidden) || !(p->rc > 0) || !(p->sigma > 0))
+        return MPNN_E_INVALID_ARG;
+    for (int t = 0; t < p->T; ++t)
+        if (!(p->layer_scale[t] > 0) || !std::isfinite(p->layer_scale[t])) return MPNN_E_INVALID_ARG;
+    mpnn_ctx *ctx = new (std::nothrow) mpnn_ctx;
+    if (!ctx) return MPNN_E_OOM;
+    mpnn::Context &cx = ctx->cx;
+    cx.S = p->n_species; cx.K = p->K; cx.L = p->L; cx.T = p->T; cx.H = p->hidden;
+    cx.M = mpnn::n_mono(cx.L);
+    cx.D = mpnn::n_feat(cx.K, cx.L);
+    cx.DP = (cx.D + 15) / 16 * 16;
+    cx.rc = p->rc; cx.sigma = p->sigma; cx.e_scale = p->e_scale;
+    cx.mass.assign(p->mass, p->mass + cx.S);
+    cx.inv_scale_host.resize(cx.T);
+    for (int t = 0; t < cx.T; ++t) cx.inv_scale_host[t] = (float)(1.0 / p->layer_scale[t]);
+    mpnn::ModelDev md{};
+    for (int k = 0; k < cx.K; ++k) md.mu[k] = (float)p->mu[k];
+    for (int s = 0; s < cx.S; ++s) {
+        for (int k = 0; k < cx.K; ++k) md.c0[s * cx.K + k] = (float)p->c0[s * cx.K + k];
+        md.mass[s] = p->mass[s];
+        if (!(p->mass[s] > 0)) {
+            delete ctx;
+            return MPNN_E_INVALID_ARG;
+        }
+    }
+    for (int t = 0; t < cx.T; ++t) md.inv_scale[t] = cx.inv_scale_host[t];
+    md.e_scale = (float)p->e_scale;
+    md.neg_half_inv_s2 = (float)(-1.0 / (2.0 * p->sigma * p->sigma));
+    md.inv_s2 = (float)(1.0 / (p->sigma * p->sigma));
+    md.rc = (float)p->rc;
+    md.inv_rc = (float)(1.0 / p->rc);
+    md.pi_over_rc = (float)(mpnn::kPi / p->rc);
+    md.rc2 = p->rc * p->rc;
+    Status s = cx.grow(cx.model, sizeof md);
+    if (!s.bad()) {
+        if (hipMemcpy(cx.model.p, &md, sizeof md, hipMemcpyHostToDevice) != hipSuccess)
+            s = Status::err(MPNN_E_HIP, "upload of model constants failed");
+    }
+    if (!s.bad()) s = mpnn::pack_weights(cx, p->mlp);
+    if (s.bad()) {
+        delete ctx;
+        return s.code;
+    }
+    *out = ctx;
+    return MPNN_OK;
+}
+
+void mpnn_destroy(mpnn_ctx *ctx) { delete ctx; }
+
+mpnn_status mpnn_set_stream(mpnn_ctx *ctx, void *hip_stream) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    ctx->cx.stream = static_cast<hipStream_t>(hip_stream);
+    return mpnn::finish(ctx, Status::ok());
+}
+
+mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t *types, int64_t n,
+                                 const double box[3], double rc, double skin) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (n < 0 || !box || (n > 0 && (!pos || !types)) || !(skin >= 0) || !std::isfinite(skin))
+        return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "bad arguments"));
+    if (!(std::fabs(rc - cx.rc) <= 1e-12 * cx.rc))
+        return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "rc differs from the model's cutoff"));
+    if (n > INT32_MAX) return mpnn::finish(ctx, Status::err(MPNN_E_CAPACITY, "too many atoms"));
+    for (int a = 0; a < 3; ++a)
+        if (!std::isfinite(box[a])) return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "bad box"));
+    Status s = cx.grow(cx.types_caller, sizeof(int32_t) * (n > 0 ? n : 1));
+    if (!s.bad() && n > 0) {
+        if (hipMemcpyAsync(cx.types_caller.p, types, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, cx.stream) !=
+            hipSuccess)
+            s = Status::err(MPNN_E_HIP, "copy of types failed");
+    }
+    if (!s.bad()) s = mpnn::build_neighbors(cx, pos, types, n, box, skin, nullptr);
+    return mpnn::finish(ctx, s);
+}
+
+static Status load_positions(mpnn::Context &cx, const double *pos) {
+    // new caller-order positions: rebuild if any atom left the skin, else keep the list
+    const int64_t n1 = cx.n > 0 ? cx.n : 1;
+    MPNN_TRY(cx.grow(cx.stage_pos, sizeof(double) * 3 * n1));
+    MPNN_HIP(hipMemcpyAsync(cx.stage_pos.p, pos, sizeof(double) * 3 * cx.n, hipMemcpyDeviceToDevice, cx.stream));
+    MPNN_TRY(mpnn::permute_in_vec3(cx, cx.stage_pos.as<double>(), cx.pos.as<double>()));
+    MPNN_TRY(mpnn::reset_skin_flag(cx));
+    MPNN_TRY(mpnn::skin_check(cx));
+    bool ex = false;
+    double md = 0;
+    MPNN_TRY(mpnn::read_skin_flag(cx, &ex, &md));
+    if (ex) MPNN_TRY(mpnn::rebuild_from_state(cx));
+    cx.forces_valid = false;
+    return Status::ok();
+}
+
+mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
+                               double *atom_energy) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
+    Status s;
+    if (pos) s = load_positions(cx, pos);
+    if (!s.bad()) s = mpnn::evaluate(cx, forces);
+    if (!s.bad() && atom_energy) s = mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, cx.n, atom_energy);
+    if (!s.bad() && energy) {
+        s = mpnn::energy_sum(cx, energy);
+        if (!s.bad() && !std::isfinite(*energy)) s = Status::err(MPNN_E_NONFINITE, "non-finite energy");
+    }
+    return mpnn::finish(ctx, s);
+}
+
+mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t rebuild_every,
+                         mpnn_md_stats *stats) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
+    if (n_steps < 0 || rebuild_every < 0 || !std::isfinite(dt_fs))
+        return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "bad arguments"));
+    auto run = [&]() -> Status {
+        int64_t rebuilds = 0;
+        double max_disp = 0.0;
+        if (!cx.forces_valid) MPNN_TRY(mpnn::evaluate(cx, nullptr));
+        MPNN_TRY(mpnn::reset_skin_flag(cx));
+        for (int32_t s = 0; s < n_steps; ++s) {
+            MPNN_TRY(mpnn::kick_drift(cx, dt_fs));
+            ++cx.since_build;
+            bool need = rebuild_every > 0 && cx.since_build >= rebuild_every;
+            bool ex = false;
+            double md = 0.0;
+            MPNN_TRY(mpnn::read_skin_flag(cx, &ex, &md));
+            max_disp = md > max_disp ? md : max_disp;
+            if (need || ex) {
+                MPNN_TRY(mpnn::rebuild_from_state(cx));
+                MPNN_TRY(mpnn::reset_skin_flag(cx));
+                ++rebuilds;
+            }
+            MPNN_TRY(mpnn::evaluate(cx, nullptr));
+            MPNN_TRY(mpnn::kick(cx, dt_fs));
+            ++cx.step;
+        }
+        if (stats) {
+            double ep = 0, ke = 0;
+            MPNN_TRY(mpnn::energy_sum(cx, &ep));
+            MPNN_TRY(mpnn::kinetic_energy(cx, &ke));
+            stats->epot = ep;
+            stats->ekin = ke;
+            stats->temp = cx.n > 1 ? 2.0 * ke / ((3.0 * cx.n - 3.0) * mpnn::kBoltzmann) : 0.0;
+            stats->rebuilds = rebuilds;
+            stats->max_disp = max_disp;
+            stats->steps = cx.step;
+        } else {
+            MPNN_HIP(hipStreamSynchronize(cx.stream));
+        }
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
+}
+
+mpnn_status mpnn_set_state(mpnn_ctx *ctx, const double *pos, const double *vel) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
+    auto run = [&]() -> Status {
+        if (pos) {
+            const int64_t n1 = cx.n > 0 ? cx.n : 1;
+            MPNN_TRY(cx.grow(cx.stage_pos, sizeof(double) * 3 * n1));
+            MPNN_TRY(cx.grow(cx.stage_vel, sizeof(double) * 3 * n1));
+            if (cx.n > 0) {
+                MPNN_HIP(hipMemcpyAsync(cx.stage_pos.p, pos, sizeof(double) * 3 * cx.n, hipMemcpyDeviceToDevice,
+                                        cx.stream));
+                if (vel)
+                    MPNN_HIP(hipMemcpyAsync(cx.stage_vel.p, vel, sizeof(double) * 3 * cx.n,
+                                            hipMemcpyDeviceToDevice, cx.stream));
+                else
+                    MPNN_TRY(mpnn::unpermute_vec3(cx, cx.vel.as<double>(), cx.stage_vel.as<double>()));
+            }
+            double box[3] = {cx.box[0], cx.box[1], cx.box[2]};
+            MPNN_TRY(mpnn::build_neighbors(cx, cx.stage_pos.as<double>(), cx.types_caller.as<int32_t>(), cx.n, box,
+                                           cx.skin, cx.stage_vel.as<double>()));
+        } else if (vel) {
+            MPNN_TRY(mpnn::permute_in_vec3(cx, vel, cx.vel.as<double>()));
+        }
+        MPNN_HIP(hipStreamSynchronize(cx.stream));
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
+}
+
+mpnn_status mpnn_get_state(mpnn_ctx *ctx, double *pos, double *vel, int64_t *step) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
+    auto run = [&]() -> Status {
+        if (pos) MPNN_TRY(mpnn::unpermute_vec3(cx, cx.pos.as<double>(), pos));
+        if (vel) MPNN_TRY(mpnn::unpermute_vec3(cx, cx.vel.as<double>(), vel));
+        if (step) *step = cx.step;
+        MPNN_HIP(hipStreamSynchronize(cx.stream));
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
+}
+
+mpnn_status mpnn_get_pairs(mpnn_ctx *ctx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j,
+                           int32_t *shift) {
+    if (!ctx || !n_pairs) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
+    if (cap > 0 && (!i || !j || !shift)) return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "null output"));
+    auto run = [&]() -> Status {
+        MPNN_TRY(mpnn::get_pairs(cx, cap, n_pairs, i, j, shift));
+        MPNN_HIP(hipStreamSynchronize(cx.stream));
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
+}
+
+mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, double *out) {
+    if (!ctx || !out) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built || !cx.forces_valid) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "no evaluation yet"));
+    if (which != 3 && (t < 0 || t >= cx.T)) return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "bad layer"));
+    const int KM = cx.K * cx.M;
+    auto run = [&]() -> Status {
+        switch (which) {
+            case 0:
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.c.as<float>() + (int64_t)t * cx.NN * cx.K, cx.K, cx.n, out));
+                break;
+            case 1:
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.O.as<float>() + (int64_t)t * cx.n * KM, KM, cx.n, out));
+                break;
+            case 2:
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.GO.as<float>() + (int64_t)t * cx.n * KM, KM, cx.n, out));
+                break;
+            case 3:
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, cx.n, out));
+                break;
+            default:
+                return Status::err(MPNN_E_INVALID_ARG, "bad selector");
+        }
+        MPNN_HIP(hipStreamSynchronize(cx.stream));
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
+}
+
+mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info) {
+    if (!ctx || !info) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    info->n_local = cx.n;
+    info->n_ghost = cx.G;
+    info->n_edges = cx.E;
+    for (int a = 0; a < 3; ++a) info->cells[a] = cx.nc[a];
+    info->bytes_device = (int64_t)cx.device_bytes;
+    return mpnn::finish(ctx, Status::ok());
+}
+
+const char *mpnn_last_error(const mpnn_ctx *ctx) { return ctx ? ctx->cx.last_error.c_str() : "null context"; }
+
+}  // extern "C"

@@ -1,0 +1,149 @@
+// Host-side context of the MPNN library and the launchers each translation unit provides.
+#pragma once
+
+#include <string>
+#include <vector>
+
+#include "../../include/mpnn.h"
+#include "common.h"
+
+namespace mpnn {
+
+struct Status {
+    mpnn_status code = MPNN_OK;
+    std::string msg;
+    static Status ok() { return Status(); }
+    static Status err(mpnn_status c, std::string m) {
+        Status s;
+        s.code = c;
+        s.msg = std::move(m);
+        return s;
+    }
+    bool bad() const { return code != MPNN_OK; }
+};
+
+#define MPNN_HIP(call)                                                                      \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return ::mpnn::Status::err(MPNN_E_HIP, std::string(#call) + ": " +              \
+                                                       hipGetErrorString(e_));              \
+    } while (0)
+
+#define MPNN_TRY(expr)                                                                      \
+    do {                                                                                    \
+        ::mpnn::Status s_ = (expr);                                                         \
+        if (s_.bad()) return s_;                                                            \
+    } while (0)
+
+// A growable device allocation.
+struct Buf {
+    void *p = nullptr;
+    size_t bytes = 0;
+    template <class T> T *as() const { return static_cast<T *>(p); }
+};
+
+// Packed per-(layer, species) network block, all float, offsets in floats.  Matrices are in
+// the matrix-core A-operand order (see mlp.hip): W1 [H][DP], W2 [H][H], W3 [16][H],
+// W1t [DP][H], W2t [H][H], W3t [H][16], then biases b1 [H], b2 [H], b3 [16].
+struct NetLayout {
+    size_t W1, W2, W3, W1t, W2t, W3t, b1, b2, b3, stride;
+};
+
+struct Context {
+    // ---- model ----
+    int S = 0, K = 0, L = 0, T = 0, H = 0, M = 0, D = 0, DP = 0;
+    double rc = 0, sigma = 0, e_scale = 0;
+    std::vector<double> mass;
+    NetLayout net{};
+    Buf weights;        // float, T*S blocks of net.stride
+    Buf model;          // ModelDev
+    hipStream_t stream = nullptr;
+
+    // ---- system ----
+    bool built = false;
+    bool forces_valid = false;  // F_sorted matches the current positions
+    int64_t n = 0, G = 0, NN = 0, E = 0;
+    double box[3] = {0, 0, 0};
+    double skin = 0, rcut = 0;
+    int nc[3] = {0, 0, 0};      // interior cells per axis
+    double hcell[3] = {0, 0, 0};
+    int64_t step = 0;
+    int since_build = 0;
+    std::vector<int64_t> sp_count;  // atoms per species (host copy)
+
+    // per-atom / per-node state (sorted, locals first then ghosts)
+    Buf perm, inv_perm;             // int32 [n]: sorted -> caller, caller -> sorted
+    Buf pos;                        // double [NN][3]
+    Buf vel;                        // double [n][3]
+    Buf ref;                        // double [n][3], positions at the last build
+    Buf types;                      // int32 [NN]
+    Buf ghost_owner, ghost_code;    // int32 [G]
+    Buf ghost_off;                  // int64 [n+1] ghosts of each owner
+    Buf row_off, nbr;               // int64 [n+1], int32 [E]
+    Buf t_off, t_recv, t_eid;       // int64 [NN+1], int32 [E], int32 [E]
+    Buf sp_list, sp_off;            // int32 [n], int64 [S+1]
+
+    // per-evaluation buffers
+    Buf c;        // float [T][NN][K]
+    Buf O;        // float [T][n][K*M]
+    Buf GO;       // float [T][n][K*M]
+    Buf Gc;       // float [NN][K]
+    Buf gedge;    // float [E][3]
+    Buf Frecv;    // double [n][3]
+    Buf F;        // double [n][3] (sorted)
+    Buf Ei;       // float [n]
+    Buf red;      // double scratch for reductions
+    Buf flag;     // uint64 [4]: displacement flag, max displacement bits
+    Buf tmp_a, tmp_b, tmp_c, tmp_d, tmp_scan;  // build scratch
+
+    std::string last_error;
+    size_t device_bytes = 0;
+
+    Buf types_caller;             // int32 [n] species in caller order (for rebuilds)
+    Buf stage_pos, stage_vel;     // double [n][3] caller-order staging
+    std::vector<float> inv_scale_host;  // 1 / s_t
+
+    Status grow(Buf &b, size_t bytes);
+    Status grow_keep(Buf &b, size_t bytes, size_t keep);
+    void release(Buf &b);
+    ~Context();
+};
+
+// ---- scan.hip ----
+// out[0..n] = exclusive prefix sum of in[0..n-1] (int32), out[n] = total.  int64 output.
+Status exclusive_scan(Context &cx, const int32_t *in, int64_t n, int64_t *out);
+
+// ---- neighbors.hip ----
+Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *types_caller,
+                       int64_t n, const double box[3], double skin, const double *vel_caller);
+Status refresh_ghost_positions(Context &cx);
+Status get_pairs(Context &cx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j, int32_t *s);
+
+// ---- edges.hip ----
+Status aggregate(Context &cx, int t);
+Status refresh_ghost_features(Context &cx, int t);
+Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold
+Status force_edges(Context &cx);                  // dE/dr_e over all layers, receiver sums
+Status force_gather(Context &cx, double *F_caller);
+
+// ---- mlp.hip ----
+Status mlp_forward(Context &cx, int t);           // c^{t+1} from O^t (t < T-1)
+Status mlp_energy(Context &cx);                   // E_i and dE/dO^{T-1}
+Status mlp_backward(Context &cx, int t);          // dE/dO^t from dE/dc^{t+1}
+Status pack_weights(Context &cx, const double *mlp);
+
+// ---- integrate.hip ----
+Status energy_sum(Context &cx, double *E_host);
+Status kick_drift(Context &cx, double dt);       // first half-kick + drift + skin test
+Status kick(Context &cx, double dt);             // second half-kick
+Status skin_check(Context &cx);                  // displacement test only
+Status kinetic_energy(Context &cx, double *ke_host);
+Status read_skin_flag(Context &cx, bool *exceeded, double *max_disp);
+Status reset_skin_flag(Context &cx);
+Status unpermute_vec3(Context &cx, const double *sorted, double *caller);
+Status permute_in_vec3(Context &cx, const double *caller, double *sorted);
+Status unpermute_float(Context &cx, const float *sorted, int width, int64_t stride_rows,
+                       double *caller);
+
+}  // namespace mpnn

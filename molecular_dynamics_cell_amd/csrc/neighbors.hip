@@ -1,0 +1,558 @@
+// Neighbour build for one GPU's subdomain (paper, section "Parallelization Algorithm",
+// Fig. 3a: each process holds its local atoms (LAs) with full neighbour lists plus ghost atoms
+// (GAs) inside the cutoff of its LAs; Fig. 2: one list, built once, is reused by all T layers).
+// On one GPU the subdomain is the whole periodic box and the ghost shell is made of periodic
+// images within rc + skin of the box (a Verlet skin lets the list live for several steps).
+//
+// Pipeline (all on the device; the host reads three counts to size arrays):
+//   wrap + cell key -> counting sort by Morton cell code (ties by caller id) -> sorted state
+//   -> ghost images per owner (count / scan / fill) -> bin all nodes on the extended grid
+//   -> receiver rows (count / scan / fill over the 27-cell stencil, fp64 distance test)
+//   -> sender-major transpose (count / scan / fill / per-segment sort by edge id)
+//   -> per-species atom lists for the atomic networks.
+#include "impl.h"
+
+namespace mpnn {
+
+namespace {
+
+__device__ __forceinline__ uint32_t spread3(uint32_t v) {  // 10 bits -> every third bit
+    v &= 0x3ffu;
+    v = (v | (v << 16)) & 0x030000ffu;
+    v = (v | (v << 8)) & 0x0300f00fu;
+    v = (v | (v << 4)) & 0x030c30c3u;
+    v = (v | (v << 2)) & 0x09249249u;
+    return v;
+}
+
+struct Grid {
+    double L[3], h[3];
+    int n[3];
+    int morton;  // 1: Morton code of the interior cell, 0: linear index
+};
+
+__device__ __forceinline__ double wrap1(double r, double L) {
+    double f = floor(__ddiv_rn(r, L));
+    return __dsub_rn(r, __dmul_rn(L, f));
+}
+
+__device__ __forceinline__ int interior_cell(double x, double h, int n) {
+    int c = (int)floor(__ddiv_rn(x, h));
+    return c < 0 ? 0 : (c >= n ? n - 1 : c);
+}
+
+__global__ void k_wrap_key(int64_t n, const double *__restrict__ pos_in, Grid g,
+                           double *__restrict__ pos_w, int32_t *__restrict__ key) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int c[3];
+    for (int a = 0; a < 3; ++a) {
+        double x = wrap1(pos_in[3 * i + a], g.L[a]);
+        pos_w[3 * i + a] = x;
+        c[a] = interior_cell(x, g.h[a], g.n[a]);
+    }
+    key[i] = g.morton ? (int32_t)(spread3(c[0]) << 2 | spread3(c[1]) << 1 | spread3(c[2]))
+                      : (int32_t)((c[0] * g.n[1] + c[1]) * g.n[2] + c[2]);
+}
+
+__global__ void k_count(int64_t n, const int32_t *__restrict__ key, int32_t *__restrict__ cnt) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) atomicAdd(&cnt[key[i]], 1);
+}
+
+__global__ void k_scatter(int64_t n, const int32_t *__restrict__ key, const int64_t *__restrict__ off,
+                          int32_t *__restrict__ cursor, int32_t *__restrict__ out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        int32_t k = key[i];
+        out[off[k] + atomicAdd(&cursor[k], 1)] = (int32_t)i;
+    }
+}
+
+// Each segment (one key) sorted ascending, which makes the scatter order-independent.
+__global__ void k_sort_segments(int64_t nseg, const int64_t *__restrict__ off, int32_t *__restrict__ v) {
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nseg) return;
+    int64_t b = off[s], e = off[s + 1];
+    for (int64_t p = b + 1; p < e; ++p) {
+        int32_t x = v[p];
+        int64_t q = p - 1;
+        while (q >= b && v[q] > x) {
+            v[q + 1] = v[q];
+            --q;
+        }
+        v[q + 1] = x;
+    }
+}
+
+// Same, carrying a payload along with the key.
+__global__ void k_sort_segments_kv(int64_t nseg, const int64_t *__restrict__ off,
+                                   int32_t *__restrict__ k, int32_t *__restrict__ v) {
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nseg) return;
+    int64_t b = off[s], e = off[s + 1];
+    for (int64_t p = b + 1; p < e; ++p) {
+        int32_t x = k[p], y = v[p];
+        int64_t q = p - 1;
+        while (q >= b && k[q] > x) {
+            k[q + 1] = k[q];
+            v[q + 1] = v[q];
+            --q;
+        }
+        k[q + 1] = x;
+        v[q + 1] = y;
+    }
+}
+
+__global__ void k_gather_sorted(int64_t n, const int32_t *__restrict__ perm,
+                                const double *__restrict__ pos_w, const int32_t *__restrict__ types_in,
+                                const double *__restrict__ vel_in, double *__restrict__ pos,
+                                double *__restrict__ ref, int32_t *__restrict__ types,
+                                double *__restrict__ vel, int32_t *__restrict__ inv_perm) {
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= n) return;
+    int32_t c = perm[s];
+    inv_perm[c] = (int32_t)s;
+    types[s] = types_in[c];
+    for (int a = 0; a < 3; ++a) {
+        double x = pos_w[3 * (int64_t)c + a];
+        pos[3 * s + a] = x;
+        ref[3 * s + a] = x;
+        vel[3 * s + a] = vel_in ? vel_in[3 * (int64_t)c + a] : 0.0;
+    }
+}
+
+// An image x + s*L (s = -1, 0, 1 per axis) belongs to the ghost shell when every component
+// lies in [-w, L + w).
+__device__ __forceinline__ bool in_shell(const double *x, int code, const double *L, double w) {
+    int s[3];
+    shift_of(code, s[0], s[1], s[2]);
+    for (int a = 0; a < 3; ++a) {
+        double y = __dadd_rn(x[a], (double)s[a] * L[a]);
+        if (!(y >= -w && y < L[a] + w)) return false;
+    }
+    return true;
+}
+
+__global__ void k_ghost_count(int64_t n, const double *__restrict__ pos, Grid g, double w,
+                              int32_t *__restrict__ cnt) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    int c = 0;
+    for (int code = 0; code < 27; ++code)
+        if (code != 13 && in_shell(x, code, g.L, w)) ++c;
+    cnt[i] = c;
+}
+
+__global__ void k_ghost_fill(int64_t n, const double *__restrict__ pos, Grid g, double w,
+                             const int64_t *__restrict__ off, int32_t *__restrict__ owner,
+                             int32_t *__restrict__ code_out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    int64_t o = off[i];
+    for (int code = 0; code < 27; ++code)
+        if (code != 13 && in_shell(x, code, g.L, w)) {
+            owner[o] = (int32_t)i;
+            code_out[o] = code;
+            ++o;
+        }
+}
+
+// Ghost g = image of its owner: position owner + s*L (exactly as in the distance test).
+__global__ void k_ghost_pos(int64_t G, int64_t n, const int32_t *__restrict__ owner,
+                            const int32_t *__restrict__ code, Grid g, double *__restrict__ pos,
+                            int32_t *__restrict__ types) {
+    int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= G) return;
+    int32_t o = owner[k];
+    int s[3];
+    shift_of(code[k], s[0], s[1], s[2]);
+    for (int a = 0; a < 3; ++a) pos[3 * (n + k) + a] = __dadd_rn(pos[3 * (int64_t)o + a], (double)s[a] * g.L[a]);
+    if (types) types[n + k] = types[o];
+}
+
+__device__ __forceinline__ int ext_cell(double x, double h, int n) {
+    int c = (int)floor(__ddiv_rn(x, h)) + 1;
+    return c < 0 ? 0 : (c > n + 1 ? n + 1 : c);
+}
+
+__global__ void k_ext_key(int64_t NN, const double *__restrict__ pos, Grid g, int32_t *__restrict__ key) {
+    int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= NN) return;
+    int cx = ext_cell(pos[3 * v], g.h[0], g.n[0]);
+    int cy = ext_cell(pos[3 * v + 1], g.h[1], g.n[1]);
+    int cz = ext_cell(pos[3 * v + 2], g.h[2], g.n[2]);
+    key[v] = (int32_t)((cx * (g.n[1] + 2) + cy) * (g.n[2] + 2) + cz);
+}
+
+// Receiver rows: every node v != i of the 27 extended cells around local atom i with
+// (dx*dx + dy*dy) + dz*dz < rcut^2 in fp64.  Cells in fixed (dx, dy, dz) order, nodes of a cell
+// in ascending id, so rows are deterministic.
+template <bool FILL>
+__global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
+                       const int64_t *__restrict__ coff, const int32_t *__restrict__ cnodes,
+                       double rcut2, int32_t *__restrict__ cnt, const int64_t *__restrict__ row_off,
+                       int32_t *__restrict__ nbr) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const int cx = ext_cell(xi, g.h[0], g.n[0]);
+    const int cy = ext_cell(yi, g.h[1], g.n[1]);
+    const int cz = ext_cell(zi, g.h[2], g.n[2]);
+    const int ny = g.n[1] + 2, nz = g.n[2] + 2;
+    int64_t o = FILL ? row_off[i] : 0;
+    int32_t c = 0;
+    for (int dx = -1; dx <= 1; ++dx) {
+        int x = cx + dx;
+        if (x < 0 || x > g.n[0] + 1) continue;
+        for (int dy = -1; dy <= 1; ++dy) {
+            int y = cy + dy;
+            if (y < 0 || y > g.n[1] + 1) continue;
+            for (int dz = -1; dz <= 1; ++dz) {
+                int z = cz + dz;
+                if (z < 0 || z > g.n[2] + 1) continue;
+                int64_t cell = ((int64_t)x * ny + y) * nz + z;
+                for (int64_t p = coff[cell]; p < coff[cell + 1]; ++p) {
+                    int32_t v = cnodes[p];
+                    if (v == (int32_t)i) continue;
+                    double d2 = d2_exact(__dsub_rn(pos[3 * (int64_t)v], xi),
+                                         __dsub_rn(pos[3 * (int64_t)v + 1], yi),
+                                         __dsub_rn(pos[3 * (int64_t)v + 2], zi));
+                    if (d2 < rcut2) {
+                        if (FILL) nbr[o++] = v;
+                        else ++c;
+                    }
+                }
+            }
+        }
+    }
+    if (!FILL) cnt[i] = c;
+}
+
+__global__ void k_tcount(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
+                         int32_t *__restrict__ cnt) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) atomicAdd(&cnt[nbr[e]], 1);
+}
+
+__global__ void k_tfill(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
+                        const int64_t *__restrict__ t_off, int32_t *__restrict__ cursor,
+                        int32_t *__restrict__ t_eid) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) {
+        int32_t v = nbr[e];
+        t_eid[t_off[v] + atomicAdd(&cursor[v], 1)] = (int32_t)e;
+    }
+}
+
+// Receiver of every edge (rows are contiguous).
+__global__ void k_edge_receiver(int64_t n, const int64_t *__restrict__ row_off, int32_t *__restrict__ recv) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) recv[e] = (int32_t)i;
+}
+
+__global__ void k_tmap_recv(int64_t E, const int32_t *__restrict__ t_eid, const int32_t *__restrict__ recv_of_edge,
+                            int32_t *__restrict__ t_recv) {
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < E) t_recv[s] = recv_of_edge[t_eid[s]];
+}
+
+__global__ void k_flag_species(int64_t n, const int32_t *__restrict__ types, int s, int32_t *__restrict__ f) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) f[i] = types[i] == s;
+}
+
+__global__ void k_species_scatter(int64_t n, const int32_t *__restrict__ types, int s,
+                                  const int64_t *__restrict__ rank, int64_t base, int32_t *__restrict__ list) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n && types[i] == s) list[base + rank[i]] = (int32_t)i;
+}
+
+__global__ void k_c0(int64_t NN, int K, const int32_t *__restrict__ types, const ModelDev *__restrict__ md,
+                     float *__restrict__ c) {
+    int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= NN) return;
+    int s = types[v];
+    for (int k = 0; k < K; ++k) c[v * K + k] = md->c0[s * K + k];
+}
+
+__global__ void k_validate(int64_t n, const double *__restrict__ p, const int32_t *__restrict__ types, int S,
+                           int32_t *__restrict__ bad) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 3 * n && !isfinite(p[i])) atomicOr(bad, 1);
+    if (i < n && (types[i] < 0 || types[i] >= S)) atomicOr(bad, 2);
+}
+
+__global__ void k_pairs(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
+                        const int32_t *__restrict__ perm, const int32_t *__restrict__ ghost_owner,
+                        const int32_t *__restrict__ ghost_code, int64_t cap, int32_t *__restrict__ pi,
+                        int32_t *__restrict__ pj, int32_t *__restrict__ ps) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    for (int64_t e = row_off[i]; e < row_off[i + 1] && e < cap; ++e) {
+        int32_t v = nbr[e];
+        int sx = 0, sy = 0, sz = 0;
+        int32_t o = v;
+        if (v >= n) {
+            o = ghost_owner[v - n];
+            shift_of(ghost_code[v - n], sx, sy, sz);
+        }
+        pi[e] = perm[i];
+        pj[e] = perm[o];
+        ps[3 * e] = sx; ps[3 * e + 1] = sy; ps[3 * e + 2] = sz;
+    }
+}
+
+Grid make_grid(const Context &cx) {
+    Grid g;
+    for (int a = 0; a < 3; ++a) {
+        g.L[a] = cx.box[a];
+        g.h[a] = cx.hcell[a];
+        g.n[a] = cx.nc[a];
+    }
+    int mx = cx.nc[0] > cx.nc[1] ? cx.nc[0] : cx.nc[1];
+    mx = mx > cx.nc[2] ? mx : cx.nc[2];
+    int bits = 0;
+    while ((1 << bits) < mx) ++bits;
+    int64_t cells = (int64_t)cx.nc[0] * cx.nc[1] * cx.nc[2];
+    g.morton = bits <= 10 && ((int64_t)1 << (3 * bits)) <= 8 * cells;
+    return g;
+}
+
+int64_t key_range(const Grid &g) {
+    if (!g.morton) return (int64_t)g.n[0] * g.n[1] * g.n[2];
+    int mx = g.n[0] > g.n[1] ? g.n[0] : g.n[1];
+    mx = mx > g.n[2] ? mx : g.n[2];
+    int bits = 0;
+    while ((1 << bits) < mx) ++bits;
+    return (int64_t)1 << (3 * bits);
+}
+
+template <class T>
+Status fetch(Context &cx, const T *dev, T *host) {
+    MPNN_HIP(hipMemcpyAsync(host, dev, sizeof(T), hipMemcpyDeviceToHost, cx.stream));
+    MPNN_HIP(hipStreamSynchronize(cx.stream));
+    return Status::ok();
+}
+
+// Counting sort of `n` items by key in [0, nkeys): out_off [nkeys+1] offsets, out_items the
+// item ids ordered by (key, id).
+Status counting_sort(Context &cx, const int32_t *key, int64_t n, int64_t nkeys, int64_t *out_off,
+                     int32_t *out_items, int32_t *cnt_scratch) {
+    MPNN_HIP(hipMemsetAsync(cnt_scratch, 0, sizeof(int32_t) * (size_t)nkeys, cx.stream));
+    k_count<<<grid_for(n), kBlock, 0, cx.stream>>>(n, key, cnt_scratch);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(exclusive_scan(cx, cnt_scratch, nkeys, out_off));
+    MPNN_HIP(hipMemsetAsync(cnt_scratch, 0, sizeof(int32_t) * (size_t)nkeys, cx.stream));
+    k_scatter<<<grid_for(n), kBlock, 0, cx.stream>>>(n, key, out_off, cnt_scratch, out_items);
+    MPNN_HIP(hipGetLastError());
+    k_sort_segments<<<grid_for(nkeys), kBlock, 0, cx.stream>>>(nkeys, out_off, out_items);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+}  // namespace
+
+Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *types_caller, int64_t n,
+                       const double box[3], double skin, const double *vel_caller) {
+    cx.built = false;
+    cx.forces_valid = false;
+    const double w = cx.rc + skin;
+    for (int a = 0; a < 3; ++a) {
+        if (!(box[a] > w)) return Status::err(MPNN_E_BOX, "box edge must exceed rc + skin");
+        int c = (int)floor(box[a] / (w + 1e-8));
+        if (c < 1) return Status::err(MPNN_E_BOX, "box edge must exceed rc + skin");
+        cx.nc[a] = c;
+        cx.hcell[a] = box[a] / c;
+        cx.box[a] = box[a];
+    }
+    cx.skin = skin;
+    cx.rcut = w;
+    cx.n = n;
+    const Grid g = make_grid(cx);
+    const int64_t nkeys = key_range(g);
+    const int64_t next = (int64_t)(cx.nc[0] + 2) * (cx.nc[1] + 2) * (cx.nc[2] + 2);
+    const int64_t n1 = n > 0 ? n : 1;
+
+    // ---- wrap, Morton order, sorted state ----
+    MPNN_TRY(cx.grow(cx.tmp_a, sizeof(double) * 3 * n1));            // wrapped caller-order pos
+    MPNN_TRY(cx.grow(cx.tmp_b, sizeof(int32_t) * (size_t)(n1 > next ? n1 : next) * 2));
+    MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)(nkeys > next ? nkeys : next) + 64));
+    MPNN_TRY(cx.grow(cx.tmp_d, sizeof(int64_t) * (size_t)((nkeys > next ? nkeys : next) + 1)));
+    double *pos_w = cx.tmp_a.as<double>();
+    int32_t *key = cx.tmp_b.as<int32_t>();
+    int32_t *cnt = cx.tmp_c.as<int32_t>();
+    int64_t *off = cx.tmp_d.as<int64_t>();
+    MPNN_TRY(cx.grow(cx.perm, sizeof(int32_t) * n1));
+    MPNN_TRY(cx.grow(cx.inv_perm, sizeof(int32_t) * n1));
+    MPNN_TRY(cx.grow(cx.vel, sizeof(double) * 3 * n1));
+    MPNN_TRY(cx.grow(cx.ref, sizeof(double) * 3 * n1));
+    MPNN_TRY(cx.grow(cx.flag, sizeof(uint64_t) * 4));
+    if (n > 0) {
+        MPNN_HIP(hipMemsetAsync(cx.flag.p, 0, sizeof(int32_t), cx.stream));
+        k_validate<<<grid_for(3 * n), kBlock, 0, cx.stream>>>(n, pos_caller, types_caller, cx.S,
+                                                              cx.flag.as<int32_t>());
+        MPNN_HIP(hipGetLastError());
+        int32_t bad = 0;
+        MPNN_TRY(fetch(cx, cx.flag.as<int32_t>(), &bad));
+        if (bad & 1) return Status::err(MPNN_E_NONFINITE, "non-finite position");
+        if (bad & 2) return Status::err(MPNN_E_INVALID_ARG, "species index out of range");
+    }
+    k_wrap_key<<<grid_for(n), kBlock, 0, cx.stream>>>(n, pos_caller, g, pos_w, key);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(counting_sort(cx, key, n, nkeys, off, cx.perm.as<int32_t>(), cnt));
+
+    // sorted positions go straight into the node array; ghosts are appended later
+    MPNN_TRY(cx.grow(cx.types, sizeof(int32_t) * n1));
+    MPNN_TRY(cx.grow(cx.pos, sizeof(double) * 3 * n1));
+    k_gather_sorted<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.perm.as<int32_t>(), pos_w, types_caller,
+                                                           vel_caller, cx.pos.as<double>(), cx.ref.as<double>(),
+                                                           cx.types.as<int32_t>(), cx.vel.as<double>(),
+                                                           cx.inv_perm.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+
+    // ---- ghost shell: images within rc + skin of the box (margin 1e-9 A) ----
+    const double wg = w + 1e-9;
+    MPNN_TRY(cx.grow(cx.ghost_off, sizeof(int64_t) * (n1 + 1)));
+    k_ghost_count<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, wg, key);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(exclusive_scan(cx, key, n, cx.ghost_off.as<int64_t>()));
+    int64_t G = 0;
+    MPNN_TRY(fetch(cx, cx.ghost_off.as<int64_t>() + n, &G));
+    if (n + G > INT32_MAX) return Status::err(MPNN_E_CAPACITY, "too many nodes");
+    cx.G = G;
+    cx.NN = n + G;
+    const int64_t NN1 = cx.NN > 0 ? cx.NN : 1;
+    MPNN_TRY(cx.grow(cx.ghost_owner, sizeof(int32_t) * (G > 0 ? G : 1)));
+    MPNN_TRY(cx.grow(cx.ghost_code, sizeof(int32_t) * (G > 0 ? G : 1)));
+    {
+        // keep sorted local state while the node arrays grow
+        MPNN_TRY(cx.grow_keep(cx.pos, sizeof(double) * 3 * NN1, sizeof(double) * 3 * n1));
+        MPNN_TRY(cx.grow_keep(cx.types, sizeof(int32_t) * NN1, sizeof(int32_t) * n1));
+    }
+    k_ghost_fill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, wg, cx.ghost_off.as<int64_t>(),
+                                                        cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+    k_ghost_pos<<<grid_for(G), kBlock, 0, cx.stream>>>(G, n, cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>(),
+                                                       g, cx.pos.as<double>(), cx.types.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+
+    // ---- bin every node on the extended grid (one cell layer of ghosts per side) ----
+    MPNN_TRY(cx.grow(cx.tmp_b, sizeof(int32_t) * (size_t)(NN1 > next ? NN1 : next) * 2));
+    key = cx.tmp_b.as<int32_t>();
+    int32_t *cnodes = key + (NN1 > next ? NN1 : next);
+    k_ext_key<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.pos.as<double>(), g, key);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(counting_sort(cx, key, cx.NN, next, off, cnodes, cnt));
+
+    // ---- receiver rows ----
+    const double rcut2 = w * w;
+    MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)(n1 > next ? n1 : next) + 64));
+    cnt = cx.tmp_c.as<int32_t>();
+    MPNN_TRY(cx.grow(cx.row_off, sizeof(int64_t) * (n1 + 1)));
+    k_rows<false><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, cnt,
+                                                         nullptr, nullptr);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(exclusive_scan(cx, cnt, n, cx.row_off.as<int64_t>()));
+    int64_t E = 0;
+    MPNN_TRY(fetch(cx, cx.row_off.as<int64_t>() + n, &E));
+    if (E > INT32_MAX) return Status::err(MPNN_E_CAPACITY, "more than 2^31-1 neighbour entries");
+    cx.E = E;
+    const int64_t E1 = E > 0 ? E : 1;
+    MPNN_TRY(cx.grow(cx.nbr, sizeof(int32_t) * E1));
+    k_rows<true><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, nullptr,
+                                                        cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+
+    // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
+    MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
+    MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)NN1 + 64));
+    cnt = cx.tmp_c.as<int32_t>();
+    MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
+    k_tcount<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(), cnt);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(exclusive_scan(cx, cnt, cx.NN, cx.t_off.as<int64_t>()));
+    MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
+    k_tfill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(),
+                                                   cx.t_off.as<int64_t>(), cnt, cx.t_eid.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+    k_sort_segments<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+    {
+        // receiver of each edge, then of each transposed entry (reuses the gradient buffer)
+        MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
+        int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p);
+        k_edge_receiver<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), recv);
+        MPNN_HIP(hipGetLastError());
+        k_tmap_recv<<<grid_for(E), kBlock, 0, cx.stream>>>(E, cx.t_eid.as<int32_t>(), recv, cx.t_recv.as<int32_t>());
+        MPNN_HIP(hipGetLastError());
+    }
+
+    // ---- atoms grouped by species (ascending sorted index within a species) ----
+    MPNN_TRY(cx.grow(cx.sp_list, sizeof(int32_t) * n1));
+    MPNN_TRY(cx.grow(cx.sp_off, sizeof(int64_t) * (cx.S + 1)));
+    cx.sp_count.assign(cx.S, 0);
+    std::vector<int64_t> sp_off(cx.S + 1, 0);
+    MPNN_TRY(cx.grow(cx.tmp_d, sizeof(int64_t) * (size_t)(n1 + 1)));
+    int64_t *rank = cx.tmp_d.as<int64_t>();
+    for (int s = 0; s < cx.S; ++s) {
+        k_flag_species<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.types.as<int32_t>(), s, cnt);
+        MPNN_HIP(hipGetLastError());
+        MPNN_TRY(exclusive_scan(cx, cnt, n, rank));
+        int64_t cs = 0;
+        MPNN_TRY(fetch(cx, rank + n, &cs));
+        k_species_scatter<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.types.as<int32_t>(), s, rank, sp_off[s],
+                                                                 cx.sp_list.as<int32_t>());
+        MPNN_HIP(hipGetLastError());
+        cx.sp_count[s] = cs;
+        sp_off[s + 1] = sp_off[s] + cs;
+    }
+    MPNN_HIP(hipMemcpyAsync(cx.sp_off.p, sp_off.data(), sizeof(int64_t) * (cx.S + 1), hipMemcpyHostToDevice,
+                            cx.stream));
+
+    // ---- per-evaluation buffers and layer-0 messages ----
+    const int KM = cx.K * cx.M;
+    MPNN_TRY(cx.grow(cx.c, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * n1 * KM));
+    MPNN_TRY(cx.grow(cx.GO, sizeof(float) * (size_t)cx.T * n1 * KM));
+    MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.Frecv, sizeof(double) * 3 * n1));
+    MPNN_TRY(cx.grow(cx.F, sizeof(double) * 3 * n1));
+    MPNN_TRY(cx.grow(cx.Ei, sizeof(float) * n1));
+    k_c0<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.K, cx.types.as<int32_t>(), cx.model.as<ModelDev>(),
+                                                    cx.c.as<float>());
+    MPNN_HIP(hipGetLastError());
+    MPNN_HIP(hipStreamSynchronize(cx.stream));
+    cx.built = true;
+    cx.since_build = 0;
+    return Status::ok();
+}
+
+Status refresh_ghost_positions(Context &cx) {
+    if (cx.G == 0) return Status::ok();
+    const Grid g = make_grid(cx);
+    k_ghost_pos<<<grid_for(cx.G), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.ghost_owner.as<int32_t>(),
+                                                           cx.ghost_code.as<int32_t>(), g, cx.pos.as<double>(),
+                                                           nullptr);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status get_pairs(Context &cx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j, int32_t *s) {
+    *n_pairs = cx.E;
+    if (cap <= 0 || cx.E == 0) return Status::ok();
+    k_pairs<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(),
+                                                      cx.perm.as<int32_t>(), cx.ghost_owner.as<int32_t>(),
+                                                      cx.ghost_code.as<int32_t>(), cap, i, j, s);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+}  // namespace mpnn

@@ -305,26 +305,35 @@ def model_spec(cfg: int) -> ModelSpec:
                      skin=c["skin"])
 
 
+def _f32(a):
+    """Round to the nearest float32 value (kept as float64)."""
+    return np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
+
+
 def random_params(spec: ModelSpec, seed: int, masses, layer_scale=None, e_scale: float = 1.0) -> Params:
     """Random-init weights: W, b ~ N(0, 1/fan_in); C0 ~ N(0, 1).  Draw order: C0, then for
-    t in 0..T-1, for s in 0..S-1: W1, b1, W2, b2, W3, b3."""
+    t in 0..T-1, for s in 0..S-1: W1, b1, W2, b2, W3, b3.
+
+    Every drawn value (and every radial centre) is rounded to the nearest float32, so an fp32
+    implementation holds exactly the same parameters as an fp64 one; the frozen layer and energy
+    scales are powers of two for the same reason."""
     rng = _rng(seed)
     K, L, T, H, S = spec.K, spec.L, spec.T, spec.H, spec.n_species
     D = K * (K + 1) * (L + 1) // 2
-    mu = np.array([k * spec.rc / (K - 1) for k in range(K)]) if K > 1 else np.zeros(1)
-    c0 = rng.standard_normal((S, K))
+    mu = _f32([k * spec.rc / (K - 1) for k in range(K)]) if K > 1 else np.zeros(1)
+    c0 = _f32(rng.standard_normal((S, K)))
     mlp = []
     for t in range(T):
         out = K if t < T - 1 else 1
         per_s = []
         for _s in range(S):
             w = {}
-            w["W1"] = rng.standard_normal((H, D)) / np.sqrt(D)
-            w["b1"] = rng.standard_normal(H) / np.sqrt(D)
-            w["W2"] = rng.standard_normal((H, H)) / np.sqrt(H)
-            w["b2"] = rng.standard_normal(H) / np.sqrt(H)
-            w["W3"] = rng.standard_normal((out, H)) / np.sqrt(H)
-            w["b3"] = rng.standard_normal(out) / np.sqrt(H)
+            w["W1"] = _f32(rng.standard_normal((H, D)) / np.sqrt(D))
+            w["b1"] = _f32(rng.standard_normal(H) / np.sqrt(D))
+            w["W2"] = _f32(rng.standard_normal((H, H)) / np.sqrt(H))
+            w["b2"] = _f32(rng.standard_normal(H) / np.sqrt(H))
+            w["W3"] = _f32(rng.standard_normal((out, H)) / np.sqrt(H))
+            w["b3"] = _f32(rng.standard_normal(out) / np.sqrt(H))
             per_s.append(w)
         mlp.append(per_s)
     if layer_scale is None:
