@@ -1,0 +1,235 @@
+"""Benchmark: atom-steps/s of the MPNN energy+force+MD hot path on one MI355X.
+
+Workload (default): fcc Ag, 80^3 conventional cells = 2,048,000 local atoms (one GPU's
+subdomain of a 100M-atom run) plus the periodic-image ghost shell of width rc + skin;
+T = 3 message-passing layers, K = 8 radial primitives, L = 2, MLP 2x64 SiLU, rc = 6 A,
+skin = 1 A; velocity-Verlet steps of 1 fs with a neighbour rebuild every 20 steps.
+One "step" = one MD step of the whole path (half-kick + drift, skin test, rebuild when due,
+ghost refresh, T forward layers, energy network, reverse pass, force gather, half-kick).
+
+Prints ONE JSON line.  Timing: warmup steps untimed, then `--steps` steps bracketed by
+torch.cuda.synchronize(); inputs are resident in HBM before the timed region.  Per-kernel
+durations come from the library's hipEvent profiler on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VALU_TFLOPS = 157.3       # MI355X published fp32 vector peak
+FP32_MFMA_TFLOPS = 157.3       # MI355X published dense fp32 matrix peak
+METRIC = "atom-steps/s (E+F, T=3) on 2.05M-atom Ag subdomain, 1 MI355X; % HBM roof"
+
+
+def kernel_model(fam, g):
+    """Algorithmic (bytes, flops, unit) per launch of kernel family `fam`."""
+    N, NN, EL, EA = g["N"], g["NN"], g["EL"], g["EA"]
+    K, M, D, H, T = g["K"], g["M"], g["D"], g["H"], g["T"]
+    KM = K * M
+    if fam == "aggregate":
+        b = 8 * (N + 1) + 4 * EL + 24 * NN + 4 * K * NN + 4 * KM * N
+        f = EA * (2 * KM + 6 * K + 20)
+        return b, f, "alu"
+    if fam == "message_grad":
+        b = 8 * (NN + 1) + 4 * EL + 24 * NN + 4 * KM * N + 4 * K * NN
+        f = EA * (2 * KM + 8 * K + 20)
+        return b, f, "alu"
+    if fam == "edge_forces":
+        b = 8 * (N + 1) + 4 * EL + 24 * NN + T * (4 * KM * N + 4 * K * NN) + 12 * EL + 24 * N
+        f = T * EA * (4 * KM + 8 * K + 6 * M + 40)
+        return b, f, "alu"
+    if fam == "force_gather":
+        b = 8 * (NN + 1) + 8 * (N + 1) + 4 * EL + 12 * EL + 24 * N + 48 * N
+        return b, 3 * EL, "hbm"
+    if fam == "net_forward":
+        b = 4 * KM * N + 4 * K * N
+        f = N * 2 * (H * D + H * H + K * H)
+        return b, f, "mfma"
+    if fam == "net_energy":
+        b = 8 * KM * N + 4 * N
+        f = N * 2 * (2 * H * D + 2 * H * H + 2 * H) + N * 2 * K * KM
+        return b, f, "mfma"
+    if fam == "net_backward":
+        b = 8 * KM * N + 4 * K * N
+        f = N * 2 * (2 * H * D + 2 * H * H + K * H + K * H) + N * 2 * K * KM
+        return b, f, "mfma"
+    return None
+
+
+def roofline_for(fam, ms_avg, g):
+    bytes_, flops, kind = kernel_model(fam, g)
+    t = ms_avg * 1e-3
+    gbs = bytes_ / t / 1e9
+    tfs = flops / t / 1e12
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_cmp = flops / ((FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS) * 1e12)
+    if kind == "hbm" or t_hbm >= t_cmp:
+        return {"kernel": fam, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes": int(bytes_), "avg_ms": round(ms_avg, 4)}
+    peak = FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS
+    return {"kernel": fam, "bound": "mfma" if kind == "mfma" else "alu", "achieved": round(tfs, 2),
+            "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": None,
+            "algorithmic_flops": int(flops), "algorithmic_bytes": int(bytes_),
+            "hbm_GBs_at_algorithmic_bytes": round(gbs, 1), "avg_ms": round(ms_avg, 4)}
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """fp64 oracle (as it stands) on a bounded periodic sample of the same workload."""
+    import oracle
+    from molecular_dynamics_cell_amd import inputs as I
+    p = I.make_params(cfg)
+    if cfg in (1, 4):
+        s = I.ag(10, 1004, 1104, name="Ag4000")
+        sample = "fcc Ag 10^3 cells (4,000 atoms, periodic), same model and lattice"
+    elif cfg == 3:
+        s = I.hea(13)
+        sample = "bcc HEA 13^3 cells (4,394 atoms, periodic), same model"
+    elif cfg == 5:
+        s = I.make_system(5, reduced=True)
+        sample = "CHON gas, 4,002 atoms at 0.5 g/cm3, same model"
+    else:
+        s = I.make_system(2)
+        sample = "the full 4,608-atom water box"
+    m = oracle.Model(p)
+    rb = I.CONFIGS[cfg]["rebuild_every"]
+    dt = I.CONFIGS[cfg]["dt"]
+    t0 = time.perf_counter()
+    oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, dt, 1, rebuild_every=rb)
+    t1 = time.perf_counter() - t0
+    steps = int(max(1, min(200, budget_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, dt, steps, rebuild_every=rb)
+    el = time.perf_counter() - t0
+    return {"value": round(s.n * steps / el, 1), "unit": "atom-steps/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}; {steps} velocity-Verlet steps (E+F each step) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=4, help="benchmark system 1..5 (default 4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--ef-evals", type=int, default=10)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also launch one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the multi-GPU halo exchange is designed, "
+              "not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from molecular_dynamics_cell_amd import binding, inputs as I
+
+    dev = torch.device("cuda:0")
+    cfg = args.config
+    c = I.CONFIGS[cfg]
+    t_setup = time.perf_counter()
+    s = I.make_system(cfg)
+    p = I.make_params(cfg)
+    m = binding.MPNN(p, dev)
+    pos = torch.tensor(s.pos, device=dev)
+    m.build_neighbors(pos, torch.tensor(s.types, device=dev), s.box)
+    m.set_state(vel=torch.tensor(s.vel, device=dev))
+    info = m.info()
+    # active edges (d < rc) of the initial configuration, for the algorithmic work model
+    pi, pj, ps = m.get_pairs()
+    pw = pos.remainder(torch.tensor(s.box, device=dev))
+    r = pw[pj.long()] + ps.double() * torch.tensor(s.box, device=dev) - pw[pi.long()]
+    EA = int((r.square().sum(1) < p.spec.rc ** 2).sum().item())
+    del pi, pj, ps, r, pw
+    torch.cuda.empty_cache()
+    print(f"setup {time.perf_counter() - t_setup:.1f} s: {info}", file=sys.stderr, flush=True)
+
+    if args.copy_mib:
+        a = torch.ones(args.copy_mib * 262144, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    E0, _, _ = m.energy_forces()
+    m.md_step(c["dt"], args.warmup, c["rebuild_every"], stats=False)
+    torch.cuda.synchronize()
+    if not args.no_profile:
+        m.set_profiling(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    st = m.md_step(c["dt"], args.steps, c["rebuild_every"], stats=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = m.profile() if not args.no_profile else {}
+    m.set_profiling(False)
+    st = m.md_step(c["dt"], 0, c["rebuild_every"])      # energies at the end of the run
+    elapsed = t1 - t0
+    value = s.n * args.steps / elapsed
+
+    # E+F only: median of evaluations on the current state
+    ef = []
+    for _ in range(args.ef_evals):
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        m.energy_forces(energy=False)
+        torch.cuda.synchronize()
+        ef.append(time.perf_counter() - a0)
+    ef_rate = s.n / float(np.median(ef)) if ef else None
+
+    g = dict(N=s.n, NN=info["n_local"] + info["n_ghost"], EL=info["n_edges"], EA=EA, K=p.spec.K,
+             M=(p.spec.L + 1) * (p.spec.L + 2) * (p.spec.L + 3) // 6, D=p.D, H=p.spec.H, T=p.spec.T)
+    kernels = {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                   "ms_avg": round(v[0] / v[1], 4) if v[1] else 0.0}
+               for k, v in prof.items() if v[1]}
+    roof = None
+    modeled = [k for k in kernels if kernel_model(k, g) is not None]
+    if modeled:
+        dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
+        roof = roofline_for(dom, kernels[dom]["ms_avg"], g)
+    for k in modeled:
+        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "atom-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name}: {s.n} atoms + {info['n_ghost']} ghosts, T={p.spec.T}, "
+                               f"K={p.spec.K}, L={p.spec.L}, MLP 2x{p.spec.H}, rc={p.spec.rc}, "
+                               f"skin={p.spec.skin}, dt={c['dt']} fs, rebuild every {c['rebuild_every']}",
+                   "atoms": s.n, "ghosts": info["n_ghost"], "verlet_entries": info["n_edges"],
+                   "active_edges": EA, "parallelism": "single GPU"},
+        "roofline": roof,
+        "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,
+        "md": {"epot_start": E0, "epot_end": st["epot"], "ekin_end": st["ekin"],
+               "temp_end": st["temp"], "steps_total": st["steps"]},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

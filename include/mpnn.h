@@ -153,6 +153,16 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
 
 mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info);
 
+/* Event profiler: enable != 0 resets the counters and records a hipEvent pair on the context's
+ * stream around every kernel family launched afterwards; 0 stops recording.  Durations are
+ * collected at the library's own synchronisation points. */
+mpnn_status mpnn_set_profiling(mpnn_ctx *ctx, int32_t enable);
+
+/* Accumulated device time and launch count of kernel family idx (0 <= idx < number of families;
+ * MPNN_E_INVALID_ARG past the end).  *name is a static string. */
+mpnn_status mpnn_get_profile(mpnn_ctx *ctx, int32_t idx, const char **name, double *total_ms,
+                             int64_t *launches);
+
 /* Text of the last error on this context ("" if none); valid until the next call. */
 const char *mpnn_last_error(const mpnn_ctx *ctx);
 

@@ -72,6 +72,9 @@ def lib():
             "mpnn_get_pairs": ([p, i64, C.POINTER(C.c_int64), p, p, p], st),
             "mpnn_get_intermediate": ([p, i32, i32, p], st),
             "mpnn_get_info": ([p, C.POINTER(Info)], st),
+            "mpnn_set_profiling": ([p, i32], st),
+            "mpnn_get_profile": ([p, i32, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
+                                  C.POINTER(C.c_int64)], st),
             "mpnn_last_error": ([p], C.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -187,6 +190,23 @@ class MPNN:
         width = {0: self.K, 1: self.K * self.M, 2: self.K * self.M, 3: 1}[which]
         out = torch.empty((self.n, width), dtype=torch.float64, device=self.device)
         self._check(lib().mpnn_get_intermediate(self.h, int(which), int(t), _dptr(out)))
+        return out
+
+    def set_profiling(self, enable: bool):
+        self._check(lib().mpnn_set_profiling(self.h, 1 if enable else 0))
+
+    def profile(self) -> dict:
+        """{kernel family: (total ms, launches)} from the library's event profiler."""
+        out = {}
+        idx = 0
+        while True:
+            name = C.c_char_p()
+            ms = C.c_double()
+            cnt = C.c_int64()
+            if lib().mpnn_get_profile(self.h, idx, C.byref(name), C.byref(ms), C.byref(cnt)) != 0:
+                break
+            out[name.value.decode()] = (ms.value, cnt.value)
+            idx += 1
         return out
 
     def info(self):

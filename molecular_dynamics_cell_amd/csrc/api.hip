@@ -43,6 +43,52 @@ Status Context::grow_keep(Buf &b, size_t bytes, size_t keep) {
     return Status::ok();
 }
 
+const char *const kProfNames[kProfCount] = {
+    "build_sort", "build_ghosts", "build_rows", "build_transpose", "build_species", "ghost_positions",
+    "aggregate", "net_forward", "net_energy", "net_backward", "ghost_messages", "message_grad",
+    "ghost_grad_fold", "edge_forces", "force_gather", "kick_drift", "kick", "reduce"};
+
+void Context::prof_begin(int id) {
+    if (!prof_on) return;
+    if (prof_open.empty()) prof_open.assign(kProfCount, nullptr);
+    hipEvent_t e = nullptr;
+    if (!prof_pool.empty()) {
+        e = prof_pool.back();
+        prof_pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+        return;
+    }
+    (void)hipEventRecord(e, stream);
+    prof_open[id] = e;
+}
+
+void Context::prof_end(int id) {
+    if (!prof_on || prof_open.empty() || !prof_open[id]) return;
+    hipEvent_t e = nullptr;
+    if (!prof_pool.empty()) {
+        e = prof_pool.back();
+        prof_pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+        return;
+    }
+    (void)hipEventRecord(e, stream);
+    prof_pending.push_back({id, prof_open[id], e});
+    prof_open[id] = nullptr;
+}
+
+void Context::prof_harvest() {
+    for (const Pending &p : prof_pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+            prof_ms[p.id] += ms;
+            prof_launches[p.id] += 1;
+        }
+        prof_pool.push_back(p.a);
+        prof_pool.push_back(p.b);
+    }
+    prof_pending.clear();
+}
+
 void Context::release(Buf &b) {
     if (b.p) {
         (void)hipFree(b.p);
@@ -59,6 +105,8 @@ Context::~Context() {
                   &gedge, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c, &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel};
     for (Buf *b : all) release(*b);
+    prof_harvest();
+    for (hipEvent_t e : prof_pool) (void)hipEventDestroy(e);
 }
 
 namespace {
@@ -225,6 +273,10 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
         s = mpnn::energy_sum(cx, energy);
         if (!s.bad() && !std::isfinite(*energy)) s = Status::err(MPNN_E_NONFINITE, "non-finite energy");
     }
+    if (cx.prof_on && !s.bad()) {
+        if (hipStreamSynchronize(cx.stream) != hipSuccess) s = Status::err(MPNN_E_HIP, "stream sync failed");
+        cx.prof_harvest();
+    }
     return mpnn::finish(ctx, s);
 }
 
@@ -247,6 +299,7 @@ mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t r
             bool ex = false;
             double md = 0.0;
             MPNN_TRY(mpnn::read_skin_flag(cx, &ex, &md));
+            cx.prof_harvest();
             max_disp = md > max_disp ? md : max_disp;
             if (need || ex) {
                 MPNN_TRY(mpnn::rebuild_from_state(cx));
@@ -270,6 +323,7 @@ mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t r
         } else {
             MPNN_HIP(hipStreamSynchronize(cx.stream));
         }
+        cx.prof_harvest();
         return Status::ok();
     };
     return mpnn::finish(ctx, run());
@@ -370,6 +424,29 @@ mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info) {
     info->n_edges = cx.E;
     for (int a = 0; a < 3; ++a) info->cells[a] = cx.nc[a];
     info->bytes_device = (int64_t)cx.device_bytes;
+    return mpnn::finish(ctx, Status::ok());
+}
+
+mpnn_status mpnn_set_profiling(mpnn_ctx *ctx, int32_t enable) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (hipStreamSynchronize(cx.stream) != hipSuccess)
+        return mpnn::finish(ctx, Status::err(MPNN_E_HIP, "stream sync failed"));
+    cx.prof_harvest();
+    for (int i = 0; i < mpnn::kProfCount; ++i) {
+        cx.prof_ms[i] = 0.0;
+        cx.prof_launches[i] = 0;
+    }
+    cx.prof_on = enable != 0;
+    return mpnn::finish(ctx, Status::ok());
+}
+
+mpnn_status mpnn_get_profile(mpnn_ctx *ctx, int32_t idx, const char **name, double *total_ms, int64_t *launches) {
+    if (!ctx || idx < 0 || idx >= mpnn::kProfCount) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (name) *name = mpnn::kProfNames[idx];
+    if (total_ms) *total_ms = cx.prof_ms[idx];
+    if (launches) *launches = cx.prof_launches[idx];
     return mpnn::finish(ctx, Status::ok());
 }
 

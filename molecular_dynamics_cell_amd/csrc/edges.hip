@@ -284,6 +284,7 @@ __global__ void k_force_gather(int64_t n, const int32_t *__restrict__ perm, cons
 }  // namespace
 
 Status aggregate(Context &cx, int t) {
+    ProfScope ps_(cx, kProfAggregate);
     if (cx.n == 0) return Status::ok();
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
@@ -295,6 +296,7 @@ Status aggregate(Context &cx, int t) {
 }
 
 Status refresh_ghost_features(Context &cx, int t) {
+    ProfScope ps_(cx, kProfGhostFeat);
     if (cx.G == 0) return Status::ok();
     float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
     k_ghost_feat<<<grid_for(cx.G * cx.K), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.K, cx.ghost_owner.as<int32_t>(), ct);
@@ -305,10 +307,14 @@ Status refresh_ghost_features(Context &cx, int t) {
 Status backward_messages(Context &cx, int t) {
     if (cx.n == 0) return Status::ok();
     const float *GOt = cx.GO.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_message_grad<KK, LL><<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(
-                                      cx.NN, cx.pos.as<double>(), cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(),
-                                      GOt, cx.model.as<ModelDev>(), cx.Gc.as<float>())));
-    MPNN_HIP(hipGetLastError());
+    {
+        ProfScope ps_(cx, kProfMessageGrad);
+        MPNN_DISPATCH_KL(cx.K, cx.L, (k_message_grad<KK, LL><<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(
+                                          cx.NN, cx.pos.as<double>(), cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(),
+                                          GOt, cx.model.as<ModelDev>(), cx.Gc.as<float>())));
+        MPNN_HIP(hipGetLastError());
+    }
+    ProfScope ps_(cx, kProfGhostFold);
     k_fold_ghost_grad<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.K, cx.ghost_off.as<int64_t>(),
                                                                  cx.Gc.as<float>());
     MPNN_HIP(hipGetLastError());
@@ -316,6 +322,7 @@ Status backward_messages(Context &cx, int t) {
 }
 
 Status force_edges(Context &cx) {
+    ProfScope ps_(cx, kProfEdgeForces);
     if (cx.n == 0) return Status::ok();
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_edge_forces<KK, LL><<<grid_for(cx.n), kBlock, 0, cx.stream>>>(
                                       cx.n, cx.T, cx.NN, cx.pos.as<double>(), cx.row_off.as<int64_t>(),
@@ -326,6 +333,7 @@ Status force_edges(Context &cx) {
 }
 
 Status force_gather(Context &cx, double *F_caller) {
+    ProfScope ps_(cx, kProfForceGather);
     if (cx.n == 0) return Status::ok();
     k_force_gather<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(),
                                                             cx.t_eid.as<int32_t>(), cx.ghost_off.as<int64_t>(),

@@ -36,6 +36,15 @@ struct Status {
         if (s_.bad()) return s_;                                                            \
     } while (0)
 
+// Kernel families timed by the optional event profiler (mpnn_set_profiling).
+enum ProfId {
+    kProfBuildSort = 0, kProfBuildGhost, kProfBuildRows, kProfBuildTranspose, kProfBuildSpecies,
+    kProfGhostPos, kProfAggregate, kProfNetForward, kProfNetEnergy, kProfNetBackward, kProfGhostFeat,
+    kProfMessageGrad, kProfGhostFold, kProfEdgeForces, kProfForceGather, kProfKickDrift, kProfKick,
+    kProfReduce, kProfCount
+};
+extern const char *const kProfNames[kProfCount];
+
 // A growable device allocation.
 struct Buf {
     void *p = nullptr;
@@ -100,6 +109,18 @@ struct Context {
     std::string last_error;
     size_t device_bytes = 0;
 
+    // ---- event profiler ----
+    bool prof_on = false;
+    double prof_ms[kProfCount] = {};
+    int64_t prof_launches[kProfCount] = {};
+    std::vector<hipEvent_t> prof_pool;
+    struct Pending { int id; hipEvent_t a, b; };
+    std::vector<Pending> prof_pending;
+    std::vector<hipEvent_t> prof_open;  // start event per id while a scope is open
+    void prof_begin(int id);
+    void prof_end(int id);
+    void prof_harvest();                // after a stream synchronisation
+
     Buf types_caller;             // int32 [n] species in caller order (for rebuilds)
     Buf stage_pos, stage_vel;     // double [n][3] caller-order staging
     std::vector<float> inv_scale_host;  // 1 / s_t
@@ -108,6 +129,14 @@ struct Context {
     Status grow_keep(Buf &b, size_t bytes, size_t keep);
     void release(Buf &b);
     ~Context();
+};
+
+// Times the launches issued while it lives (no-op unless profiling is on).
+struct ProfScope {
+    Context &cx;
+    int id;
+    ProfScope(Context &c, int i) : cx(c), id(i) { cx.prof_begin(id); }
+    ~ProfScope() { cx.prof_end(id); }
 };
 
 // ---- scan.hip ----

@@ -147,6 +147,7 @@ __global__ void k_unpermute_float(int64_t n, int width, const int32_t *__restric
 }  // namespace
 
 Status energy_sum(Context &cx, double *E_host) {
+    ProfScope ps_(cx, kProfReduce);
     if (cx.n == 0) {
         *E_host = 0.0;
         return Status::ok();
@@ -159,6 +160,7 @@ Status energy_sum(Context &cx, double *E_host) {
 }
 
 Status kinetic_energy(Context &cx, double *ke_host) {
+    ProfScope ps_(cx, kProfReduce);
     if (cx.n == 0) {
         *ke_host = 0.0;
         return Status::ok();
@@ -172,6 +174,7 @@ Status kinetic_energy(Context &cx, double *ke_host) {
 }
 
 Status kick_drift(Context &cx, double dt) {
+    ProfScope ps_(cx, kProfKickDrift);
     if (cx.n == 0) return Status::ok();
     const double hs = 0.5 * cx.skin;
     k_kick_drift<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, dt, hs * hs, cx.types.as<int32_t>(),
@@ -192,6 +195,7 @@ Status skin_check(Context &cx) {
 }
 
 Status kick(Context &cx, double dt) {
+    ProfScope ps_(cx, kProfKick);
     if (cx.n == 0) return Status::ok();
     k_kick<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, dt, cx.types.as<int32_t>(), cx.model.as<ModelDev>(),
                                                      cx.F.as<double>(), cx.vel.as<double>());

@@ -329,6 +329,7 @@ Status pack_weights(Context &cx, const double *mlp) {
 }
 
 Status mlp_forward(Context &cx, int t) {
+    ProfScope ps_(cx, kProfNetForward);
     NetArgs a = make_args(cx, t);
     a.c_next = cx.c.as<float>() + (int64_t)(t + 1) * cx.NN * cx.K;
     a.inv_scale = cx.inv_scale_host[t];
@@ -337,6 +338,7 @@ Status mlp_forward(Context &cx, int t) {
 }
 
 Status mlp_energy(Context &cx) {
+    ProfScope ps_(cx, kProfNetEnergy);
     const int t = cx.T - 1;
     NetArgs a = make_args(cx, t);
     a.inv_scale = cx.inv_scale_host[t];
@@ -347,6 +349,7 @@ Status mlp_energy(Context &cx) {
 }
 
 Status mlp_backward(Context &cx, int t) {
+    ProfScope ps_(cx, kProfNetBackward);
     NetArgs a = make_args(cx, t);
     a.inv_scale = cx.inv_scale_host[t];
     a.Gc = cx.Gc.as<float>();

@@ -403,6 +403,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         if (bad & 1) return Status::err(MPNN_E_NONFINITE, "non-finite position");
         if (bad & 2) return Status::err(MPNN_E_INVALID_ARG, "species index out of range");
     }
+    cx.prof_begin(kProfBuildSort);
     k_wrap_key<<<grid_for(n), kBlock, 0, cx.stream>>>(n, pos_caller, g, pos_w, key);
     MPNN_HIP(hipGetLastError());
     MPNN_TRY(counting_sort(cx, key, n, nkeys, off, cx.perm.as<int32_t>(), cnt));
@@ -416,7 +417,10 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
                                                            cx.inv_perm.as<int32_t>());
     MPNN_HIP(hipGetLastError());
 
+    cx.prof_end(kProfBuildSort);
+
     // ---- ghost shell: images within rc + skin of the box (margin 1e-9 A) ----
+    cx.prof_begin(kProfBuildGhost);
     const double wg = w + 1e-9;
     MPNN_TRY(cx.grow(cx.ghost_off, sizeof(int64_t) * (n1 + 1)));
     k_ghost_count<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, wg, key);
@@ -442,7 +446,10 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
                                                        g, cx.pos.as<double>(), cx.types.as<int32_t>());
     MPNN_HIP(hipGetLastError());
 
+    cx.prof_end(kProfBuildGhost);
+
     // ---- bin every node on the extended grid (one cell layer of ghosts per side) ----
+    cx.prof_begin(kProfBuildRows);
     MPNN_TRY(cx.grow(cx.tmp_b, sizeof(int32_t) * (size_t)(NN1 > next ? NN1 : next) * 2));
     key = cx.tmp_b.as<int32_t>();
     int32_t *cnodes = key + (NN1 > next ? NN1 : next);
@@ -469,7 +476,10 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
                                                         cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>());
     MPNN_HIP(hipGetLastError());
 
+    cx.prof_end(kProfBuildRows);
+
     // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
+    cx.prof_begin(kProfBuildTranspose);
     MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
     MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
@@ -495,7 +505,10 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         MPNN_HIP(hipGetLastError());
     }
 
+    cx.prof_end(kProfBuildTranspose);
+
     // ---- atoms grouped by species (ascending sorted index within a species) ----
+    cx.prof_begin(kProfBuildSpecies);
     MPNN_TRY(cx.grow(cx.sp_list, sizeof(int32_t) * n1));
     MPNN_TRY(cx.grow(cx.sp_off, sizeof(int64_t) * (cx.S + 1)));
     cx.sp_count.assign(cx.S, 0);
@@ -529,6 +542,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     k_c0<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.K, cx.types.as<int32_t>(), cx.model.as<ModelDev>(),
                                                     cx.c.as<float>());
     MPNN_HIP(hipGetLastError());
+    cx.prof_end(kProfBuildSpecies);
     MPNN_HIP(hipStreamSynchronize(cx.stream));
     cx.built = true;
     cx.since_build = 0;
@@ -536,6 +550,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
 }
 
 Status refresh_ghost_positions(Context &cx) {
+    ProfScope ps_(cx, kProfGhostPos);
     if (cx.G == 0) return Status::ok();
     const Grid g = make_grid(cx);
     k_ghost_pos<<<grid_for(cx.G), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.ghost_owner.as<int32_t>(),
