@@ -31,22 +31,33 @@ METRIC = "atom-steps/s (E+F, T=3) on 2.05M-atom Ag subdomain, 1 MI355X; % HBM ro
 
 
 def kernel_model(fam, g):
-    """Algorithmic (bytes, flops, unit) per launch of kernel family `fam`."""
+    """Algorithmic (bytes, flops, kind) per launch of kernel family `fam`.
+
+    Bytes count each array the kernel must touch once (index streams, per-atom state read or
+    written, per-edge outputs); gathered neighbour data (positions, messages) is counted once
+    per node, not per edge.  Flops count the contractions of the method per active edge or
+    per atom (multiply-add = 2), not the basis transcendentals.  N local atoms, NN nodes,
+    EL Verlet entries, EA active entries (d < rc)."""
     N, NN, EL, EA = g["N"], g["NN"], g["EL"], g["EA"]
     K, M, D, H, T = g["K"], g["M"], g["D"], g["H"], g["T"]
     KM = K * M
+    if fam == "compact":
+        b = 8 * (N + 1) + 4 * EL + 24 * NN + 8 * EA + 4 * N + (EL - EA) * (12 + 4 * K)
+        return b, 8 * EL, "hbm"
     if fam == "aggregate":
-        b = 8 * (N + 1) + 4 * EL + 24 * NN + 4 * K * NN + 4 * KM * N
-        f = EA * (2 * KM + 6 * K + 20)
+        b = 8 * (N + 1) + 4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * KM * N
+        f = EA * (2 * KM + 2 * K)
+        return b, f, "alu"
+    if fam == "backward_layer":
+        w_frac = (T - 1) / T                       # layers that emit dE/dc edge terms
+        g_rw = (12 + 24 * (T - 1)) / T             # first layer writes, later ones accumulate
+        b = (8 * (N + 1) + 4 * N + 8 * EA + 24 * NN + 4 * K * NN + 4 * KM * N
+             + w_frac * 4 * K * EA + g_rw * EA + 24 * N * (2 * T - 1) / T)
+        f = EA * (4 * KM + 6 * K + 6 * M)
         return b, f, "alu"
     if fam == "message_grad":
-        b = 8 * (NN + 1) + 4 * EL + 24 * NN + 4 * KM * N + 4 * K * NN
-        f = EA * (2 * KM + 8 * K + 20)
-        return b, f, "alu"
-    if fam == "edge_forces":
-        b = 8 * (N + 1) + 4 * EL + 24 * NN + T * (4 * KM * N + 4 * K * NN) + 12 * EL + 24 * N
-        f = T * EA * (4 * KM + 8 * K + 6 * M + 40)
-        return b, f, "alu"
+        b = 8 * (NN + 1) + 4 * EL + 4 * K * EL + 4 * K * NN
+        return b, K * EL, "hbm"
     if fam == "force_gather":
         b = 8 * (NN + 1) + 8 * (N + 1) + 4 * EL + 12 * EL + 24 * N + 48 * N
         return b, 3 * EL, "hbm"

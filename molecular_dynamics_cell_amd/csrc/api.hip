@@ -45,8 +45,8 @@ Status Context::grow_keep(Buf &b, size_t bytes, size_t keep) {
 
 const char *const kProfNames[kProfCount] = {
     "build_sort", "build_ghosts", "build_rows", "build_transpose", "build_species", "ghost_positions",
-    "aggregate", "net_forward", "net_energy", "net_backward", "ghost_messages", "message_grad",
-    "ghost_grad_fold", "edge_forces", "force_gather", "kick_drift", "kick", "reduce"};
+    "compact", "aggregate", "net_forward", "net_energy", "net_backward", "ghost_messages",
+    "backward_layer", "message_grad", "ghost_grad_fold", "force_gather", "kick_drift", "kick", "reduce"};
 
 void Context::prof_begin(int id) {
     if (!prof_on) return;
@@ -101,8 +101,9 @@ void Context::release(Buf &b) {
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
-                  &ghost_off, &row_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &GO, &Gc,
-                  &gedge, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c, &tmp_d, &tmp_scan,
+                  &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &GO, &Gc,
+                  &gedge, &w, &act_e, &act_n, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
+                  &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel};
     for (Buf *b : all) release(*b);
     prof_harvest();
@@ -120,6 +121,7 @@ bool supported(int K, int L, int H) {
 // per-layer ghost refresh, then Eq. 3-5 backward with the ghost->owner folds.
 Status evaluate(Context &cx, double *F_caller) {
     MPNN_TRY(refresh_ghost_positions(cx));
+    MPNN_TRY(compact_active(cx));
     for (int t = 0; t < cx.T; ++t) {
         MPNN_TRY(aggregate(cx, t));
         if (t < cx.T - 1) {
@@ -129,11 +131,13 @@ Status evaluate(Context &cx, double *F_caller) {
             MPNN_TRY(mlp_energy(cx));
         }
     }
-    for (int t = cx.T - 1; t >= 1; --t) {
-        MPNN_TRY(backward_messages(cx, t));
-        MPNN_TRY(mlp_backward(cx, t - 1));
+    for (int t = cx.T - 1; t >= 0; --t) {
+        MPNN_TRY(backward_layer(cx, t));
+        if (t >= 1) {
+            MPNN_TRY(backward_messages(cx, t));
+            MPNN_TRY(mlp_backward(cx, t - 1));
+        }
     }
-    MPNN_TRY(force_edges(cx));
     MPNN_TRY(force_gather(cx, F_caller));
     cx.forces_valid = true;
     return Status::ok();
@@ -200,6 +204,8 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     md.rc = (float)p->rc;
     md.inv_rc = (float)(1.0 / p->rc);
     md.pi_over_rc = (float)(mpnn::kPi / p->rc);
+    md.exp2_coef = (float)(-1.0 / (2.0 * p->sigma * p->sigma * std::log(2.0)));
+    md.dfc_scale = (float)(-0.5 * mpnn::kPi / p->rc);
     md.rc2 = p->rc * p->rc;
     Status s = cx.grow(cx.model, sizeof md);
     if (!s.bad()) {

@@ -18,6 +18,20 @@ inline unsigned grid_for(int64_t n, int block = kBlock) {
     return (unsigned)((n + block - 1) / block > 0 ? (n + block - 1) / block : 1);
 }
 
+// XCD-aware launches: the hardware deals consecutive workgroups round-robin to the 8 XCDs, each
+// with its own L2.  Launch a multiple of 8 groups and let group b work on logical block
+// (b % 8) * (groups / 8) + b / 8, so every XCD sweeps one contiguous (spatially compact) range
+// of the cell-ordered atoms.
+constexpr int kXcds = 8;
+inline unsigned grid_xcd(int64_t n, int block = kBlock) {
+    const int64_t g = ((n + block - 1) / block + kXcds - 1) / kXcds * kXcds;
+    return (unsigned)(g > 0 ? g : kXcds);
+}
+__device__ __forceinline__ int64_t xcd_block() {
+    const int64_t per = gridDim.x / kXcds;
+    return (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+}
+
 // ------------------------------------------------------------------------------------------
 // Compile-time structure of the orbital basis (paper, "REANN Architecture": primitives with
 // angular momenta lx+ly+lz = l <= L; Eq. 1 weights l!/(lx! ly! lz!)).
@@ -83,9 +97,19 @@ struct ModelDev {
     float neg_half_inv_s2;  // -1 / (2 sigma^2)
     float inv_s2;           // 1 / sigma^2
     float rc, inv_rc, pi_over_rc;
+    float exp2_coef;        // -log2(e) / (2 sigma^2): R_k = exp2(exp2_coef (d - mu_k)^2)
+    float dfc_scale;        // -pi / (2 rc): df_c/dd = dfc_scale sin(pi d / rc)
     double rc2;             // rc^2 (fp64, for the active-edge test)
     double mass[16];        // amu per species
 };
+
+// Sliced-ELLPACK neighbour storage: rows are grouped in slabs of 64 consecutive (cell-ordered)
+// atoms; entry j of row i lives at slab_off[i / 64] + 64 j + i % 64, so the 64 lanes of a wave
+// that each walk one row touch 64 consecutive words per step.
+constexpr int kSlab = 64;
+__host__ __device__ inline int64_t sell_base(const int64_t *slab_off, int64_t i) {
+    return slab_off[i / kSlab] + (i % kSlab);
+}
 
 // Periodic image shift code 0..26 <-> (sx, sy, sz) in {-1,0,1}^3; 13 is the identity.
 __host__ __device__ inline void shift_of(int code, int &sx, int &sy, int &sz) {

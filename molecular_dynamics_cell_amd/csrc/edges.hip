@@ -13,11 +13,13 @@ namespace mpnn {
 
 namespace {
 
-// Edge basis of one edge, fp32, from the fp64 displacement.
-template <int K, int L>
+// Edge basis of one edge, fp32, from the fp64 displacement: hardware exp2 of a pre-scaled
+// argument for the Gaussians, correctly rounded sqrt and 1/d, the accurate cospi/sinpi for the
+// cutoff (the hardware sqrt and cos/sin shifted the total energy by several 1e-6 relative).
+template <int K, int L, bool DERIV>
 struct Basis {
     static constexpr int M = n_mono(L);
-    float R[K], fc, A[M];
+    float R[K], dR[DERIV ? K : 1], fc, dfc, A[M];
     float d, inv_d, v;  // v = d / rc
     float rx, ry, rz;
     float ux[L + 1], uy[L + 1], uz[L + 1];
@@ -28,19 +30,21 @@ struct Basis {
         rx = (float)dx; ry = (float)dy; rz = (float)dz;
         d = sqrtf(rx * rx + ry * ry + rz * rz);
         inv_d = 1.0f / d;
-        // x / rc as a refined quotient (no bias from rounding 1/rc), cos(pi d/rc) via cospi
+        // x / rc as a refined quotient (no bias from rounding 1/rc)
         const float rc = md->rc, ir = md->inv_rc;
         auto div_rc = [rc, ir](float x) {
             const float q = x * ir;
             return fmaf(fmaf(-q, rc, x), ir, q);
         };
         v = div_rc(d);
-        fc = 0.5f * (1.0f + cospif(v));
-        const float nh = md->neg_half_inv_s2;
+        fc = 0.5f + 0.5f * cospif(v);
+        if (DERIV) dfc = md->dfc_scale * sinpif(v);
+        const float c2 = md->exp2_coef, is2 = md->inv_s2;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            float x = d - mu[k];
-            R[k] = expf(nh * x * x);
+            const float x = d - mu[k];
+            R[k] = __builtin_amdgcn_exp2f(c2 * x * x);
+            if (DERIV) dR[k] = -x * is2 * R[k];
         }
         const float qx = div_rc(rx), qy = div_rc(ry), qz = div_rc(rz);
         ux[0] = uy[0] = uz[0] = 1.0f;
@@ -55,32 +59,60 @@ struct Basis {
     }
 };
 
+// Per-step active list: the Verlet entries of each row with d^2 < rc^2 (fp64, the same
+// expression as the build), compacted in row order.  Per-edge outputs of inactive entries are
+// never written; the sender-major gathers repeat the same test on the same operands.
+__global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
+                                                 const int64_t *__restrict__ slab_off,
+                                                 const int32_t *__restrict__ len,
+                                                 const int32_t *__restrict__ nbr, double rc2,
+                                                 int32_t *__restrict__ act_e, int32_t *__restrict__ act_n,
+                                                 int32_t *__restrict__ nact) {
+    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const int64_t b = sell_base(slab_off, i);
+    const int nl = len[i];
+    int o = 0;
+    for (int j = 0; j < nl; ++j) {
+        const int64_t e = b + kSlab * j;
+        const int64_t v = nbr[e];
+        const double d2 = d2_exact(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi),
+                                   __dsub_rn(pos[3 * v + 2], zi));
+        if (d2 < rc2) {
+            act_e[b + kSlab * o] = (int32_t)e;
+            act_n[b + kSlab * o] = (int32_t)v;
+            ++o;
+        }
+    }
+    nact[i] = o;
+}
+
+// O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum).
 template <int K, int L>
 __global__ __launch_bounds__(256) void k_aggregate(int64_t n, const double *__restrict__ pos,
-                                                   const int64_t *__restrict__ row_off,
-                                                   const int32_t *__restrict__ nbr, const float *__restrict__ c,
+                                                   const int64_t *__restrict__ slab_off,
+                                                   const int32_t *__restrict__ nact,
+                                                   const int32_t *__restrict__ act_n, const float *__restrict__ c,
                                                    const ModelDev *__restrict__ md, float *__restrict__ O) {
     constexpr int M = n_mono(L);
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
     if (i >= n) return;
     float mu[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
-    const double rc2 = md->rc2;
     const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
     float acc[K][M];
 #pragma unroll
     for (int k = 0; k < K; ++k)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[k][m] = 0.0f;
-    const int64_t e1 = row_off[i + 1];
-    for (int64_t e = row_off[i]; e < e1; ++e) {
-        const int64_t v = nbr[e];
-        const double dx = __dsub_rn(pos[3 * v], xi), dy = __dsub_rn(pos[3 * v + 1], yi),
-                     dz = __dsub_rn(pos[3 * v + 2], zi);
-        if (!(d2_exact(dx, dy, dz) < rc2)) continue;
-        Basis<K, L> b;
-        b.eval(dx, dy, dz, md, mu);
+    const int64_t b0 = sell_base(slab_off, i);
+    const int na = nact[i];
+    for (int a = 0; a < na; ++a) {
+        const int64_t v = act_n[b0 + kSlab * a];
+        Basis<K, L, false> b;
+        b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
         const float *cv = c + v * K;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -96,45 +128,130 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, const double *__re
         for (int m = 0; m < M; ++m) o[k * M + m] = acc[k][m];
 }
 
-// dE/dc^t of every node v (sender side): sum over the edges v sends of u_k R_k f_c, with
-// u_k = sum_m dE/dO_i[k,m] A_m of the receiving row i (Eq. 4, first term, as a VJP).
-template <int K, int L>
-__global__ __launch_bounds__(256) void k_message_grad(int64_t NN, const double *__restrict__ pos,
-                                                      const int64_t *__restrict__ t_off,
-                                                      const int32_t *__restrict__ t_recv,
-                                                      const float *__restrict__ GO, const ModelDev *__restrict__ md,
-                                                      float *__restrict__ Gc) {
+// Reverse pass of layer t over one receiver row per thread (Eq. 4 as a VJP), with
+// G = dE/dO^t_i held in registers for the whole row.  For every active edge e = (i <- v):
+//   u_k = sum_m G[k,m] A_m,       w_e[k] = u_k R_k f_c        (dE/dc^t_v contribution, t >= 1)
+//   s = sum_k c_v[k] u_k (R'_k f_c + R_k f'_c),  Q_m = sum_k c_v[k] R_k f_c G[k,m]
+//   dE/dr_e += s r/d + sum_m Q_m dA_m/dr              (accumulated over layers)
+// The receiver-side force sum is accumulated in fp64 per row.
+template <int K, int L, bool FIRST, bool WANT_W>
+__global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double *__restrict__ pos,
+                                                        const int64_t *__restrict__ slab_off,
+                                                        const int32_t *__restrict__ nact,
+                                                        const int32_t *__restrict__ act_e,
+                                                        const int32_t *__restrict__ act_n, const float *__restrict__ c,
+                                                        const float *__restrict__ GO, const ModelDev *__restrict__ md,
+                                                        float *__restrict__ w, float *__restrict__ gedge,
+                                                        double *__restrict__ Frecv) {
     constexpr int M = n_mono(L);
-    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (v >= NN) return;
+    constexpr Mono<L> mono;
+    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
+    if (i >= n) return;
     float mu[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
-    const double rc2 = md->rc2;
-    const double xv = pos[3 * v], yv = pos[3 * v + 1], zv = pos[3 * v + 2];
-    float acc[K];
+    const float ir = md->inv_rc;
+    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    float G[K][M];
+    const float *gi = GO + i * (K * M);
 #pragma unroll
-    for (int k = 0; k < K; ++k) acc[k] = 0.0f;
-    const int64_t s1 = t_off[v + 1];
-    for (int64_t s = t_off[v]; s < s1; ++s) {
-        const int64_t i = t_recv[s];
-        // same operands and order as the receiver-side test: r = x_sender - x_receiver
-        const double dx = __dsub_rn(xv, pos[3 * i]), dy = __dsub_rn(yv, pos[3 * i + 1]),
-                     dz = __dsub_rn(zv, pos[3 * i + 2]);
-        if (!(d2_exact(dx, dy, dz) < rc2)) continue;
-        Basis<K, L> b;
-        b.eval(dx, dy, dz, md, mu);
-        const float *gi = GO + i * (K * M);
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) G[k][m] = gi[k * M + m];
+    double F[3] = {0.0, 0.0, 0.0};
+    const int64_t b0 = sell_base(slab_off, i);
+    const int na = nact[i];
+    for (int a = 0; a < na; ++a) {
+        const int64_t v = act_n[b0 + kSlab * a], e = act_e[b0 + kSlab * a];
+        Basis<K, L, true> b;
+        b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
+        const float *cv = c + v * K;
+        float s = 0.0f, Q[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) Q[m] = 0.0f;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             float u = 0.0f;
 #pragma unroll
-            for (int m = 0; m < M; ++m) u += gi[k * M + m] * b.A[m];
-            acc[k] += u * b.R[k] * b.fc;
+            for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
+            const float Rf = b.R[k] * b.fc;
+            if (WANT_W) w[e * K + k] = u * Rf;
+            s += cv[k] * u * (b.dR[k] * b.fc + b.R[k] * b.dfc);
+            const float P = cv[k] * Rf;
+#pragma unroll
+            for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
+        }
+        // radial part along r/d, angular part through dA_m/dr
+        float g[3] = {s * b.rx * b.inv_d, s * b.ry * b.inv_d, s * b.rz * b.inv_d};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            const int lx = mono.lx[m], ly = mono.ly[m], lz = mono.lz[m];
+            if (lx) g[0] += Q[m] * (float)lx * b.ux[lx - 1] * b.uy[ly] * b.uz[lz] * ir;
+            if (ly) g[1] += Q[m] * (float)ly * b.ux[lx] * b.uy[ly - 1] * b.uz[lz] * ir;
+            if (lz) g[2] += Q[m] * (float)lz * b.ux[lx] * b.uy[ly] * b.uz[lz - 1] * ir;
+        }
+        float *ge = gedge + 3 * e;
+        if (FIRST) {
+            ge[0] = g[0]; ge[1] = g[1]; ge[2] = g[2];
+        } else {
+            ge[0] += g[0]; ge[1] += g[1]; ge[2] += g[2];
+        }
+        F[0] += (double)g[0];
+        F[1] += (double)g[1];
+        F[2] += (double)g[2];
+    }
+    if (FIRST) {
+        Frecv[3 * i] = F[0]; Frecv[3 * i + 1] = F[1]; Frecv[3 * i + 2] = F[2];
+    } else {
+        Frecv[3 * i] += F[0]; Frecv[3 * i + 1] += F[1]; Frecv[3 * i + 2] += F[2];
+    }
+}
+
+// Sender-major gathers use 16 lanes per node: lane q takes entries q, q+16, ... of the node's
+// list (skipping entries outside rc, tested exactly as the receiver row did), and the 16
+// partial sums are combined by a fixed butterfly, so the result is reproducible.
+constexpr int kGatherLanes = 16;
+
+__device__ __forceinline__ bool edge_active(const double *__restrict__ pos, int64_t sender, int64_t recv,
+                                            double rc2) {
+    return d2_exact(__dsub_rn(pos[3 * sender], pos[3 * recv]), __dsub_rn(pos[3 * sender + 1], pos[3 * recv + 1]),
+                    __dsub_rn(pos[3 * sender + 2], pos[3 * recv + 2])) < rc2;
+}
+
+template <class T>
+__device__ __forceinline__ T group_sum16(T x) {
+#pragma unroll
+    for (int o = kGatherLanes / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kGatherLanes);
+    return x;
+}
+
+// dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
+// term, gathered without atomics).
+template <int K>
+__global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__restrict__ t_off,
+                                                  const int32_t *__restrict__ t_recv,
+                                                  const int32_t *__restrict__ t_eid, const double *__restrict__ pos,
+                                                  double rc2, const float *__restrict__ w, float *__restrict__ Gc) {
+    const int64_t v = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
+    const int q = threadIdx.x % kGatherLanes;
+    const bool ok = v < NN;
+    float acc[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc[k] = 0.0f;
+    if (ok) {
+        const int64_t s1 = t_off[v + 1];
+        for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
+            if (!edge_active(pos, v, t_recv[s], rc2)) continue;
+            const float *we = w + (int64_t)t_eid[s] * K;
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc[k] += we[k];
         }
     }
 #pragma unroll
-    for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
+    for (int k = 0; k < K; ++k) acc[k] = group_sum16(acc[k]);
+    if (ok && q == 0)
+#pragma unroll
+        for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
 }
 
 // Ghost -> owner sum of dE/dc (the reverse ghost exchange), ghosts of an owner in order.
@@ -159,116 +276,42 @@ __global__ void k_ghost_feat(int64_t G, int64_t n, int K, const int32_t *__restr
     c[(n + g) * K + k] = c[(int64_t)owner[g] * K + k];
 }
 
-// dE/dr_e of every edge summed over the T layers (Eq. 4, both terms), one receiver row per
-// thread; layer-outer so dE/dO^t of the row stays in registers.  Writes the per-edge vectors
-// and the receiver-side force sum (fp64).
-template <int K, int L>
-__global__ __launch_bounds__(256) void k_edge_forces(int64_t n, int T, int64_t NN, const double *__restrict__ pos,
-                                                     const int64_t *__restrict__ row_off,
-                                                     const int32_t *__restrict__ nbr, const float *__restrict__ c,
-                                                     const float *__restrict__ GO, const ModelDev *__restrict__ md,
-                                                     float *__restrict__ gedge, double *__restrict__ Frecv) {
-    constexpr int M = n_mono(L);
-    constexpr Mono<L> mono;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float mu[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
-    const double rc2 = md->rc2;
-    const float inv_s2 = md->inv_s2, ir = md->inv_rc;
-    const float dfc_scale = -0.5f * md->pi_over_rc;
-    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
-    const int64_t e0 = row_off[i], e1 = row_off[i + 1];
-    double F[3] = {0.0, 0.0, 0.0};
-    for (int t = 0; t < T; ++t) {
-        float G[K][M];
-        const float *gi = GO + ((int64_t)t * n + i) * (K * M);
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-#pragma unroll
-            for (int m = 0; m < M; ++m) G[k][m] = gi[k * M + m];
-        const float *ct = c + (int64_t)t * NN * K;
-        for (int64_t e = e0; e < e1; ++e) {
-            const int64_t v = nbr[e];
-            const double dx = __dsub_rn(pos[3 * v], xi), dy = __dsub_rn(pos[3 * v + 1], yi),
-                         dz = __dsub_rn(pos[3 * v + 2], zi);
-            float g[3] = {0.0f, 0.0f, 0.0f};
-            if (d2_exact(dx, dy, dz) < rc2) {
-                Basis<K, L> b;
-                b.eval(dx, dy, dz, md, mu);
-                const float dfc = dfc_scale * sinpif(b.v);
-                const float *cv = ct + v * K;
-                float s = 0.0f, Q[M];
-#pragma unroll
-                for (int m = 0; m < M; ++m) Q[m] = 0.0f;
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    float u = 0.0f;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
-                    const float dR = -(b.d - mu[k]) * inv_s2 * b.R[k];
-                    s += cv[k] * u * (dR * b.fc + b.R[k] * dfc);
-                    const float P = cv[k] * b.R[k] * b.fc;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
-                }
-                // radial part along r/d, angular part through dA_m/dr
-                g[0] = s * b.rx * b.inv_d;
-                g[1] = s * b.ry * b.inv_d;
-                g[2] = s * b.rz * b.inv_d;
-#pragma unroll
-                for (int m = 0; m < M; ++m) {
-                    const int lx = mono.lx[m], ly = mono.ly[m], lz = mono.lz[m];
-                    if (lx) g[0] += Q[m] * (float)lx * b.ux[lx - 1] * b.uy[ly] * b.uz[lz] * ir;
-                    if (ly) g[1] += Q[m] * (float)ly * b.ux[lx] * b.uy[ly - 1] * b.uz[lz] * ir;
-                    if (lz) g[2] += Q[m] * (float)lz * b.ux[lx] * b.uy[ly] * b.uz[lz - 1] * ir;
-                }
+// F_i = sum_{edges received by i} dE/dr_e - sum_{active edges sent by i or by its ghost images}
+// dE/dr_e (r_e = r_sender - r_receiver), in fp64; 16 lanes per atom as in the gathers above.
+__global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *__restrict__ perm,
+                                                      const int64_t *__restrict__ t_off,
+                                                      const int32_t *__restrict__ t_recv,
+                                                      const int32_t *__restrict__ t_eid,
+                                                      const int64_t *__restrict__ ghost_off,
+                                                      const double *__restrict__ pos, double rc2,
+                                                      const double *__restrict__ Frecv, const float *__restrict__ gedge,
+                                                      double *__restrict__ F, double *__restrict__ Fcaller) {
+    const int64_t i = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
+    const int q = threadIdx.x % kGatherLanes;
+    const bool ok = i < n;
+    double f[3] = {0.0, 0.0, 0.0};
+    if (ok) {
+        const int64_t g0 = ghost_off[i], g1 = ghost_off[i + 1];
+        for (int64_t vv = -1; vv < g1 - g0; ++vv) {       // the atom itself, then its ghost images
+            const int64_t v = vv < 0 ? i : n + g0 + vv;
+            const int64_t s1 = t_off[v + 1];
+            for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
+                if (!edge_active(pos, v, t_recv[s], rc2)) continue;
+                const float *ge = gedge + 3 * (int64_t)t_eid[s];
+                f[0] -= (double)ge[0];
+                f[1] -= (double)ge[1];
+                f[2] -= (double)ge[2];
             }
-            float *ge = gedge + 3 * e;
-            if (t == 0) {
-                ge[0] = g[0]; ge[1] = g[1]; ge[2] = g[2];
-            } else {
-                ge[0] += g[0]; ge[1] += g[1]; ge[2] += g[2];
-            }
-            F[0] += (double)g[0];
-            F[1] += (double)g[1];
-            F[2] += (double)g[2];
         }
     }
-    Frecv[3 * i] = F[0];
-    Frecv[3 * i + 1] = F[1];
-    Frecv[3 * i + 2] = F[2];
-}
-
-// F_i = sum_{edges received by i} dE/dr_e - sum_{edges sent by i or by its ghost images} dE/dr_e
-// (r_e = r_sender - r_receiver), in fp64, in the fixed order of the transposed lists.
-__global__ void k_force_gather(int64_t n, const int32_t *__restrict__ perm, const int64_t *__restrict__ t_off,
-                               const int32_t *__restrict__ t_eid, const int64_t *__restrict__ ghost_off,
-                               const double *__restrict__ Frecv, const float *__restrict__ gedge,
-                               double *__restrict__ F, double *__restrict__ Fcaller) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    double f[3] = {Frecv[3 * i], Frecv[3 * i + 1], Frecv[3 * i + 2]};
-    for (int64_t s = t_off[i]; s < t_off[i + 1]; ++s) {
-        const int64_t e = t_eid[s];
-        f[0] -= (double)gedge[3 * e];
-        f[1] -= (double)gedge[3 * e + 1];
-        f[2] -= (double)gedge[3 * e + 2];
-    }
-    for (int64_t g = ghost_off[i]; g < ghost_off[i + 1]; ++g) {
-        const int64_t v = n + g;
-        for (int64_t s = t_off[v]; s < t_off[v + 1]; ++s) {
-            const int64_t e = t_eid[s];
-            f[0] -= (double)gedge[3 * e];
-            f[1] -= (double)gedge[3 * e + 1];
-            f[2] -= (double)gedge[3 * e + 2];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) f[a] = group_sum16(f[a]);
+    if (ok && q == 0) {
+        for (int a = 0; a < 3; ++a) {
+            const double v = Frecv[3 * i + a] + f[a];
+            F[3 * i + a] = v;
+            if (Fcaller) Fcaller[3 * (int64_t)perm[i] + a] = v;
         }
-    }
-    for (int a = 0; a < 3; ++a) F[3 * i + a] = f[a];
-    if (Fcaller) {
-        const int64_t c = perm[i];
-        for (int a = 0; a < 3; ++a) Fcaller[3 * c + a] = f[a];
     }
 }
 
@@ -283,14 +326,24 @@ __global__ void k_force_gather(int64_t n, const int32_t *__restrict__ perm, cons
 
 }  // namespace
 
+Status compact_active(Context &cx) {
+    ProfScope ps_(cx, kProfCompact);
+    if (cx.n == 0) return Status::ok();
+    k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
+                                                        cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(), cx.rc * cx.rc, cx.act_e.as<int32_t>(),
+                                                        cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
 Status aggregate(Context &cx, int t) {
     ProfScope ps_(cx, kProfAggregate);
     if (cx.n == 0) return Status::ok();
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_for(cx.n), kBlock, 0, cx.stream>>>(
-                                      cx.n, cx.pos.as<double>(), cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(),
-                                      ct, cx.model.as<ModelDev>(), Ot)));
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
+                                      cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),
+                                      cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), Ot)));
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
@@ -304,14 +357,45 @@ Status refresh_ghost_features(Context &cx, int t) {
     return Status::ok();
 }
 
-Status backward_messages(Context &cx, int t) {
+Status backward_layer(Context &cx, int t) {
+    ProfScope ps_(cx, kProfBackwardLayer);
     if (cx.n == 0) return Status::ok();
+    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
     const float *GOt = cx.GO.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
+    const bool first = (t == cx.T - 1), want_w = (t >= 1);
+#define MPNN_BWD(FIRST_, W_)                                                                               \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+                                      cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
+                                      cx.act_e.as<int32_t>(), cx.act_n.as<int32_t>(), ct, GOt,                     \
+                                      cx.model.as<ModelDev>(), cx.w.as<float>(), cx.gedge.as<float>(),             \
+                                      cx.Frecv.as<double>())))
+    if (first && want_w) MPNN_BWD(true, true);
+    else if (first) MPNN_BWD(true, false);
+    else if (want_w) MPNN_BWD(false, true);
+    else MPNN_BWD(false, false);
+#undef MPNN_BWD
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status backward_messages(Context &cx, int t) {
+    (void)t;
+    if (cx.n == 0) return Status::ok();
     {
         ProfScope ps_(cx, kProfMessageGrad);
-        MPNN_DISPATCH_KL(cx.K, cx.L, (k_message_grad<KK, LL><<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(
-                                          cx.NN, cx.pos.as<double>(), cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(),
-                                          GOt, cx.model.as<ModelDev>(), cx.Gc.as<float>())));
+        const unsigned gg = grid_xcd(cx.NN * kGatherLanes);
+#define MPNN_GW(KK)                                                                                        \
+    k_gather_w<KK><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(),       \
+                                                 cx.t_eid.as<int32_t>(), cx.pos.as<double>(), cx.rc * cx.rc,  \
+                                                 cx.w.as<float>(), cx.Gc.as<float>())
+        switch (cx.K) {
+            case 2: MPNN_GW(2); break;
+            case 4: MPNN_GW(4); break;
+            case 8: MPNN_GW(8); break;
+            case 12: MPNN_GW(12); break;
+            default: return Status::err(MPNN_E_INVALID_ARG, "unsupported K");
+        }
+#undef MPNN_GW
         MPNN_HIP(hipGetLastError());
     }
     ProfScope ps_(cx, kProfGhostFold);
@@ -321,24 +405,13 @@ Status backward_messages(Context &cx, int t) {
     return Status::ok();
 }
 
-Status force_edges(Context &cx) {
-    ProfScope ps_(cx, kProfEdgeForces);
-    if (cx.n == 0) return Status::ok();
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_edge_forces<KK, LL><<<grid_for(cx.n), kBlock, 0, cx.stream>>>(
-                                      cx.n, cx.T, cx.NN, cx.pos.as<double>(), cx.row_off.as<int64_t>(),
-                                      cx.nbr.as<int32_t>(), cx.c.as<float>(), cx.GO.as<float>(),
-                                      cx.model.as<ModelDev>(), cx.gedge.as<float>(), cx.Frecv.as<double>())));
-    MPNN_HIP(hipGetLastError());
-    return Status::ok();
-}
-
 Status force_gather(Context &cx, double *F_caller) {
     ProfScope ps_(cx, kProfForceGather);
     if (cx.n == 0) return Status::ok();
-    k_force_gather<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(),
-                                                            cx.t_eid.as<int32_t>(), cx.ghost_off.as<int64_t>(),
-                                                            cx.Frecv.as<double>(), cx.gedge.as<float>(),
-                                                            cx.F.as<double>(), F_caller);
+    k_force_gather<<<grid_xcd(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(
+        cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(), cx.t_eid.as<int32_t>(),
+        cx.ghost_off.as<int64_t>(), cx.pos.as<double>(), cx.rc * cx.rc, cx.Frecv.as<double>(), cx.gedge.as<float>(),
+        cx.F.as<double>(), F_caller);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

@@ -39,9 +39,9 @@ struct Status {
 // Kernel families timed by the optional event profiler (mpnn_set_profiling).
 enum ProfId {
     kProfBuildSort = 0, kProfBuildGhost, kProfBuildRows, kProfBuildTranspose, kProfBuildSpecies,
-    kProfGhostPos, kProfAggregate, kProfNetForward, kProfNetEnergy, kProfNetBackward, kProfGhostFeat,
-    kProfMessageGrad, kProfGhostFold, kProfEdgeForces, kProfForceGather, kProfKickDrift, kProfKick,
-    kProfReduce, kProfCount
+    kProfGhostPos, kProfCompact, kProfAggregate, kProfNetForward, kProfNetEnergy, kProfNetBackward,
+    kProfGhostFeat, kProfBackwardLayer, kProfMessageGrad, kProfGhostFold, kProfForceGather,
+    kProfKickDrift, kProfKick, kProfReduce, kProfCount
 };
 extern const char *const kProfNames[kProfCount];
 
@@ -72,7 +72,7 @@ struct Context {
     // ---- system ----
     bool built = false;
     bool forces_valid = false;  // F_sorted matches the current positions
-    int64_t n = 0, G = 0, NN = 0, E = 0;
+    int64_t n = 0, G = 0, NN = 0, E = 0, E_sell = 0;
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
     int nc[3] = {0, 0, 0};      // interior cells per axis
@@ -89,7 +89,10 @@ struct Context {
     Buf types;                      // int32 [NN]
     Buf ghost_owner, ghost_code;    // int32 [G]
     Buf ghost_off;                  // int64 [n+1] ghosts of each owner
-    Buf row_off, nbr;               // int64 [n+1], int32 [E]
+    Buf row_off;                    // int64 [n+1] prefix of row lengths (canonical pair order)
+    Buf row_len;                    // int32 [n] Verlet entries per row
+    Buf slab_off;                   // int64 [n/64+2] start of each 64-row slab
+    Buf nbr;                        // int32 [E_sell] sender node of each entry (sliced ELLPACK)
     Buf t_off, t_recv, t_eid;       // int64 [NN+1], int32 [E], int32 [E]
     Buf sp_list, sp_off;            // int32 [n], int64 [S+1]
 
@@ -98,7 +101,10 @@ struct Context {
     Buf O;        // float [T][n][K*M]
     Buf GO;       // float [T][n][K*M]
     Buf Gc;       // float [NN][K]
-    Buf gedge;    // float [E][3]
+    Buf gedge;    // float [E][3]  dE/dr_e summed over layers
+    Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
+    Buf act_e, act_n;  // int32 [E]: active entries of each row (list index, sender node)
+    Buf nact;     // int32 [n] active entries per row
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
     Buf Ei;       // float [n]
@@ -150,10 +156,11 @@ Status refresh_ghost_positions(Context &cx);
 Status get_pairs(Context &cx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j, int32_t *s);
 
 // ---- edges.hip ----
+Status compact_active(Context &cx);               // per-step active entries (d < rc)
 Status aggregate(Context &cx, int t);
 Status refresh_ghost_features(Context &cx, int t);
+Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold
-Status force_edges(Context &cx);                  // dE/dr_e over all layers, receiver sums
 Status force_gather(Context &cx, double *F_caller);
 
 // ---- mlp.hip ----

@@ -85,6 +85,40 @@ __global__ void k_sort_segments(int64_t nseg, const int64_t *__restrict__ off, i
     }
 }
 
+// One wave per segment: every element's rank is the count of smaller keys in the segment
+// (keys are distinct), so the result does not depend on the scatter order.  Segments longer
+// than the LDS tile fall back to the insertion sort on one lane.
+constexpr int kRankTile = 512;
+__global__ __launch_bounds__(64) void k_rank_sort_segments(int64_t nseg, const int64_t *__restrict__ off,
+                                                          int32_t *__restrict__ v) {
+    __shared__ int32_t sh[kRankTile];
+    const int64_t s = blockIdx.x;
+    if (s >= nseg) return;
+    const int64_t b = off[s], len = off[s + 1] - b;
+    if (len <= 1) return;
+    if (len > kRankTile) {
+        if (threadIdx.x == 0)
+            for (int64_t p = b + 1; p < b + len; ++p) {
+                int32_t x = v[p];
+                int64_t q = p - 1;
+                while (q >= b && v[q] > x) {
+                    v[q + 1] = v[q];
+                    --q;
+                }
+                v[q + 1] = x;
+            }
+        return;
+    }
+    for (int j = threadIdx.x; j < len; j += 64) sh[j] = v[b + j];
+    __syncthreads();
+    for (int j = threadIdx.x; j < len; j += 64) {
+        const int32_t x = sh[j];
+        int r = 0;
+        for (int q = 0; q < len; ++q) r += sh[q] < x;
+        v[b + r] = x;
+    }
+}
+
 // Same, carrying a payload along with the key.
 __global__ void k_sort_segments_kv(int64_t nseg, const int64_t *__restrict__ off,
                                    int32_t *__restrict__ k, int32_t *__restrict__ v) {
@@ -193,7 +227,7 @@ __global__ void k_ext_key(int64_t NN, const double *__restrict__ pos, Grid g, in
 template <bool FILL>
 __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
                        const int64_t *__restrict__ coff, const int32_t *__restrict__ cnodes,
-                       double rcut2, int32_t *__restrict__ cnt, const int64_t *__restrict__ row_off,
+                       double rcut2, int32_t *__restrict__ cnt, const int64_t *__restrict__ slab_off,
                        int32_t *__restrict__ nbr) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -202,7 +236,8 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
     const int cy = ext_cell(yi, g.h[1], g.n[1]);
     const int cz = ext_cell(zi, g.h[2], g.n[2]);
     const int ny = g.n[1] + 2, nz = g.n[2] + 2;
-    int64_t o = FILL ? row_off[i] : 0;
+    const int64_t base = FILL ? sell_base(slab_off, i) : 0;
+    int64_t o = 0;
     int32_t c = 0;
     for (int dx = -1; dx <= 1; ++dx) {
         int x = cx + dx;
@@ -221,7 +256,7 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
                                          __dsub_rn(pos[3 * (int64_t)v + 1], yi),
                                          __dsub_rn(pos[3 * (int64_t)v + 2], zi));
                     if (d2 < rcut2) {
-                        if (FILL) nbr[o++] = v;
+                        if (FILL) nbr[base + kSlab * (o++)] = v;
                         else ++c;
                     }
                 }
@@ -231,29 +266,43 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
     if (!FILL) cnt[i] = c;
 }
 
-__global__ void k_tcount(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
-                         int32_t *__restrict__ cnt) {
+__global__ void k_tcount(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
+                         const int32_t *__restrict__ nbr, int32_t *__restrict__ cnt) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) atomicAdd(&cnt[nbr[e]], 1);
+    const int64_t b = sell_base(slab_off, i);
+    for (int j = 0; j < len[i]; ++j) atomicAdd(&cnt[nbr[b + kSlab * j]], 1);
 }
 
-__global__ void k_tfill(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
-                        const int64_t *__restrict__ t_off, int32_t *__restrict__ cursor,
-                        int32_t *__restrict__ t_eid) {
+__global__ void k_tfill(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
+                        const int32_t *__restrict__ nbr, const int64_t *__restrict__ t_off,
+                        int32_t *__restrict__ cursor, int32_t *__restrict__ t_eid) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) {
-        int32_t v = nbr[e];
+    const int64_t b = sell_base(slab_off, i);
+    for (int j = 0; j < len[i]; ++j) {
+        const int64_t e = b + kSlab * j;
+        const int32_t v = nbr[e];
         t_eid[t_off[v] + atomicAdd(&cursor[v], 1)] = (int32_t)e;
     }
 }
 
-// Receiver of every edge (rows are contiguous).
-__global__ void k_edge_receiver(int64_t n, const int64_t *__restrict__ row_off, int32_t *__restrict__ recv) {
+// Receiver of every entry.
+__global__ void k_edge_receiver(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
+                                int32_t *__restrict__ recv) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    for (int64_t e = row_off[i]; e < row_off[i + 1]; ++e) recv[e] = (int32_t)i;
+    const int64_t b = sell_base(slab_off, i);
+    for (int j = 0; j < len[i]; ++j) recv[b + kSlab * j] = (int32_t)i;
+}
+
+// Width of each 64-row slab (its longest row), times 64.
+__global__ void k_slab_width(int64_t n, int64_t nslab, const int32_t *__restrict__ len, int32_t *__restrict__ sw) {
+    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nslab) return;
+    int w = 0;
+    for (int64_t i = s * kSlab; i < (s + 1) * kSlab && i < n; ++i) w = len[i] > w ? len[i] : w;
+    sw[s] = w * kSlab;
 }
 
 __global__ void k_tmap_recv(int64_t E, const int32_t *__restrict__ t_eid, const int32_t *__restrict__ recv_of_edge,
@@ -288,14 +337,15 @@ __global__ void k_validate(int64_t n, const double *__restrict__ p, const int32_
     if (i < n && (types[i] < 0 || types[i] >= S)) atomicOr(bad, 2);
 }
 
-__global__ void k_pairs(int64_t n, const int64_t *__restrict__ row_off, const int32_t *__restrict__ nbr,
-                        const int32_t *__restrict__ perm, const int32_t *__restrict__ ghost_owner,
-                        const int32_t *__restrict__ ghost_code, int64_t cap, int32_t *__restrict__ pi,
-                        int32_t *__restrict__ pj, int32_t *__restrict__ ps) {
+__global__ void k_pairs(int64_t n, const int64_t *__restrict__ row_off, const int64_t *__restrict__ slab_off,
+                        const int32_t *__restrict__ nbr, const int32_t *__restrict__ perm,
+                        const int32_t *__restrict__ ghost_owner, const int32_t *__restrict__ ghost_code, int64_t cap,
+                        int32_t *__restrict__ pi, int32_t *__restrict__ pj, int32_t *__restrict__ ps) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
+    const int64_t b = sell_base(slab_off, i);
     for (int64_t e = row_off[i]; e < row_off[i + 1] && e < cap; ++e) {
-        int32_t v = nbr[e];
+        int32_t v = nbr[b + kSlab * (e - row_off[i])];
         int sx = 0, sy = 0, sz = 0;
         int32_t o = v;
         if (v >= n) {
@@ -465,17 +515,29 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     k_rows<false><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, cnt,
                                                          nullptr, nullptr);
     MPNN_HIP(hipGetLastError());
+    MPNN_TRY(cx.grow(cx.row_len, sizeof(int32_t) * n1));
+    if (n > 0)
+        MPNN_HIP(hipMemcpyAsync(cx.row_len.p, cnt, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, cx.stream));
     MPNN_TRY(exclusive_scan(cx, cnt, n, cx.row_off.as<int64_t>()));
     int64_t E = 0;
     MPNN_TRY(fetch(cx, cx.row_off.as<int64_t>() + n, &E));
     if (E > INT32_MAX) return Status::err(MPNN_E_CAPACITY, "more than 2^31-1 neighbour entries");
     cx.E = E;
-    const int64_t E1 = E > 0 ? E : 1;
+    // slab layout: width of a slab = its longest row
+    const int64_t nslab = (n + kSlab - 1) / kSlab;
+    MPNN_TRY(cx.grow(cx.slab_off, sizeof(int64_t) * (size_t)(nslab + 2)));
+    k_slab_width<<<grid_for(nslab), kBlock, 0, cx.stream>>>(n, nslab, cx.row_len.as<int32_t>(), cnt);
+    MPNN_HIP(hipGetLastError());
+    MPNN_TRY(exclusive_scan(cx, cnt, nslab, cx.slab_off.as<int64_t>()));
+    int64_t Es = 0;
+    MPNN_TRY(fetch(cx, cx.slab_off.as<int64_t>() + nslab, &Es));
+    if (Es > INT32_MAX) return Status::err(MPNN_E_CAPACITY, "more than 2^31-1 neighbour slots");
+    cx.E_sell = Es;
+    const int64_t E1 = Es > 0 ? Es : 1;
     MPNN_TRY(cx.grow(cx.nbr, sizeof(int32_t) * E1));
     k_rows<true><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, nullptr,
-                                                        cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>());
+                                                        cx.slab_off.as<int64_t>(), cx.nbr.as<int32_t>());
     MPNN_HIP(hipGetLastError());
-
     cx.prof_end(kProfBuildRows);
 
     // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
@@ -486,20 +548,24 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)NN1 + 64));
     cnt = cx.tmp_c.as<int32_t>();
     MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
-    k_tcount<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(), cnt);
+    k_tcount<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
+                                                    cx.nbr.as<int32_t>(), cnt);
     MPNN_HIP(hipGetLastError());
     MPNN_TRY(exclusive_scan(cx, cnt, cx.NN, cx.t_off.as<int64_t>()));
     MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
-    k_tfill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(),
-                                                   cx.t_off.as<int64_t>(), cnt, cx.t_eid.as<int32_t>());
+    k_tfill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
+                                                   cx.nbr.as<int32_t>(), cx.t_off.as<int64_t>(), cnt,
+                                                   cx.t_eid.as<int32_t>());
     MPNN_HIP(hipGetLastError());
-    k_sort_segments<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>());
+    if (cx.NN > 0)
+        k_rank_sort_segments<<<(unsigned)cx.NN, 64, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     {
         // receiver of each edge, then of each transposed entry (reuses the gradient buffer)
         MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
         int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p);
-        k_edge_receiver<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.row_off.as<int64_t>(), recv);
+        k_edge_receiver<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(),
+                                                               cx.row_len.as<int32_t>(), recv);
         MPNN_HIP(hipGetLastError());
         k_tmap_recv<<<grid_for(E), kBlock, 0, cx.stream>>>(E, cx.t_eid.as<int32_t>(), recv, cx.t_recv.as<int32_t>());
         MPNN_HIP(hipGetLastError());
@@ -536,6 +602,10 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * n1 * KM));
     MPNN_TRY(cx.grow(cx.GO, sizeof(float) * (size_t)cx.T * n1 * KM));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.act_e, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
+    if (cx.T > 1) MPNN_TRY(cx.grow(cx.w, sizeof(float) * (size_t)E1 * cx.K));
     MPNN_TRY(cx.grow(cx.Frecv, sizeof(double) * 3 * n1));
     MPNN_TRY(cx.grow(cx.F, sizeof(double) * 3 * n1));
     MPNN_TRY(cx.grow(cx.Ei, sizeof(float) * n1));
@@ -563,7 +633,8 @@ Status refresh_ghost_positions(Context &cx) {
 Status get_pairs(Context &cx, int64_t cap, int64_t *n_pairs, int32_t *i, int32_t *j, int32_t *s) {
     *n_pairs = cx.E;
     if (cap <= 0 || cx.E == 0) return Status::ok();
-    k_pairs<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.row_off.as<int64_t>(), cx.nbr.as<int32_t>(),
+    k_pairs<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.row_off.as<int64_t>(), cx.slab_off.as<int64_t>(),
+                                                      cx.nbr.as<int32_t>(),
                                                       cx.perm.as<int32_t>(), cx.ghost_owner.as<int32_t>(),
                                                       cx.ghost_code.as<int32_t>(), cap, i, j, s);
     MPNN_HIP(hipGetLastError());
