@@ -102,7 +102,7 @@ Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &GO, &Gc,
-                  &gedge, &w, &act_e, &act_n, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
+                  &gedge, &w, &amap, &act_n, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel};
     for (Buf *b : all) release(*b);

@@ -60,13 +60,15 @@ struct Basis {
 };
 
 // Per-step active list: the Verlet entries of each row with d^2 < rc^2 (fp64, the same
-// expression as the build), compacted in row order.  Per-edge outputs of inactive entries are
-// never written; the sender-major gathers repeat the same test on the same operands.
+// expression as the build), compacted in row order into the row's leading slots (sender node of
+// active entry a at slot base + 64 a), plus the map from every Verlet slot to its active slot
+// (-1: outside rc).  Per-edge outputs live in active slots, so the row kernels write them
+// coalesced and the sender-major gathers find them through the map.
 __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
                                                  const int64_t *__restrict__ slab_off,
                                                  const int32_t *__restrict__ len,
                                                  const int32_t *__restrict__ nbr, double rc2,
-                                                 int32_t *__restrict__ act_e, int32_t *__restrict__ act_n,
+                                                 int32_t *__restrict__ amap, int32_t *__restrict__ act_n,
                                                  int32_t *__restrict__ nact) {
     const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -80,9 +82,11 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
         const double d2 = d2_exact(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi),
                                    __dsub_rn(pos[3 * v + 2], zi));
         if (d2 < rc2) {
-            act_e[b + kSlab * o] = (int32_t)e;
             act_n[b + kSlab * o] = (int32_t)v;
+            amap[e] = (int32_t)(b + kSlab * o);
             ++o;
+        } else {
+            amap[e] = -1;
         }
     }
     nact[i] = o;
@@ -138,7 +142,6 @@ template <int K, int L, bool FIRST, bool WANT_W>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
-                                                        const int32_t *__restrict__ act_e,
                                                         const int32_t *__restrict__ act_n, const float *__restrict__ c,
                                                         const float *__restrict__ GO, const ModelDev *__restrict__ md,
                                                         float *__restrict__ w, float *__restrict__ gedge,
@@ -162,7 +165,8 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double 
     const int64_t b0 = sell_base(slab_off, i);
     const int na = nact[i];
     for (int a = 0; a < na; ++a) {
-        const int64_t v = act_n[b0 + kSlab * a], e = act_e[b0 + kSlab * a];
+        const int64_t e = b0 + kSlab * a;   // active slot: per-edge outputs are stored here
+        const int64_t v = act_n[e];
         Basis<K, L, true> b;
         b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
         const float *cv = c + v * K;
@@ -212,12 +216,6 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double 
 // partial sums are combined by a fixed butterfly, so the result is reproducible.
 constexpr int kGatherLanes = 16;
 
-__device__ __forceinline__ bool edge_active(const double *__restrict__ pos, int64_t sender, int64_t recv,
-                                            double rc2) {
-    return d2_exact(__dsub_rn(pos[3 * sender], pos[3 * recv]), __dsub_rn(pos[3 * sender + 1], pos[3 * recv + 1]),
-                    __dsub_rn(pos[3 * sender + 2], pos[3 * recv + 2])) < rc2;
-}
-
 template <class T>
 __device__ __forceinline__ T group_sum16(T x) {
 #pragma unroll
@@ -229,9 +227,8 @@ __device__ __forceinline__ T group_sum16(T x) {
 // term, gathered without atomics).
 template <int K>
 __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__restrict__ t_off,
-                                                  const int32_t *__restrict__ t_recv,
-                                                  const int32_t *__restrict__ t_eid, const double *__restrict__ pos,
-                                                  double rc2, const float *__restrict__ w, float *__restrict__ Gc) {
+                                                  const int32_t *__restrict__ t_eid, const int32_t *__restrict__ amap,
+                                                  const float *__restrict__ w, float *__restrict__ Gc) {
     const int64_t v = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
     const int q = threadIdx.x % kGatherLanes;
     const bool ok = v < NN;
@@ -241,8 +238,9 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
     if (ok) {
         const int64_t s1 = t_off[v + 1];
         for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-            if (!edge_active(pos, v, t_recv[s], rc2)) continue;
-            const float *we = w + (int64_t)t_eid[s] * K;
+            const int32_t a = amap[t_eid[s]];
+            if (a < 0) continue;
+            const float *we = w + (int64_t)a * K;
 #pragma unroll
             for (int k = 0; k < K; ++k) acc[k] += we[k];
         }
@@ -280,10 +278,9 @@ __global__ void k_ghost_feat(int64_t G, int64_t n, int K, const int32_t *__restr
 // dE/dr_e (r_e = r_sender - r_receiver), in fp64; 16 lanes per atom as in the gathers above.
 __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *__restrict__ perm,
                                                       const int64_t *__restrict__ t_off,
-                                                      const int32_t *__restrict__ t_recv,
                                                       const int32_t *__restrict__ t_eid,
+                                                      const int32_t *__restrict__ amap,
                                                       const int64_t *__restrict__ ghost_off,
-                                                      const double *__restrict__ pos, double rc2,
                                                       const double *__restrict__ Frecv, const float *__restrict__ gedge,
                                                       double *__restrict__ F, double *__restrict__ Fcaller) {
     const int64_t i = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
@@ -296,8 +293,9 @@ __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *
             const int64_t v = vv < 0 ? i : n + g0 + vv;
             const int64_t s1 = t_off[v + 1];
             for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-                if (!edge_active(pos, v, t_recv[s], rc2)) continue;
-                const float *ge = gedge + 3 * (int64_t)t_eid[s];
+                const int32_t a = amap[t_eid[s]];
+                if (a < 0) continue;
+                const float *ge = gedge + 3 * (int64_t)a;
                 f[0] -= (double)ge[0];
                 f[1] -= (double)ge[1];
                 f[2] -= (double)ge[2];
@@ -330,7 +328,7 @@ Status compact_active(Context &cx) {
     ProfScope ps_(cx, kProfCompact);
     if (cx.n == 0) return Status::ok();
     k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
-                                                        cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(), cx.rc * cx.rc, cx.act_e.as<int32_t>(),
+                                                        cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(), cx.rc * cx.rc, cx.amap.as<int32_t>(),
                                                         cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     return Status::ok();
@@ -366,7 +364,7 @@ Status backward_layer(Context &cx, int t) {
 #define MPNN_BWD(FIRST_, W_)                                                                               \
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
-                                      cx.act_e.as<int32_t>(), cx.act_n.as<int32_t>(), ct, GOt,                     \
+                                      cx.act_n.as<int32_t>(), ct, GOt,                                             \
                                       cx.model.as<ModelDev>(), cx.w.as<float>(), cx.gedge.as<float>(),             \
                                       cx.Frecv.as<double>())))
     if (first && want_w) MPNN_BWD(true, true);
@@ -385,9 +383,8 @@ Status backward_messages(Context &cx, int t) {
         ProfScope ps_(cx, kProfMessageGrad);
         const unsigned gg = grid_xcd(cx.NN * kGatherLanes);
 #define MPNN_GW(KK)                                                                                        \
-    k_gather_w<KK><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(),       \
-                                                 cx.t_eid.as<int32_t>(), cx.pos.as<double>(), cx.rc * cx.rc,  \
-                                                 cx.w.as<float>(), cx.Gc.as<float>())
+    k_gather_w<KK><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(),         \
+                                                 cx.amap.as<int32_t>(), cx.w.as<float>(), cx.Gc.as<float>())
         switch (cx.K) {
             case 2: MPNN_GW(2); break;
             case 4: MPNN_GW(4); break;
@@ -409,8 +406,8 @@ Status force_gather(Context &cx, double *F_caller) {
     ProfScope ps_(cx, kProfForceGather);
     if (cx.n == 0) return Status::ok();
     k_force_gather<<<grid_xcd(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(
-        cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(), cx.t_recv.as<int32_t>(), cx.t_eid.as<int32_t>(),
-        cx.ghost_off.as<int64_t>(), cx.pos.as<double>(), cx.rc * cx.rc, cx.Frecv.as<double>(), cx.gedge.as<float>(),
+        cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.amap.as<int32_t>(),
+        cx.ghost_off.as<int64_t>(), cx.Frecv.as<double>(), cx.gedge.as<float>(),
         cx.F.as<double>(), F_caller);
     MPNN_HIP(hipGetLastError());
     return Status::ok();

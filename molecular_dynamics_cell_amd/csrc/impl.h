@@ -103,7 +103,8 @@ struct Context {
     Buf Gc;       // float [NN][K]
     Buf gedge;    // float [E][3]  dE/dr_e summed over layers
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
-    Buf act_e, act_n;  // int32 [E]: active entries of each row (list index, sender node)
+    Buf amap;     // int32 [E]: active slot of each Verlet slot this step (-1: d >= rc)
+    Buf act_n;    // int32 [E]: sender node of each active slot
     Buf nact;     // int32 [n] active entries per row
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)

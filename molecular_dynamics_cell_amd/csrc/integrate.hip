@@ -83,19 +83,28 @@ __global__ void k_kick_drift(int64_t n, double dt, double half_skin2, const int3
                              double *__restrict__ vel, double *__restrict__ pos, const double *__restrict__ ref,
                              unsigned long long *__restrict__ flag) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const double a = 0.5 * dt * kAccel / md->mass[types[i]];
     double d2 = 0.0;
-    for (int c = 0; c < 3; ++c) {
-        const double v = vel[3 * i + c] + a * F[3 * i + c];
-        vel[3 * i + c] = v;
-        const double x = pos[3 * i + c] + dt * v;
-        pos[3 * i + c] = x;
-        const double dd = x - ref[3 * i + c];
-        d2 += dd * dd;
+    if (i < n) {
+        const double a = 0.5 * dt * kAccel / md->mass[types[i]];
+        for (int c = 0; c < 3; ++c) {
+            const double v = vel[3 * i + c] + a * F[3 * i + c];
+            vel[3 * i + c] = v;
+            const double x = pos[3 * i + c] + dt * v;
+            pos[3 * i + c] = x;
+            const double dd = x - ref[3 * i + c];
+            d2 += dd * dd;
+        }
     }
-    if (d2 > half_skin2) atomicOr(&flag[0], 1ull);
-    atomicMax(&flag[1], (unsigned long long)__double_as_longlong(d2));
+    // one atomic per wave: wave maximum of d2 (non-negative doubles order like their bits)
+    unsigned long long bits = (unsigned long long)__double_as_longlong(d2);
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long other = __shfl_xor(bits, o);
+        bits = other > bits ? other : bits;
+    }
+    if ((threadIdx.x & 63) == 0) {
+        if (__longlong_as_double((long long)bits) > half_skin2) atomicOr(&flag[0], 1ull);
+        atomicMax(&flag[1], bits);
+    }
 }
 
 __global__ void k_skin_check(int64_t n, double half_skin2, const double *__restrict__ pos,

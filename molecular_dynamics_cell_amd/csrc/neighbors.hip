@@ -602,7 +602,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * n1 * KM));
     MPNN_TRY(cx.grow(cx.GO, sizeof(float) * (size_t)cx.T * n1 * KM));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)NN1 * cx.K));
-    MPNN_TRY(cx.grow(cx.act_e, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.amap, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
     if (cx.T > 1) MPNN_TRY(cx.grow(cx.w, sizeof(float) * (size_t)E1 * cx.K));
