@@ -76,8 +76,38 @@ def kernel_model(fam, g):
     return None
 
 
-def roofline_for(fam, ms_avg, g):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ag2m.json")
+
+
+def csrc_digest():
+    """SHA-256 over the HIP sources, to tell whether stored counter readings are current."""
+    import hashlib
+    d = os.path.join(ROOT, "molecular_dynamics_cell_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(fam, cfg):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE readings (scaled
+    by the copy-kernel calibration), or None if absent or taken on different kernel sources."""
+    if cfg != 4 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(fam)
+    if k is None or t.get("source_sha256") != csrc_digest():
+        return None
+    return int((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024)
+
+
+def roofline_for(fam, ms_avg, g, cfg=4):
     bytes_, flops, kind = kernel_model(fam, g)
+    traffic = measured_traffic(fam, cfg)
     t = ms_avg * 1e-3
     gbs = bytes_ / t / 1e9
     tfs = flops / t / 1e12
@@ -85,11 +115,11 @@ def roofline_for(fam, ms_avg, g):
     t_cmp = flops / ((FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS) * 1e12)
     if kind == "hbm" or t_hbm >= t_cmp:
         return {"kernel": fam, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": int(bytes_), "avg_ms": round(ms_avg, 4)}
     peak = FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS
     return {"kernel": fam, "bound": "mfma" if kind == "mfma" else "alu", "achieved": round(tfs, 2),
-            "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": None,
+            "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": traffic,
             "algorithmic_flops": int(flops), "algorithmic_bytes": int(bytes_),
             "hbm_GBs_at_algorithmic_bytes": round(gbs, 1), "avg_ms": round(ms_avg, 4)}
 
@@ -209,9 +239,9 @@ def main():
     modeled = [k for k in kernels if kernel_model(k, g) is not None]
     if modeled:
         dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
-        roof = roofline_for(dom, kernels[dom]["ms_avg"], g)
+        roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg)
     for k in modeled:
-        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g)
+        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg)
 
     out = {
         "metric": METRIC,

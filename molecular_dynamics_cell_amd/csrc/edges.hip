@@ -13,9 +13,24 @@ namespace mpnn {
 
 namespace {
 
+// sin and cos of theta = (pi/2) v for v in [0, 1], from their Taylor series (error terms
+// theta^15/15! and theta^14/14!, below 1e-8 on [0, pi/2]); pi/2 is split into two floats so the
+// argument carries no rounding bias.
+__device__ __forceinline__ void sincos_half_pi(float v, float &s, float &c) {
+    const float t = fmaf(v, 1.57079637f, v * -4.37113900e-8f);
+    const float t2 = t * t;
+    s = t * fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, 1.0f / 6227020800.0f, -1.0f / 39916800.0f),
+                                                     1.0f / 362880.0f), -1.0f / 5040.0f), 1.0f / 120.0f),
+                             -1.0f / 6.0f), 1.0f);
+    c = fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, fmaf(t2, 1.0f / 479001600.0f, -1.0f / 3628800.0f),
+                                                 1.0f / 40320.0f), -1.0f / 720.0f), 1.0f / 24.0f), -0.5f), 1.0f);
+}
+
 // Edge basis of one edge, fp32, from the fp64 displacement: hardware exp2 of a pre-scaled
-// argument for the Gaussians, correctly rounded sqrt and 1/d, the accurate cospi/sinpi for the
-// cutoff (the hardware sqrt and cos/sin shifted the total energy by several 1e-6 relative).
+// argument for the Gaussians, correctly rounded sqrt and 1/d, and the cutoff written as
+// f_c = (1 + cos(pi v))/2 = cos^2(pi v/2), f_c' = -(pi/rc) sin(pi v/2) cos(pi v/2), which has no
+// cancellation near rc.  (The hardware sqrt and cos/sin shifted the total energy by several
+// 1e-6 relative.)
 template <int K, int L, bool DERIV>
 struct Basis {
     static constexpr int M = n_mono(L);
@@ -37,8 +52,10 @@ struct Basis {
             return fmaf(fmaf(-q, rc, x), ir, q);
         };
         v = div_rc(d);
-        fc = 0.5f + 0.5f * cospif(v);
-        if (DERIV) dfc = md->dfc_scale * sinpif(v);
+        float sh, ch;
+        sincos_half_pi(v, sh, ch);
+        fc = ch * ch;
+        if (DERIV) dfc = 2.0f * md->dfc_scale * sh * ch;
         const float c2 = md->exp2_coef, is2 = md->inv_s2;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
