@@ -101,7 +101,7 @@ void Context::release(Buf &b) {
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
-                  &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &GO, &Gc,
+                  &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amap, &act_n, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel};
@@ -274,7 +274,7 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
     Status s;
     if (pos) s = load_positions(cx, pos);
     if (!s.bad()) s = mpnn::evaluate(cx, forces);
-    if (!s.bad() && atom_energy) s = mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, cx.n, atom_energy);
+    if (!s.bad() && atom_energy) s = mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, 0, atom_energy);
     if (!s.bad() && energy) {
         s = mpnn::energy_sum(cx, energy);
         if (!s.bad() && !std::isfinite(*energy)) s = Status::err(MPNN_E_NONFINITE, "non-finite energy");
@@ -402,16 +402,18 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
     auto run = [&]() -> Status {
         switch (which) {
             case 0:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.c.as<float>() + (int64_t)t * cx.NN * cx.K, cx.K, cx.n, out));
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.c.as<float>() + (int64_t)t * cx.NN * cx.K, cx.K, 0, out));
                 break;
             case 1:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.O.as<float>() + (int64_t)t * cx.n * KM, KM, cx.n, out));
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.O.as<float>() + (int64_t)t * cx.np * mpnn::pad16(KM), KM, cx.np, out));
                 break;
             case 2:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.GO.as<float>() + (int64_t)t * cx.n * KM, KM, cx.n, out));
+                MPNN_TRY(cx.grow(cx.tmp_a, sizeof(float) * (size_t)(cx.n > 0 ? cx.n : 1) * KM));
+                MPNN_TRY(mpnn::assemble_go(cx, t, cx.tmp_a.as<float>()));
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.tmp_a.as<float>(), KM, 0, out));
                 break;
             case 3:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, cx.n, out));
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, 0, out));
                 break;
             default:
                 return Status::err(MPNN_E_INVALID_ARG, "bad selector");

@@ -80,6 +80,34 @@ struct Feat {
     }
 };
 
+// Feature q (order: l-major, then the upper-triangle rank of (a, b), a <= b) -> (l, a, b);
+// q past the last feature gives l > L (zero padding).
+struct FeatIdx {
+    int l, a, b;
+};
+constexpr FeatIdx feat_idx(int K, int q) {
+    const int P = K * (K + 1) / 2;
+    int r = q % P, x = 0;
+    while (r >= K - x) {
+        r -= K - x;
+        ++x;
+    }
+    return FeatIdx{q / P, x, x + r};
+}
+
+// ------------------------------------------------------------------------------------------
+// Per-atom vectors of the networks (orbital coefficients O, density features rho/s, dE/drho)
+// are stored column-tiled: element q of atom i at ((q / 16) np + i) 16 + q % 16, where np is
+// the atom count rounded up to whole 256-row blocks.  Sixteen columns of consecutive atoms form
+// one contiguous run, so a block writes a tile with full-line stores and a network tile reads
+// 64 contiguous bytes per atom.
+// ------------------------------------------------------------------------------------------
+constexpr int pad16(int w) { return (w + 15) / 16 * 16; }
+inline int64_t pad_rows(int64_t n) { return (n + kBlock - 1) / kBlock * kBlock; }
+__host__ __device__ __forceinline__ int64_t tiled(int64_t np, int64_t i, int q) {
+    return ((int64_t)(q >> 4) * np + i) * 16 + (q & 15);
+}
+
 // ------------------------------------------------------------------------------------------
 // fp64 helpers that are never contracted into FMAs, so pair distances are bit-identical to a
 // plain left-to-right evaluation of (dx*dx + dy*dy) + dz*dz.

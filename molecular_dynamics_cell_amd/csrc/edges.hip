@@ -7,6 +7,8 @@
 //
 // Every reduction has a fixed order (one thread owns one output row and walks its list), so
 // results are bitwise reproducible and no floating-point atomics are used.
+#include <utility>
+
 #include "impl.h"
 
 namespace mpnn {
@@ -76,6 +78,116 @@ struct Basis {
     }
 };
 
+// Density feature q of one atom from its orbital coefficients held in registers (Eq. 1 outer
+// sum): rho[(a,b),l] = sum over the monomials m of degree l of w_m O[a,m] O[b,m].  Q is a template
+// argument, so every register index is resolved at compile time; Q past the last feature is 0.
+template <int K, int L, int Q>
+__device__ __forceinline__ float feature_q(const float (&O)[K][n_mono(L)]) {
+    constexpr FeatIdx f = feat_idx(K, Q);
+    if constexpr (f.l > L) {
+        return 0.0f;
+    } else {
+        constexpr Mono<L> mono;
+        constexpr int m0 = f.l * (f.l + 1) * (f.l + 2) / 6, m1 = m0 + (f.l + 1) * (f.l + 2) / 2;
+        float acc = 0.0f;
+#pragma unroll
+        for (int m = m0; m < m1; ++m) acc += mono.w[m] * O[f.a][m] * O[f.b][m];
+        return acc;
+    }
+}
+
+template <int K, int L, int KT, int... J>
+__device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], float s, float (&v)[16],
+                                             std::integer_sequence<int, J...>) {
+    ((v[J] = feature_q<K, L, 16 * KT + J>(O) * s), ...);
+}
+
+// One 16-column tile of the block's 256 rows: thread t holds the 16 values of row i0 + t; the
+// tile is staged through LDS (rows padded to 80 bytes) and written as one contiguous 16 KB run,
+// 1 KB per store instruction.  All threads of the block call it.
+__device__ __forceinline__ void store_tile(const float (&v)[16], float4 *__restrict__ lds, float *__restrict__ dst) {
+    const int t = threadIdx.x;
+    float4 *row = lds + 5 * t;
+    row[0] = float4{v[0], v[1], v[2], v[3]};
+    row[1] = float4{v[4], v[5], v[6], v[7]};
+    row[2] = float4{v[8], v[9], v[10], v[11]};
+    row[3] = float4{v[12], v[13], v[14], v[15]};
+    __syncthreads();
+    float4 *out = reinterpret_cast<float4 *>(dst);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int f = p * kBlock + t;
+        out[f] = lds[5 * (f >> 2) + (f & 3)];
+    }
+    __syncthreads();
+}
+
+template <int K, int L, int KT>
+__device__ __forceinline__ void store_o_tile(const float (&O)[K][n_mono(L)], float4 *lds, float *dst) {
+    constexpr int M = n_mono(L);
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int q = 16 * KT + j;
+        v[j] = q < K * M ? O[q / M][q % M] : 0.0f;
+    }
+    store_tile(v, lds, dst);
+}
+
+template <int K, int L, int... KT>
+__device__ __forceinline__ void store_o_rows(const float (&O)[K][n_mono(L)], float4 *lds, float *base, int64_t np,
+                                             std::integer_sequence<int, KT...>) {
+    (store_o_tile<K, L, KT>(O, lds, base + (int64_t)KT * np * 16), ...);
+}
+
+template <int K, int L, int KT>
+__device__ __forceinline__ void store_feature_tile(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *dst) {
+    float v[16];
+    feature_tile<K, L, KT>(O, s, v, std::make_integer_sequence<int, 16>{});
+    store_tile(v, lds, dst);
+}
+
+template <int K, int L, int... KT>
+__device__ __forceinline__ void store_feature_rows(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *base,
+                                                   int64_t np, std::integer_sequence<int, KT...>) {
+    (store_feature_tile<K, L, KT>(O, s, lds, base + (int64_t)KT * np * 16), ...);
+}
+
+// Chain rule through the features: dE/dO[c,m] = w_m sum_b (1 + [b == c]) dE/drho[(b,c), l_m] O[b,m],
+// from the atom's column-tiled dE/drho and O rows; one template instance per feature Q, so the
+// register indices of G are compile-time constants.
+template <int K, int L, int Q>
+__device__ __forceinline__ void go_term(const float *__restrict__ grho, const float *__restrict__ O, int64_t np,
+                                        int64_t i, float (&G)[K][n_mono(L)]) {
+    constexpr int M = n_mono(L);
+    constexpr FeatIdx f = feat_idx(K, Q);
+    constexpr Mono<L> mono;
+    constexpr int m0 = f.l * (f.l + 1) * (f.l + 2) / 6, m1 = m0 + (f.l + 1) * (f.l + 2) / 2;
+    const float g = grho[tiled(np, i, Q)];
+#pragma unroll
+    for (int m = m0; m < m1; ++m) {
+        const float wg = mono.w[m] * g;
+        G[f.a][m] += wg * O[tiled(np, i, f.b * M + m)];
+        G[f.b][m] += wg * O[tiled(np, i, f.a * M + m)];
+    }
+}
+
+template <int K, int L, int... Q>
+__device__ __forceinline__ void go_terms(const float *__restrict__ grho, const float *__restrict__ O, int64_t np,
+                                         int64_t i, float (&G)[K][n_mono(L)], std::integer_sequence<int, Q...>) {
+    (go_term<K, L, Q>(grho, O, np, i, G), ...);
+}
+
+template <int K, int L>
+__device__ __forceinline__ void assemble_go_row(const float *__restrict__ grho, const float *__restrict__ O,
+                                                int64_t np, int64_t i, float (&G)[K][n_mono(L)]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int m = 0; m < n_mono(L); ++m) G[k][m] = 0.0f;
+    go_terms<K, L>(grho, O, np, i, G, std::make_integer_sequence<int, n_feat(K, L)>{});
+}
+
 // Per-step active list: the Verlet entries of each row with d^2 < rc^2 (fp64, the same
 // expression as the build), compacted in row order into the row's leading slots (sender node of
 // active entry a at slot base + 64 a), plus the map from every Verlet slot to its active slot
@@ -109,58 +221,63 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
     nact[i] = o;
 }
 
-// O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum).
+// O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
+// atom's density features from it; both leave through LDS-staged, column-tiled stores.
 template <int K, int L>
-__global__ __launch_bounds__(256) void k_aggregate(int64_t n, const double *__restrict__ pos,
+__global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
                                                    const int32_t *__restrict__ act_n, const float *__restrict__ c,
-                                                   const ModelDev *__restrict__ md, float *__restrict__ O) {
-    constexpr int M = n_mono(L);
-    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    float mu[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
-    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+                                                   const ModelDev *__restrict__ md, float inv_scale,
+                                                   float *__restrict__ O, float *__restrict__ feat) {
+    constexpr int M = n_mono(L), KMT = pad16(K * M) / 16, DT = pad16(n_feat(K, L)) / 16;
+    __shared__ float4 lds[5 * kBlock];
+    const int64_t i0 = xcd_block() * kBlock;
+    if (i0 >= n) return;                       // whole block past the end (grid rounded to 8 XCDs)
+    const int64_t i = i0 + threadIdx.x;
     float acc[K][M];
 #pragma unroll
     for (int k = 0; k < K; ++k)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[k][m] = 0.0f;
-    const int64_t b0 = sell_base(slab_off, i);
-    const int na = nact[i];
-    for (int a = 0; a < na; ++a) {
-        const int64_t v = act_n[b0 + kSlab * a];
-        Basis<K, L, false> b;
-        b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
-        const float *cv = c + v * K;
+    if (i < n) {
+        float mu[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const float P = cv[k] * b.R[k] * b.fc;
+        for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
+        const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+        const int64_t b0 = sell_base(slab_off, i);
+        const int na = nact[i];
+        for (int a = 0; a < na; ++a) {
+            const int64_t v = act_n[b0 + kSlab * a];
+            Basis<K, L, false> b;
+            b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
+            const float *cv = c + v * K;
 #pragma unroll
-            for (int m = 0; m < M; ++m) acc[k][m] += P * b.A[m];
+            for (int k = 0; k < K; ++k) {
+                const float P = cv[k] * b.R[k] * b.fc;
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[k][m] += P * b.A[m];
+            }
         }
     }
-    float *o = O + i * (K * M);
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int m = 0; m < M; ++m) o[k * M + m] = acc[k][m];
+    // rows n..np-1 of the last block are padding: written, never read
+    store_o_rows<K, L>(acc, lds, O + i0 * 16, np, std::make_integer_sequence<int, KMT>{});
+    store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, std::make_integer_sequence<int, DT>{});
 }
 
 // Reverse pass of layer t over one receiver row per thread (Eq. 4 as a VJP), with
-// G = dE/dO^t_i held in registers for the whole row.  For every active edge e = (i <- v):
+// G = dE/dO^t_i formed from dE/drho^t_i and held in registers for the whole row.  For every active edge e = (i <- v):
 //   u_k = sum_m G[k,m] A_m,       w_e[k] = u_k R_k f_c        (dE/dc^t_v contribution, t >= 1)
 //   s = sum_k c_v[k] u_k (R'_k f_c + R_k f'_c),  Q_m = sum_k c_v[k] R_k f_c G[k,m]
 //   dE/dr_e += s r/d + sum_m Q_m dA_m/dr              (accumulated over layers)
 // The receiver-side force sum is accumulated in fp64 per row.
 template <int K, int L, bool FIRST, bool WANT_W>
-__global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double *__restrict__ pos,
+__global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
                                                         const int32_t *__restrict__ act_n, const float *__restrict__ c,
-                                                        const float *__restrict__ GO, const ModelDev *__restrict__ md,
+                                                        const float *__restrict__ Grho, const float *__restrict__ Ot,
+                                                        const ModelDev *__restrict__ md,
                                                         float *__restrict__ w, float *__restrict__ gedge,
                                                         double *__restrict__ Frecv) {
     constexpr int M = n_mono(L);
@@ -173,11 +290,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, const double 
     const float ir = md->inv_rc;
     const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
     float G[K][M];
-    const float *gi = GO + i * (K * M);
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int m = 0; m < M; ++m) G[k][m] = gi[k * M + m];
+    assemble_go_row<K, L>(Grho, Ot, np, i, G);
     double F[3] = {0.0, 0.0, 0.0};
     const int64_t b0 = sell_base(slab_off, i);
     const int na = nact[i];
@@ -330,6 +443,21 @@ __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *
     }
 }
 
+// dE/dO^t rows of every atom (for inspection; the reverse pass forms them in registers).
+template <int K, int L>
+__global__ __launch_bounds__(256) void k_assemble_go(int64_t n, int64_t np, const float *__restrict__ Grho,
+                                                     const float *__restrict__ Ot, float *__restrict__ out) {
+    constexpr int M = n_mono(L);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float G[K][M];
+    assemble_go_row<K, L>(Grho, Ot, np, i, G);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) out[i * (K * M) + k * M + m] = G[k][m];
+}
+
 #define MPNN_DISPATCH_KL(K_, L_, CALL)                                                 \
     do {                                                                               \
         if ((K_) == 8 && (L_) == 2) { constexpr int KK = 8, LL = 2; CALL; }            \
@@ -355,10 +483,12 @@ Status aggregate(Context &cx, int t) {
     ProfScope ps_(cx, kProfAggregate);
     if (cx.n == 0) return Status::ok();
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
-    float *Ot = cx.O.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
+    float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
+    float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
-                                      cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),
-                                      cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), Ot)));
+                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),
+                                      cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), cx.inv_scale_host[t],
+                                      Ot, Ft)));
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
@@ -376,12 +506,13 @@ Status backward_layer(Context &cx, int t) {
     ProfScope ps_(cx, kProfBackwardLayer);
     if (cx.n == 0) return Status::ok();
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
-    const float *GOt = cx.GO.as<float>() + (int64_t)t * cx.n * cx.K * cx.M;
+    const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
+    const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     const bool first = (t == cx.T - 1), want_w = (t >= 1);
 #define MPNN_BWD(FIRST_, W_)                                                                               \
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
-                                      cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
-                                      cx.act_n.as<int32_t>(), ct, GOt,                                             \
+                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
+                                      cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), cx.w.as<float>(), cx.gedge.as<float>(),             \
                                       cx.Frecv.as<double>())))
     if (first && want_w) MPNN_BWD(true, true);
@@ -389,6 +520,16 @@ Status backward_layer(Context &cx, int t) {
     else if (want_w) MPNN_BWD(false, true);
     else MPNN_BWD(false, false);
 #undef MPNN_BWD
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status assemble_go(Context &cx, int t, float *out) {
+    if (cx.n == 0) return Status::ok();
+    const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
+    const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_assemble_go<KK, LL><<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.np, Gt, Ot,
+                                                                                                 out)));
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

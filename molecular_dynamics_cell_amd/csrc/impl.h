@@ -73,6 +73,7 @@ struct Context {
     bool built = false;
     bool forces_valid = false;  // F_sorted matches the current positions
     int64_t n = 0, G = 0, NN = 0, E = 0, E_sell = 0;
+    int64_t np = 0;             // n rounded up to whole 256-row blocks (column-tiled vectors)
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
     int nc[3] = {0, 0, 0};      // interior cells per axis
@@ -98,8 +99,9 @@ struct Context {
 
     // per-evaluation buffers
     Buf c;        // float [T][NN][K]
-    Buf O;        // float [T][n][K*M]
-    Buf GO;       // float [T][n][K*M]
+    Buf O;        // float [T] x column-tiled [np][pad16(K*M)]: orbital coefficients O^t
+    Buf feat;     // float [T] x column-tiled [np][DP]: density features rho^t / s_t
+    Buf grho;     // float [T] x column-tiled [np][DP]: dE/drho^t
     Buf Gc;       // float [NN][K]
     Buf gedge;    // float [E][3]  dE/dr_e summed over layers
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
@@ -161,13 +163,14 @@ Status compact_active(Context &cx);               // per-step active entries (d 
 Status aggregate(Context &cx, int t);
 Status refresh_ghost_features(Context &cx, int t);
 Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
+Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagnostics)
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold
 Status force_gather(Context &cx, double *F_caller);
 
 // ---- mlp.hip ----
-Status mlp_forward(Context &cx, int t);           // c^{t+1} from O^t (t < T-1)
-Status mlp_energy(Context &cx);                   // E_i and dE/dO^{T-1}
-Status mlp_backward(Context &cx, int t);          // dE/dO^t from dE/dc^{t+1}
+Status mlp_forward(Context &cx, int t);           // c^{t+1} from rho^t (t < T-1)
+Status mlp_energy(Context &cx);                   // E_i and dE/drho^{T-1}
+Status mlp_backward(Context &cx, int t);          // dE/drho^t from dE/dc^{t+1}
 Status pack_weights(Context &cx, const double *mlp);
 
 // ---- integrate.hip ----
@@ -180,7 +183,7 @@ Status read_skin_flag(Context &cx, bool *exceeded, double *max_disp);
 Status reset_skin_flag(Context &cx);
 Status unpermute_vec3(Context &cx, const double *sorted, double *caller);
 Status permute_in_vec3(Context &cx, const double *caller, double *sorted);
-Status unpermute_float(Context &cx, const float *sorted, int width, int64_t stride_rows,
-                       double *caller);
+// sorted rows of `width` floats (row-major, or column-tiled with row count np when np > 0)
+Status unpermute_float(Context &cx, const float *sorted, int width, int64_t np, double *caller);
 
 }  // namespace mpnn

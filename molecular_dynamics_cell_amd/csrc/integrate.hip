@@ -144,13 +144,13 @@ __global__ void k_permute_in3(int64_t n, const int32_t *__restrict__ perm, const
     for (int a = 0; a < 3; ++a) out[3 * s + a] = in[3 * c + a];
 }
 
-__global__ void k_unpermute_float(int64_t n, int width, const int32_t *__restrict__ perm,
+__global__ void k_unpermute_float(int64_t n, int width, int64_t np, const int32_t *__restrict__ perm,
                                   const float *__restrict__ in, double *__restrict__ out) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n * width) return;
     const int64_t s = q / width;
     const int w = (int)(q - s * width);
-    out[(int64_t)perm[s] * width + w] = (double)in[q];
+    out[(int64_t)perm[s] * width + w] = (double)in[np > 0 ? tiled(np, s, w) : q];
 }
 
 }  // namespace
@@ -242,11 +242,10 @@ Status permute_in_vec3(Context &cx, const double *caller, double *sorted) {
     return Status::ok();
 }
 
-Status unpermute_float(Context &cx, const float *sorted, int width, int64_t rows, double *caller) {
-    (void)rows;
+Status unpermute_float(Context &cx, const float *sorted, int width, int64_t np, double *caller) {
     if (cx.n == 0) return Status::ok();
-    k_unpermute_float<<<grid_for(cx.n * width), kBlock, 0, cx.stream>>>(cx.n, width, cx.perm.as<int32_t>(), sorted,
-                                                                       caller);
+    k_unpermute_float<<<grid_for(cx.n * width), kBlock, 0, cx.stream>>>(cx.n, width, np, cx.perm.as<int32_t>(),
+                                                                       sorted, caller);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

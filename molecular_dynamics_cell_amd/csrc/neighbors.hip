@@ -599,8 +599,11 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     // ---- per-evaluation buffers and layer-0 messages ----
     const int KM = cx.K * cx.M;
     MPNN_TRY(cx.grow(cx.c, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
-    MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * n1 * KM));
-    MPNN_TRY(cx.grow(cx.GO, sizeof(float) * (size_t)cx.T * n1 * KM));
+    cx.np = pad_rows(cx.n);
+    const size_t np1 = (size_t)(cx.np > 0 ? cx.np : kBlock);
+    MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * np1 * pad16(KM)));
+    MPNN_TRY(cx.grow(cx.feat, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
+    MPNN_TRY(cx.grow(cx.grho, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)NN1 * cx.K));
     MPNN_TRY(cx.grow(cx.amap, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
