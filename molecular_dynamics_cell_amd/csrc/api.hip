@@ -102,7 +102,7 @@ Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
-                  &gedge, &w, &amap, &act_n, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
+                  &gedge, &w, &amap, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel};
     for (Buf *b : all) release(*b);
@@ -138,6 +138,7 @@ Status evaluate(Context &cx, double *F_caller) {
             MPNN_TRY(mlp_backward(cx, t - 1));
         }
     }
+    if (cx.T == 1) MPNN_TRY(transpose_active(cx));
     MPNN_TRY(force_gather(cx, F_caller));
     cx.forces_valid = true;
     return Status::ok();

@@ -354,11 +354,14 @@ __device__ __forceinline__ T group_sum16(T x) {
 }
 
 // dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
-// term, gathered without atomics).
-template <int K>
+// term, gathered without atomics).  The first gather of an evaluation (BUILD) looks up the active
+// slot of each transposed entry through the per-step map and records it in t_act, so the later
+// gathers read it sequentially.
+template <int K, bool BUILD>
 __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__restrict__ t_off,
                                                   const int32_t *__restrict__ t_eid, const int32_t *__restrict__ amap,
-                                                  const float *__restrict__ w, float *__restrict__ Gc) {
+                                                  int32_t *__restrict__ t_act, const float *__restrict__ w,
+                                                  float *__restrict__ Gc) {
     const int64_t v = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
     const int q = threadIdx.x % kGatherLanes;
     const bool ok = v < NN;
@@ -368,7 +371,13 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
     if (ok) {
         const int64_t s1 = t_off[v + 1];
         for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-            const int32_t a = amap[t_eid[s]];
+            int32_t a;
+            if (BUILD) {
+                a = amap[t_eid[s]];
+                t_act[s] = a;
+            } else {
+                a = t_act[s];
+            }
             if (a < 0) continue;
             const float *we = w + (int64_t)a * K;
 #pragma unroll
@@ -380,6 +389,14 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
     if (ok && q == 0)
 #pragma unroll
         for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
+}
+
+// t_act alone (evaluations without message layers, where no gather builds it).
+__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, const int32_t *__restrict__ t_eid,
+                                                          const int32_t *__restrict__ amap,
+                                                          int32_t *__restrict__ t_act) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < E) t_act[s] = amap[t_eid[s]];
 }
 
 // Ghost -> owner sum of dE/dc (the reverse ghost exchange), ghosts of an owner in order.
@@ -408,8 +425,7 @@ __global__ void k_ghost_feat(int64_t G, int64_t n, int K, const int32_t *__restr
 // dE/dr_e (r_e = r_sender - r_receiver), in fp64; 16 lanes per atom as in the gathers above.
 __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *__restrict__ perm,
                                                       const int64_t *__restrict__ t_off,
-                                                      const int32_t *__restrict__ t_eid,
-                                                      const int32_t *__restrict__ amap,
+                                                      const int32_t *__restrict__ t_act,
                                                       const int64_t *__restrict__ ghost_off,
                                                       const double *__restrict__ Frecv, const float *__restrict__ gedge,
                                                       double *__restrict__ F, double *__restrict__ Fcaller) {
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *
             const int64_t v = vv < 0 ? i : n + g0 + vv;
             const int64_t s1 = t_off[v + 1];
             for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-                const int32_t a = amap[t_eid[s]];
+                const int32_t a = t_act[s];
                 if (a < 0) continue;
                 const float *ge = gedge + 3 * (int64_t)a;
                 f[0] -= (double)ge[0];
@@ -534,15 +550,29 @@ Status assemble_go(Context &cx, int t, float *out) {
     return Status::ok();
 }
 
+Status transpose_active(Context &cx) {
+    if (cx.E == 0) return Status::ok();
+    k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.stream>>>(cx.E, cx.t_eid.as<int32_t>(), cx.amap.as<int32_t>(),
+                                                                 cx.t_act.as<int32_t>());
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
 Status backward_messages(Context &cx, int t) {
-    (void)t;
     if (cx.n == 0) return Status::ok();
     {
         ProfScope ps_(cx, kProfMessageGrad);
         const unsigned gg = grid_xcd(cx.NN * kGatherLanes);
-#define MPNN_GW(KK)                                                                                        \
-    k_gather_w<KK><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(),         \
-                                                 cx.amap.as<int32_t>(), cx.w.as<float>(), cx.Gc.as<float>())
+        const bool build = (t == cx.T - 1);
+#define MPNN_GW(KK)                                                                                           \
+    if (build)                                                                                                \
+        k_gather_w<KK, true><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
+                                                           cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),      \
+                                                           cx.w.as<float>(), cx.Gc.as<float>());               \
+    else                                                                                                      \
+        k_gather_w<KK, false><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
+                                                            cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),     \
+                                                            cx.w.as<float>(), cx.Gc.as<float>())
         switch (cx.K) {
             case 2: MPNN_GW(2); break;
             case 4: MPNN_GW(4); break;
@@ -564,7 +594,7 @@ Status force_gather(Context &cx, double *F_caller) {
     ProfScope ps_(cx, kProfForceGather);
     if (cx.n == 0) return Status::ok();
     k_force_gather<<<grid_xcd(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(
-        cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.amap.as<int32_t>(),
+        cx.n, cx.perm.as<int32_t>(), cx.t_off.as<int64_t>(), cx.t_act.as<int32_t>(),
         cx.ghost_off.as<int64_t>(), cx.Frecv.as<double>(), cx.gedge.as<float>(),
         cx.F.as<double>(), F_caller);
     MPNN_HIP(hipGetLastError());

@@ -107,6 +107,7 @@ struct Context {
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
     Buf amap;     // int32 [E]: active slot of each Verlet slot this step (-1: d >= rc)
     Buf act_n;    // int32 [E]: sender node of each active slot
+    Buf t_act;    // int32 [E]: active slot of each transposed entry this step (-1: d >= rc)
     Buf nact;     // int32 [n] active entries per row
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
@@ -164,7 +165,8 @@ Status aggregate(Context &cx, int t);
 Status refresh_ghost_features(Context &cx, int t);
 Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
 Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagnostics)
-Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold
+Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
+Status transpose_active(Context &cx);             // t_act alone (T == 1)
 Status force_gather(Context &cx, double *F_caller);
 
 // ---- mlp.hip ----
