@@ -148,7 +148,8 @@ mpnn_status mpnn_get_pairs(mpnn_ctx *ctx, int64_t cap, int64_t *n_pairs, int32_t
                            int32_t *shift);
 
 /* Per-atom intermediates of the last evaluation, fp64 device out in caller order:
- * which = 0: c^t [n][K]; 1: O^t [n][K*M]; 2: dE/dO^t [n][K*M]; 3: E_i [n] (t ignored). */
+ * which = 0: c^t [n][K]; 1: O^t [n][K*M]; 2: dE/dO^t [n][K*M]; 3: E_i [n] (t ignored);
+ * 4: dE/dc^t [n][K] for 1 <= t < T (after the ghost->owner fold). */
 mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, double *out);
 
 mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info);

@@ -187,7 +187,7 @@ class MPNN:
         return i[:n], j[:n], s[:n]
 
     def get_intermediate(self, which: int, t: int = 0):
-        width = {0: self.K, 1: self.K * self.M, 2: self.K * self.M, 3: 1}[which]
+        width = {0: self.K, 1: self.K * self.M, 2: self.K * self.M, 3: 1, 4: self.K}[which]
         out = torch.empty((self.n, width), dtype=torch.float64, device=self.device)
         self._check(lib().mpnn_get_intermediate(self.h, int(which), int(t), _dptr(out)))
         return out

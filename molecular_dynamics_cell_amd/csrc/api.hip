@@ -208,6 +208,20 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     md.exp2_coef = (float)(-1.0 / (2.0 * p->sigma * p->sigma * std::log(2.0)));
     md.dfc_scale = (float)(-0.5 * mpnn::kPi / p->rc);
     md.rc2 = p->rc * p->rc;
+    {
+        const double s2 = p->sigma * p->sigma;
+        for (int k = 0; k < cx.K; ++k) md.mu64[k] = p->mu[k];
+        md.g_a0 = -1.0 / (2.0 * s2);
+        const double delta = cx.K > 1 ? p->mu[1] - p->mu[0] : 0.0;
+        md.g_e = delta / s2;
+        for (int k = 0; k + 1 < cx.K; ++k) {
+            const double dk = p->mu[k + 1] - p->mu[k];
+            md.g_c[k] = std::exp(-dk * (p->mu[k] + p->mu[k + 1]) / (2.0 * s2));
+            md.g_eps[k] = (dk - delta) / s2;
+        }
+        md.inv_rc64 = 1.0 / p->rc;
+        md.half_pi_over_rc = 0.5 * mpnn::kPi / p->rc;
+    }
     Status s = cx.grow(cx.model, sizeof md);
     if (!s.bad()) {
         if (hipMemcpy(cx.model.p, &md, sizeof md, hipMemcpyHostToDevice) != hipSuccess)
@@ -399,6 +413,7 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
     mpnn::Context &cx = ctx->cx;
     if (!cx.built || !cx.forces_valid) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "no evaluation yet"));
     if (which != 3 && (t < 0 || t >= cx.T)) return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "bad layer"));
+    if (which == 4 && cx.T < 2) return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "no message layers"));
     const int KM = cx.K * cx.M;
     auto run = [&]() -> Status {
         switch (which) {
@@ -415,6 +430,10 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
                 break;
             case 3:
                 MPNN_TRY(mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, 0, out));
+                break;
+            case 4:
+                if (t < 1) return Status::err(MPNN_E_INVALID_ARG, "dE/dc^t exists for t >= 1");
+                MPNN_TRY(mpnn::unpermute_float(cx, cx.Gc.as<float>() + (int64_t)t * cx.NN * cx.K, cx.K, 0, out));
                 break;
             default:
                 return Status::err(MPNN_E_INVALID_ARG, "bad selector");

@@ -129,6 +129,14 @@ struct ModelDev {
     float dfc_scale;        // -pi / (2 rc): df_c/dd = dfc_scale sin(pi d / rc)
     double rc2;             // rc^2 (fp64, for the active-edge test)
     double mass[16];        // amu per species
+    // fp64 constants of the aggregation basis
+    double mu64[16];        // radial centres
+    double g_a0;            // -1 / (2 sigma^2)
+    double g_e;             // delta / sigma^2, delta = mu_1 - mu_0
+    double g_c[16];         // exp(-delta_k (mu_k + mu_{k+1}) / (2 sigma^2)), delta_k = mu_{k+1} - mu_k
+    double g_eps[16];       // (delta_k - delta) / sigma^2
+    double inv_rc64;        // 1 / rc
+    double half_pi_over_rc; // pi / (2 rc)
 };
 
 // Sliced-ELLPACK neighbour storage: rows are grouped in slabs of 64 consecutive (cell-ordered)

@@ -78,20 +78,73 @@ struct Basis {
     }
 };
 
+// Aggregation factors accurate to about half an fp32 ulp each, so that every product
+// c_k R_k f_c A_m entering an orbital sum carries a single rounding: the Gaussians, the cutoff and
+// the monomials are evaluated in fp64 and rounded once.  The Gaussians follow from the ratio of
+// neighbouring centres, R_{k+1} / R_k = exp(delta_k d / s^2) exp(-delta_k (mu_k + mu_{k+1}) / (2 s^2))
+// with delta_k = mu_{k+1} - mu_k; writing delta_k = delta + (delta_k - delta), the first factor is
+// one exponential E = exp(delta d / s^2) times 1 + (delta_k - delta) d / s^2 (the next term is below
+// 1e-11), so an edge needs two fp64 exponentials.  The cutoff is cos^2(pi d / (2 rc)) from the
+// Taylor series of cos to the t^18 term (truncation below 1e-14 on [0, pi/2]).
+template <int K, int L>
+struct BasisHP {
+    static constexpr int M = n_mono(L);
+    float P[K];  // c_k R_k f_c
+    float A[M];
+
+    __device__ __forceinline__ void eval(double dx, double dy, double dz, const float *__restrict__ cv,
+                                         const ModelDev *__restrict__ md) {
+        constexpr Mono<L> mono;
+        const double d = sqrt(fma(dx, dx, fma(dy, dy, dz * dz)));
+        const double t = d * md->half_pi_over_rc, t2 = t * t;
+        double cs = -1.0 / 6402373705728000.0;                 // -1/18!
+        cs = fma(cs, t2, 1.0 / 20922789888000.0);              // 1/16!
+        cs = fma(cs, t2, -1.0 / 87178291200.0);                // -1/14!
+        cs = fma(cs, t2, 1.0 / 479001600.0);                   // 1/12!
+        cs = fma(cs, t2, -1.0 / 3628800.0);                    // -1/10!
+        cs = fma(cs, t2, 1.0 / 40320.0);                       // 1/8!
+        cs = fma(cs, t2, -1.0 / 720.0);                        // -1/6!
+        cs = fma(cs, t2, 1.0 / 24.0);                          // 1/4!
+        cs = fma(cs, t2, -0.5);
+        cs = fma(cs, t2, 1.0);
+        const double fc = cs * cs;
+        const double x0 = d - md->mu64[0];
+        double R = exp(md->g_a0 * x0 * x0);
+        const double E = exp(md->g_e * d);
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            P[k] = (float)((double)cv[k] * R * fc);
+            if (k + 1 < K) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
+        }
+        const double ux = dx * md->inv_rc64, uy = dy * md->inv_rc64, uz = dz * md->inv_rc64;
+        double px[L + 1], py[L + 1], pz[L + 1];
+        px[0] = py[0] = pz[0] = 1.0;
+#pragma unroll
+        for (int q = 1; q <= L; ++q) {
+            px[q] = px[q - 1] * ux;
+            py[q] = py[q - 1] * uy;
+            pz[q] = pz[q - 1] * uz;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) A[m] = (float)(px[mono.lx[m]] * py[mono.ly[m]] * pz[mono.lz[m]]);
+    }
+};
+
 // Density feature q of one atom from its orbital coefficients held in registers (Eq. 1 outer
-// sum): rho[(a,b),l] = sum over the monomials m of degree l of w_m O[a,m] O[b,m].  Q is a template
-// argument, so every register index is resolved at compile time; Q past the last feature is 0.
+// sum): rho[(a,b),l] = sum over the monomials m of degree l of w_m O[a,m] O[b,m], accumulated in
+// fp64.  Q is a template argument, so every register index is resolved at compile time; Q past
+// the last feature is 0.
 template <int K, int L, int Q>
-__device__ __forceinline__ float feature_q(const float (&O)[K][n_mono(L)]) {
+__device__ __forceinline__ double feature_q(const float (&O)[K][n_mono(L)]) {
     constexpr FeatIdx f = feat_idx(K, Q);
     if constexpr (f.l > L) {
-        return 0.0f;
+        return 0.0;
     } else {
         constexpr Mono<L> mono;
         constexpr int m0 = f.l * (f.l + 1) * (f.l + 2) / 6, m1 = m0 + (f.l + 1) * (f.l + 2) / 2;
-        float acc = 0.0f;
+        double acc = 0.0;
 #pragma unroll
-        for (int m = m0; m < m1; ++m) acc += mono.w[m] * O[f.a][m] * O[f.b][m];
+        for (int m = m0; m < m1; ++m) acc = fma((double)mono.w[m] * O[f.a][m], (double)O[f.b][m], acc);
         return acc;
     }
 }
@@ -99,7 +152,7 @@ __device__ __forceinline__ float feature_q(const float (&O)[K][n_mono(L)]) {
 template <int K, int L, int KT, int... J>
 __device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], float s, float (&v)[16],
                                              std::integer_sequence<int, J...>) {
-    ((v[J] = feature_q<K, L, 16 * KT + J>(O) * s), ...);
+    ((v[J] = (float)(feature_q<K, L, 16 * KT + J>(O) * s)), ...);
 }
 
 // One 16-column tile of the block's 256 rows: thread t holds the 16 values of row i0 + t; the
@@ -241,23 +294,17 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[k][m] = 0.0f;
     if (i < n) {
-        float mu[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
         const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
         const int64_t b0 = sell_base(slab_off, i);
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            Basis<K, L, false> b;
-            b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
-            const float *cv = c + v * K;
+            BasisHP<K, L> b;
+            b.eval(pos[3 * v] - xi, pos[3 * v + 1] - yi, pos[3 * v + 2] - zi, c + v * K, md);
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const float P = cv[k] * b.R[k] * b.fc;
+            for (int k = 0; k < K; ++k)
 #pragma unroll
-                for (int m = 0; m < M; ++m) acc[k][m] += P * b.A[m];
-            }
+                for (int m = 0; m < M; ++m) acc[k][m] = fmaf(b.P[k], b.A[m], acc[k][m]);
         }
     }
     // rows n..np-1 of the last block are padding: written, never read
@@ -560,6 +607,7 @@ Status transpose_active(Context &cx) {
 
 Status backward_messages(Context &cx, int t) {
     if (cx.n == 0) return Status::ok();
+    float *Gct = cx.Gc.as<float>() + (int64_t)t * cx.NN * cx.K;   // dE/dc^t, kept per layer
     {
         ProfScope ps_(cx, kProfMessageGrad);
         const unsigned gg = grid_xcd(cx.NN * kGatherLanes);
@@ -568,11 +616,11 @@ Status backward_messages(Context &cx, int t) {
     if (build)                                                                                                \
         k_gather_w<KK, true><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
                                                            cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),      \
-                                                           cx.w.as<float>(), cx.Gc.as<float>());               \
+                                                           cx.w.as<float>(), Gct);                             \
     else                                                                                                      \
         k_gather_w<KK, false><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
                                                             cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),     \
-                                                            cx.w.as<float>(), cx.Gc.as<float>())
+                                                            cx.w.as<float>(), Gct)
         switch (cx.K) {
             case 2: MPNN_GW(2); break;
             case 4: MPNN_GW(4); break;
@@ -585,7 +633,7 @@ Status backward_messages(Context &cx, int t) {
     }
     ProfScope ps_(cx, kProfGhostFold);
     k_fold_ghost_grad<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.K, cx.ghost_off.as<int64_t>(),
-                                                                 cx.Gc.as<float>());
+                                                                 Gct);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

@@ -102,7 +102,7 @@ struct Context {
     Buf O;        // float [T] x column-tiled [np][pad16(K*M)]: orbital coefficients O^t
     Buf feat;     // float [T] x column-tiled [np][DP]: density features rho^t / s_t
     Buf grho;     // float [T] x column-tiled [np][DP]: dE/drho^t
-    Buf Gc;       // float [NN][K]
+    Buf Gc;       // float [T][NN][K]  dE/dc^t (layers 1..T-1)
     Buf gedge;    // float [E][3]  dE/dr_e summed over layers
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
     Buf amap;     // int32 [E]: active slot of each Verlet slot this step (-1: d >= rc)

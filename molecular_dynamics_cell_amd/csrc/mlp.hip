@@ -10,7 +10,7 @@
 // lane per 4 k-steps).  The density features arrive from the aggregation kernel column-tiled (16
 // features of one atom contiguous), so the first product's B operand is one float4 load per lane
 // per column tile; the VJP leaves dE/drho in the same layout for the reverse edge pass, which forms
-// dE/dO from it.  No LDS and no index arithmetic beyond row offsets.
+// dE/dO from it.
 #include <cmath>
 #include <vector>
 
@@ -29,29 +29,52 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
 
 // acc[rt][c] += W[rt][kt] x[c] for every row tile rt of a matrix packed with KT column tiles:
-// one float4 of weights per lane feeds 4 k-steps of each of the CT atom tiles.
+// one float4 of weights per lane feeds 4 k-steps of each of the CT atom tiles.  The matrix cores
+// sum each 16-input chunk from zero in fp32 and the chunk is added to an fp64 accumulator, so no
+// fp32 sum runs over more than 16 products (long fp32 chains lose several 1e-7 relative on
+// these products).
 template <int RT, int CT>
 __device__ __forceinline__ void gemm_step(const float4 *__restrict__ W, int KT, int kt, const float (&x)[CT][4],
-                                          floatx4 (&acc)[RT][CT], int lane) {
+                                          double (&acc)[RT][CT][4], int lane) {
+    // one scheduling region per chunk column: keeps the compiler from hoisting the weight loads of
+    // every column at once (hundreds of registers for the 128-wide networks)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float4 w = W[(rt * KT + kt) * 64 + lane];
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
-            acc[rt][c] = mfma4(w.x, x[c][0], acc[rt][c]);
-            acc[rt][c] = mfma4(w.y, x[c][1], acc[rt][c]);
-            acc[rt][c] = mfma4(w.z, x[c][2], acc[rt][c]);
-            acc[rt][c] = mfma4(w.w, x[c][3], acc[rt][c]);
+            floatx4 t = mfma4(w.x, x[c][0], floatx4{0.f, 0.f, 0.f, 0.f});
+            t = mfma4(w.y, x[c][1], t);
+            t = mfma4(w.z, x[c][2], t);
+            t = mfma4(w.w, x[c][3], t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rt][c][i] += (double)t[i];
         }
     }
 }
 
+// accumulators start from the bias of their output row (row 16 rt + 4 grp + i)
 template <int RT, int CT>
-__device__ __forceinline__ void zero(floatx4 (&acc)[RT][CT]) {
+__device__ __forceinline__ void init_bias(double (&acc)[RT][CT][4], const float *__restrict__ b, int grp) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int c = 0; c < CT; ++c) acc[rt][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            const double v = (double)b[16 * rt + 4 * grp + i];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) acc[rt][c][i] = v;
+        }
+}
+
+template <int RT, int CT>
+__device__ __forceinline__ void zero(double (&acc)[RT][CT][4]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[rt][c][i] = 0.0;
 }
 
 constexpr int kMaxSpecies = 16;
@@ -76,7 +99,7 @@ struct NetArgs {
 enum { kForward = 0, kEnergy = 1, kBackward = 2 };
 
 template <int K, int L, int H, int MODE, int CT>
-__global__ __launch_bounds__(64) void k_net(const NetArgs a) {
+__global__ __launch_bounds__(64, (H == 128 && MODE == kBackward) ? 1 : 2) void k_net(const NetArgs a) {
     constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
     constexpr int DT = DP / 16, HT = H / 16;
     const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
@@ -93,11 +116,11 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
     const float *b1 = W + a.ob1, *b2 = W + a.ob2, *b3 = W + a.ob3;
 
     // layer 1: Z1 = W1 rho~ + b1
-    floatx4 z1[HT][CT];
-    zero(z1);
+    double z1[HT][CT][4];
+    init_bias(z1, b1, grp);
     {
         const float4 *W1 = reinterpret_cast<const float4 *>(W + a.oW1);
-#pragma unroll 2
+#pragma unroll 1
         for (int kt = 0; kt < DT; ++kt) {
             float x[CT][4];
 #pragma unroll
@@ -110,21 +133,25 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
         }
     }
     // H1 = silu(Z1); the backward pass keeps only silu'(Z1) = s (1 + z (1 - s))
-    float h1[HT][CT][4], d1[MODE == kForward ? 1 : HT][CT][4];
+    // silu'(Z1) is parked in LDS (one word per lane per value, conflict-free) until the reverse pass
+    // needs it, which keeps the 128-wide reverse networks within their register budget
+    __shared__ float sd1[MODE == kForward ? 1 : HT * CT * 4][64];
+    float h1[HT][CT][4];
 #pragma unroll
     for (int rt = 0; rt < HT; ++rt)
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float z = z1[rt][c][i] + b1[16 * rt + 4 * grp + i];
+                const float z = (float)z1[rt][c][i];
                 const float sg = sigmoid(z);
                 h1[rt][c][i] = z * sg;
-                if constexpr (MODE != kForward) d1[rt][c][i] = sg * (1.0f + z * (1.0f - sg));
+                if constexpr (MODE != kForward) sd1[(rt * CT + c) * 4 + i][lane] = sg * (1.0f + z * (1.0f - sg));
             }
     // layer 2
-    floatx4 z2[HT][CT];
-    zero(z2);
+    double z2[HT][CT][4];
+    __builtin_amdgcn_sched_barrier(0);
+    init_bias(z2, b2, grp);
     {
         const float4 *W2 = reinterpret_cast<const float4 *>(W + a.oW2);
 #pragma unroll
@@ -137,7 +164,7 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
         for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float z = z2[rt][c][i] + b2[16 * rt + 4 * grp + i];
+                const float z = (float)z2[rt][c][i];
                 const float sg = sigmoid(z);
                 h2[rt][c][i] = z * sg;
                 if constexpr (MODE != kForward) d2[rt][c][i] = sg * (1.0f + z * (1.0f - sg));
@@ -145,8 +172,8 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
 
     if constexpr (MODE != kBackward) {
         // output layer: 16 padded output rows (K messages or 1 energy)
-        floatx4 y[1][CT];
-        zero(y);
+        double y[1][CT][4];
+        init_bias(y, b3, grp);
         const float4 *W3 = reinterpret_cast<const float4 *>(W + a.oW3);
 #pragma unroll
         for (int kt = 0; kt < HT; ++kt) gemm_step<1, CT>(W3, HT, kt, h2[kt], y, lane);
@@ -157,10 +184,10 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int k = 4 * grp + i;
-                    if (k < K) a.c_next[me[c] * K + k] = y[0][c][i] + b3[k];
+                    if (k < K) a.c_next[me[c] * K + k] = (float)y[0][c][i];
                 }
             } else {
-                if (grp == 0) a.Ei[me[c]] = a.e_scale * (y[0][c][0] + b3[0]);
+                if (grp == 0) a.Ei[me[c]] = (float)((double)a.e_scale * y[0][c][0]);
             }
         }
     }
@@ -176,9 +203,23 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
                 if constexpr (MODE == kEnergy) gy[c][i] = (k == 0) ? a.e_scale : 0.0f;
                 else gy[c][i] = (k < K && me[c] >= 0) ? a.Gc[me[c] * K + k] : 0.0f;
             }
+        // a single 16-input chunk (the output width): fp32 from the matrix cores is enough
         floatx4 g2[HT][CT];
-        zero(g2);
-        gemm_step<HT, CT>(reinterpret_cast<const float4 *>(W + a.oW3t), 1, 0, gy, g2, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const float4 *W3t = reinterpret_cast<const float4 *>(W + a.oW3t);
+#pragma unroll
+            for (int rt = 0; rt < HT; ++rt) {
+                const float4 w = W3t[rt * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    floatx4 t = mfma4(w.x, gy[c][0], floatx4{0.f, 0.f, 0.f, 0.f});
+                    t = mfma4(w.y, gy[c][1], t);
+                    t = mfma4(w.z, gy[c][2], t);
+                    g2[rt][c] = mfma4(w.w, gy[c][3], t);
+                }
+            }
+        }
         float gz2[HT][CT][4];
 #pragma unroll
         for (int rt = 0; rt < HT; ++rt)
@@ -186,7 +227,7 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
             for (int c = 0; c < CT; ++c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) gz2[rt][c][i] = g2[rt][c][i] * d2[rt][c][i];
-        floatx4 g1[HT][CT];
+        double g1[HT][CT][4];
         zero(g1);
         {
             const float4 *W2t = reinterpret_cast<const float4 *>(W + a.oW2t);
@@ -199,12 +240,12 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
 #pragma unroll
             for (int c = 0; c < CT; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) gz1[rt][c][i] = g1[rt][c][i] * d1[rt][c][i];
+                for (int i = 0; i < 4; ++i) gz1[rt][c][i] = (float)g1[rt][c][i] * sd1[(rt * CT + c) * 4 + i][lane];
         // dE/drho = (W1^T dE/dZ1) / s_t, one 16-row tile at a time, stored as float4 row pieces
         const float4 *W1t = reinterpret_cast<const float4 *>(W + a.oW1t);
-#pragma unroll 2
+#pragma unroll 1
         for (int rt = 0; rt < DT; ++rt) {
-            floatx4 gr[1][CT];
+            double gr[1][CT][4];
             zero(gr);
 #pragma unroll
             for (int kt = 0; kt < HT; ++kt) gemm_step<1, CT>(W1t + (size_t)rt * HT * 64, HT, kt, gz1[kt], gr, lane);
@@ -212,15 +253,15 @@ __global__ __launch_bounds__(64) void k_net(const NetArgs a) {
             for (int c = 0; c < CT; ++c)
                 if (me[c] >= 0)
                     *reinterpret_cast<float4 *>(a.Grho + tiled(a.np, me[c], 16 * rt + 4 * grp)) =
-                        float4{gr[0][c][0] * a.inv_scale, gr[0][c][1] * a.inv_scale, gr[0][c][2] * a.inv_scale,
-                               gr[0][c][3] * a.inv_scale};
+                        float4{(float)(gr[0][c][0] * a.inv_scale), (float)(gr[0][c][1] * a.inv_scale),
+                               (float)(gr[0][c][2] * a.inv_scale), (float)(gr[0][c][3] * a.inv_scale)};
         }
     }
 }
 
-// atoms per wave: 32 for the 64-wide networks (each weight load feeds two tiles), 16 for the
-// 128-wide ones (registers)
-constexpr int tiles_per_wave(int H) { return H == 64 ? 2 : 1; }
+// atom tiles per wave: one (16 atoms); two would let each weight load feed two tiles, but the
+// fp64 chunk accumulators then exceed the register budget
+constexpr int tiles_per_wave(int) { return 1; }
 
 NetArgs make_args(Context &cx, int t) {
     NetArgs a{};
@@ -344,7 +385,7 @@ Status mlp_energy(Context &cx) {
 Status mlp_backward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetBackward);
     NetArgs a = make_args(cx, t);
-    a.Gc = cx.Gc.as<float>();
+    a.Gc = cx.Gc.as<float>() + (int64_t)(t + 1) * cx.NN * cx.K;
     MPNN_DISPATCH_NET(kBackward, a);
     return Status::ok();
 }

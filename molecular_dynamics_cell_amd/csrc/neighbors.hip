@@ -604,7 +604,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * np1 * pad16(KM)));
     MPNN_TRY(cx.grow(cx.feat, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.grho, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
-    MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
     MPNN_TRY(cx.grow(cx.amap, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
