@@ -68,7 +68,9 @@ typedef struct {
     int32_t L;                  /* maximum angular momentum */
     int32_t T;                  /* message-passing layers */
     int32_t hidden;             /* width H of both hidden layers */
-    int32_t reserved;           /* must be 0 */
+    int32_t precision;          /* 0: fp32 orbital sums and fp32 networks (fp64 accumulation of
+                                   16-product chunks); 1: fp64 orbital sums and fp64 networks,
+                                   for force distributions with heavy tails (slower) */
     double rc;                  /* cutoff radius, A */
     double sigma;               /* Gaussian standard deviation, A */
     const double *mu;           /* [K] radial centres, A */

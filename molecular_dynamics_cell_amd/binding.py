@@ -29,7 +29,7 @@ class MPNNError(RuntimeError):
 
 class _Params(C.Structure):
     _fields_ = [("n_species", C.c_int32), ("K", C.c_int32), ("L", C.c_int32), ("T", C.c_int32),
-                ("hidden", C.c_int32), ("reserved", C.c_int32), ("rc", C.c_double),
+                ("hidden", C.c_int32), ("precision", C.c_int32), ("rc", C.c_double),
                 ("sigma", C.c_double), ("mu", C.POINTER(C.c_double)), ("c0", C.POINTER(C.c_double)),
                 ("mlp", C.POINTER(C.c_double)), ("layer_scale", C.POINTER(C.c_double)),
                 ("e_scale", C.c_double), ("mass", C.POINTER(C.c_double))]
@@ -110,7 +110,7 @@ class MPNN:
                       (params.mu, params.c0, params.packed_mlp(), params.layer_scale, params.masses)]
         dp = C.POINTER(C.c_double)
         mu, c0, mlp, sc, ms = (a.ctypes.data_as(dp) for a in self._keep)
-        self._p = _Params(s.n_species, s.K, s.L, s.T, s.H, 0, s.rc, s.sigma, mu, c0, mlp, sc,
+        self._p = _Params(s.n_species, s.K, s.L, s.T, s.H, int(s.precision), s.rc, s.sigma, mu, c0, mlp, sc,
                           float(params.e_scale), ms)
         h = C.c_void_p()
         self._check(lib().mpnn_create(C.byref(self._p), C.byref(h)), None)

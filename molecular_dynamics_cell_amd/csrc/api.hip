@@ -100,7 +100,7 @@ void Context::release(Buf &b) {
 
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
-    Buf *all[] = {&weights, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
+    Buf *all[] = {&weights, &weights64, &model, &perm, &inv_perm, &pos, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amap, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
@@ -172,7 +172,7 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     if (!out) return MPNN_E_INVALID_ARG;
     *out = nullptr;
     if (!p || !p->mu || !p->c0 || !p->mlp || !p->layer_scale || !p->mass) return MPNN_E_INVALID_ARG;
-    if (p->reserved != 0 || p->n_species < 1 || p->n_species > 16 || p->T < 1 || p->T > 8 ||
+    if ((p->precision != 0 && p->precision != 1) || p->n_species < 1 || p->n_species > 16 || p->T < 1 || p->T > 8 ||
         !mpnn::supported(p->K, p->L, p->hidden) || !(p->rc > 0) || !(p->sigma > 0))
         return MPNN_E_INVALID_ARG;
     for (int t = 0; t < p->T; ++t)
@@ -181,6 +181,7 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     if (!ctx) return MPNN_E_OOM;
     mpnn::Context &cx = ctx->cx;
     cx.S = p->n_species; cx.K = p->K; cx.L = p->L; cx.T = p->T; cx.H = p->hidden;
+    cx.precision = p->precision;
     cx.M = mpnn::n_mono(cx.L);
     cx.D = mpnn::n_feat(cx.K, cx.L);
     cx.DP = (cx.D + 15) / 16 * 16;

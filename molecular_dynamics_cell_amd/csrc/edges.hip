@@ -86,11 +86,11 @@ struct Basis {
 // one exponential E = exp(delta d / s^2) times 1 + (delta_k - delta) d / s^2 (the next term is below
 // 1e-11), so an edge needs two fp64 exponentials.  The cutoff is cos^2(pi d / (2 rc)) from the
 // Taylor series of cos to the t^18 term (truncation below 1e-14 on [0, pi/2]).
-template <int K, int L>
+template <int K, int L, typename S = float>
 struct BasisHP {
     static constexpr int M = n_mono(L);
-    float P[K];  // c_k R_k f_c
-    float A[M];
+    S P[K];  // c_k R_k f_c
+    S A[M];
 
     __device__ __forceinline__ void eval(double dx, double dy, double dz, const float *__restrict__ cv,
                                          const ModelDev *__restrict__ md) {
@@ -113,7 +113,7 @@ struct BasisHP {
         const double E = exp(md->g_e * d);
 #pragma unroll
         for (int k = 0; k < K; ++k) {
-            P[k] = (float)((double)cv[k] * R * fc);
+            P[k] = (S)((double)cv[k] * R * fc);
             if (k + 1 < K) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
         }
         const double ux = dx * md->inv_rc64, uy = dy * md->inv_rc64, uz = dz * md->inv_rc64;
@@ -126,7 +126,7 @@ struct BasisHP {
             pz[q] = pz[q - 1] * uz;
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m) A[m] = (float)(px[mono.lx[m]] * py[mono.ly[m]] * pz[mono.lz[m]]);
+        for (int m = 0; m < M; ++m) A[m] = (S)(px[mono.lx[m]] * py[mono.ly[m]] * pz[mono.lz[m]]);
     }
 };
 
@@ -310,6 +310,71 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
     // rows n..np-1 of the last block are padding: written, never read
     store_o_rows<K, L>(acc, lds, O + i0 * 16, np, std::make_integer_sequence<int, KMT>{});
     store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, std::make_integer_sequence<int, DT>{});
+}
+
+// Orbital sums in fp64 (the accurate mode): channels k in [P KB, (P+1) KB) of O^t_i, with the
+// basis factors and their products kept in fp64 and one rounding when O is stored.  The K = 12,
+// L = 3 orbital block is too large for fp64 registers in one pass, so it takes several passes over
+// the edges (KB M a multiple of 16, so each pass owns whole 16-column tiles of the O rows).
+template <int K, int L, int KB, int P>
+__global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, const double *__restrict__ pos,
+                                                     const int64_t *__restrict__ slab_off,
+                                                     const int32_t *__restrict__ nact,
+                                                     const int32_t *__restrict__ act_n, const float *__restrict__ c,
+                                                     const ModelDev *__restrict__ md, float *__restrict__ O) {
+    constexpr int M = n_mono(L), Q0 = P * KB * M;
+    constexpr int T0 = Q0 / 16, T1 = (KB == K ? pad16(K * M) : Q0 + KB * M) / 16;
+    static_assert(KB == K || (KB * M) % 16 == 0, "a pass must own whole 16-column tiles");
+    __shared__ float4 lds[5 * kBlock];
+    const int64_t i0 = xcd_block() * kBlock;
+    if (i0 >= n) return;
+    const int64_t i = i0 + threadIdx.x;
+    double acc[KB][M];
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[k][m] = 0.0;
+    if (i < n) {
+        const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+        const int64_t b0 = sell_base(slab_off, i);
+        const int na = nact[i];
+        for (int a = 0; a < na; ++a) {
+            const int64_t v = act_n[b0 + kSlab * a];
+            BasisHP<K, L, double> b;
+            b.eval(pos[3 * v] - xi, pos[3 * v + 1] - yi, pos[3 * v + 2] - zi, c + v * K, md);
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int m = 0; m < M; ++m) acc[k][m] = fma(b.P[P * KB + k], b.A[m], acc[k][m]);
+        }
+    }
+#pragma unroll
+    for (int kt = T0; kt < T1; ++kt) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int q = 16 * kt + j - Q0;
+            v[j] = (q < KB * M && P * KB + q / M < K) ? (float)acc[q / M][q % M] : 0.0f;
+        }
+        store_tile(v, lds, O + (int64_t)kt * np * 16 + i0 * 16);
+    }
+}
+
+// Density features from stored (column-tiled) O rows, fp64 sums; used after the fp64 passes.
+template <int K, int L>
+__global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const float *__restrict__ O,
+                                                  float inv_scale, float *__restrict__ feat) {
+    constexpr int M = n_mono(L), DT = pad16(n_feat(K, L)) / 16;
+    __shared__ float4 lds[5 * kBlock];
+    const int64_t i0 = (int64_t)blockIdx.x * kBlock;
+    if (i0 >= n) return;
+    const int64_t i = i0 + threadIdx.x;   // rows n..np-1 read and write padding
+    float o[K][M];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) o[k][m] = O[tiled(np, i, k * M + m)];
+    store_feature_rows<K, L>(o, inv_scale, lds, feat + i0 * 16, np, std::make_integer_sequence<int, DT>{});
 }
 
 // Reverse pass of layer t over one receiver row per thread (Eq. 4 as a VJP), with
@@ -548,10 +613,35 @@ Status aggregate(Context &cx, int t) {
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
-                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),
-                                      cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), cx.inv_scale_host[t],
-                                      Ot, Ft)));
+    if (cx.precision == 0) {
+        MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
+                                          cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
+                                          cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(),
+                                          cx.inv_scale_host[t], Ot, Ft)));
+        MPNN_HIP(hipGetLastError());
+        return Status::ok();
+    }
+#define MPNN_AGG64(KK, LL, KB, P)                                                                               \
+    k_aggregate64<KK, LL, KB, P><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                                     \
+        cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), \
+        ct, cx.model.as<ModelDev>(), Ot)
+    if (cx.K == 12 && cx.L == 3) {
+        MPNN_AGG64(12, 3, 4, 0);
+        MPNN_AGG64(12, 3, 4, 1);
+        MPNN_AGG64(12, 3, 4, 2);
+    } else if (cx.K == 8 && cx.L == 2) {
+        MPNN_AGG64(8, 2, 8, 0);
+    } else if (cx.K == 4 && cx.L == 2) {
+        MPNN_AGG64(4, 2, 4, 0);
+    } else if (cx.K == 2 && cx.L == 1) {
+        MPNN_AGG64(2, 1, 2, 0);
+    } else {
+        return Status::err(MPNN_E_INVALID_ARG, "unsupported (K, L)");
+    }
+#undef MPNN_AGG64
+    MPNN_HIP(hipGetLastError());
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_features<KK, LL><<<(unsigned)(cx.np / kBlock), kBlock, 0, cx.stream>>>(
+                                      cx.n, cx.np, Ot, cx.inv_scale_host[t], Ft)));
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

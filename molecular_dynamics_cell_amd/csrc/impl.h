@@ -62,10 +62,12 @@ struct NetLayout {
 struct Context {
     // ---- model ----
     int S = 0, K = 0, L = 0, T = 0, H = 0, M = 0, D = 0, DP = 0;
+    int precision = 0;  // 0: fp32 orbital sums / fp32 networks; 1: fp64 orbital sums and networks
     double rc = 0, sigma = 0, e_scale = 0;
     std::vector<double> mass;
     NetLayout net{};
     Buf weights;        // float, T*S blocks of net.stride
+    Buf weights64;      // the same in fp64 (precision 1)
     Buf model;          // ModelDev
     hipStream_t stream = nullptr;
 

@@ -12,6 +12,7 @@
 // per column tile; the VJP leaves dE/drho in the same layout for the reverse edge pass, which forms
 // dE/dO from it.
 #include <cmath>
+#include <type_traits>
 #include <vector>
 
 #include "impl.h"
@@ -82,6 +83,7 @@ constexpr int kMaxSpecies = 16;
 struct NetArgs {
     const float *F;        // rho^t / s_t, column-tiled [np][DP]
     const float *W;        // packed weights of (t, species 0); species s at W + s*stride
+    const double *W64;     // the same in fp64 (accurate mode)
     int64_t stride;
     int64_t oW1, oW2, oW3, oW1t, oW2t, oW3t, ob1, ob2, ob3;
     int S;
@@ -259,6 +261,151 @@ __global__ __launch_bounds__(64, (H == 128 && MODE == kBackward) ? 1 : 2) void k
     }
 }
 
+// ---- accurate mode: the same networks with fp64 operands on the fp64 matrix cores ----
+// v_mfma_f64_16x16x4f64 takes its A and B operands like the fp32 instruction (lane l: A row l%16,
+// B column l%16, k-step l/16) but returns row (l/16) + 4 r of column l%16 in accumulator item r
+// (the fp32 one returns row 4 (l/16) + r).  Fed back as the next B operand, item r of a 16-row
+// tile kt is then input 16 kt + 4 r + l/16, so the weights multiplying hidden activations are
+// packed in that interleaved order; W1, whose B operand is a float4 of stored features
+// (inputs 16 kt + 4 (l/16) + r), keeps the fp32 order.  Products and sums are exact to fp64
+// rounding and the activations stay in fp64 between layers; only the stored messages, energies
+// and dE/drho are rounded to fp32.
+typedef double doublex4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ doublex4 mfma64(double a, double b, doublex4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+template <int RT>
+__device__ __forceinline__ void gemm64_step(const double *__restrict__ W, int KT, int kt, const double (&x)[4],
+                                            doublex4 (&acc)[RT], int lane) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const double2 *w = reinterpret_cast<const double2 *>(W + ((size_t)(rt * KT + kt) * 64 + lane) * 4);
+        const double2 w01 = w[0], w23 = w[1];
+        acc[rt] = mfma64(w01.x, x[0], acc[rt]);
+        acc[rt] = mfma64(w01.y, x[1], acc[rt]);
+        acc[rt] = mfma64(w23.x, x[2], acc[rt]);
+        acc[rt] = mfma64(w23.y, x[3], acc[rt]);
+    }
+}
+
+// accumulator item r of lane group grp holds output row 16 rt + grp + 4 r
+template <int RT>
+__device__ __forceinline__ void init64(doublex4 (&acc)[RT], const double *__restrict__ b, int grp) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rt][i] = b ? b[16 * rt + grp + 4 * i] : 0.0;
+}
+
+template <int K, int L, int H, int MODE>
+__global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
+    constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
+    constexpr int DT = DP / 16, HT = H / 16;
+    const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
+    const int tile = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.S && tile >= a.tile_start[s + 1]) ++s;
+    const int64_t base = (int64_t)(tile - a.tile_start[s]) * 16;
+    const int64_t cnt = a.sp_off[s + 1] - a.sp_off[s];
+    const int64_t me = (base + col < cnt) ? (int64_t)a.sp_list[a.sp_off[s] + base + col] : -1;
+    const double *W = a.W64 + (int64_t)s * a.stride;
+    // silu' of both hidden layers, parked in LDS for the reverse pass
+    __shared__ double sd[MODE == kForward ? 1 : 2 * HT * 4][64];
+
+    doublex4 z1[HT];
+    init64(z1, W + a.ob1, grp);
+#pragma unroll 1
+    for (int kt = 0; kt < DT; ++kt) {
+        float4 f = float4{0.f, 0.f, 0.f, 0.f};
+        if (me >= 0) f = *reinterpret_cast<const float4 *>(a.F + tiled(a.np, me, 16 * kt + 4 * grp));
+        const double x[4] = {f.x, f.y, f.z, f.w};
+        gemm64_step<HT>(W + a.oW1, DT, kt, x, z1, lane);
+    }
+    double h1[HT][4];
+#pragma unroll
+    for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double z = z1[rt][i], sg = 1.0 / (1.0 + exp(-z));
+            h1[rt][i] = z * sg;
+            if constexpr (MODE != kForward) sd[rt * 4 + i][lane] = sg * (1.0 + z * (1.0 - sg));
+        }
+    doublex4 z2[HT];
+    __builtin_amdgcn_sched_barrier(0);
+    init64(z2, W + a.ob2, grp);
+#pragma unroll
+    for (int kt = 0; kt < HT; ++kt) gemm64_step<HT>(W + a.oW2, HT, kt, h1[kt], z2, lane);
+    double h2[HT][4];
+#pragma unroll
+    for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double z = z2[rt][i], sg = 1.0 / (1.0 + exp(-z));
+            h2[rt][i] = z * sg;
+            if constexpr (MODE != kForward) sd[(HT + rt) * 4 + i][lane] = sg * (1.0 + z * (1.0 - sg));
+        }
+    if constexpr (MODE != kBackward) {
+        doublex4 y[1];
+        init64(y, W + a.ob3, grp);
+#pragma unroll
+        for (int kt = 0; kt < HT; ++kt) gemm64_step<1>(W + a.oW3, HT, kt, h2[kt], y, lane);
+        if (me >= 0) {
+            if constexpr (MODE == kForward) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = grp + 4 * i;
+                    if (k < K) a.c_next[me * K + k] = (float)y[0][i];
+                }
+            } else {
+                if (grp == 0) a.Ei[me] = (float)((double)a.e_scale * y[0][0]);
+            }
+        }
+    }
+    if constexpr (MODE != kForward) {
+        double gy[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = grp + 4 * i;
+            if constexpr (MODE == kEnergy) gy[i] = (k == 0) ? (double)a.e_scale : 0.0;
+            else gy[i] = (k < K && me >= 0) ? (double)a.Gc[me * K + k] : 0.0;
+        }
+        doublex4 g2[HT];
+        __builtin_amdgcn_sched_barrier(0);
+        init64<HT>(g2, nullptr, grp);
+        gemm64_step<HT>(W + a.oW3t, 1, 0, gy, g2, lane);
+        double gz2[HT][4];
+#pragma unroll
+        for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gz2[rt][i] = g2[rt][i] * sd[(HT + rt) * 4 + i][lane];
+        doublex4 g1[HT];
+        init64<HT>(g1, nullptr, grp);
+#pragma unroll
+        for (int kt = 0; kt < HT; ++kt) gemm64_step<HT>(W + a.oW2t, HT, kt, gz2[kt], g1, lane);
+        double gz1[HT][4];
+#pragma unroll
+        for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) gz1[rt][i] = g1[rt][i] * sd[rt * 4 + i][lane];
+        const double inv_scale = a.inv_scale;
+#pragma unroll 1
+        for (int rt = 0; rt < DT; ++rt) {
+            doublex4 gr[1];
+            init64<1>(gr, nullptr, grp);
+#pragma unroll
+            for (int kt = 0; kt < HT; ++kt)
+                gemm64_step<1>(W + a.oW1t + (size_t)rt * HT * 64 * 4, HT, kt, gz1[kt], gr, lane);
+            if (me >= 0)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.Grho[tiled(a.np, me, 16 * rt + grp + 4 * i)] = (float)(gr[0][i] * inv_scale);
+        }
+    }
+}
+
 // atom tiles per wave: one (16 atoms); two would let each weight load feed two tiles, but the
 // fp64 chunk accumulators then exceed the register budget
 constexpr int tiles_per_wave(int) { return 1; }
@@ -266,6 +413,7 @@ constexpr int tiles_per_wave(int) { return 1; }
 NetArgs make_args(Context &cx, int t) {
     NetArgs a{};
     a.W = cx.weights.as<float>() + (int64_t)t * cx.S * cx.net.stride;
+    a.W64 = cx.precision ? cx.weights64.as<double>() + (int64_t)t * cx.S * cx.net.stride : nullptr;
     a.stride = (int64_t)cx.net.stride;
     a.oW1 = cx.net.W1; a.oW2 = cx.net.W2; a.oW3 = cx.net.W3;
     a.oW1t = cx.net.W1t; a.oW2t = cx.net.W2t; a.oW3t = cx.net.W3t;
@@ -291,8 +439,11 @@ NetArgs make_args(Context &cx, int t) {
     return a;
 }
 
-#define MPNN_NET(K_, L_, H_, MODE_, A_) \
-    k_net<K_, L_, H_, MODE_, tiles_per_wave(H_)><<<tiles, 64, 0, cx.stream>>>(A_)
+#define MPNN_NET(K_, L_, H_, MODE_, A_)                                                          \
+    do {                                                                                         \
+        if (cx.precision) k_net64<K_, L_, H_, MODE_><<<tiles, 64, 0, cx.stream>>>(A_);          \
+        else k_net<K_, L_, H_, MODE_, tiles_per_wave(H_)><<<tiles, 64, 0, cx.stream>>>(A_);      \
+    } while (0)
 
 #define MPNN_DISPATCH_NET(MODE_, A_)                                                                    \
     do {                                                                                                \
@@ -310,16 +461,20 @@ NetArgs make_args(Context &cx, int t) {
 
 // A-operand packing of W [R][C] (row-major, fp64) for Y^T = W X^T: for row tile rt, column tile
 // ct, lane l, component i: W[16 rt + l%16][16 ct + 4 (l/16) + i] (zero outside R x C).
-void pack_a(const double *W, int R, int C, int Rp, int Cp, bool transpose, float *out) {
+// interleaved: column 16 ct + 4 i + l/16 instead (the fp64 accumulator order, for the fp64
+// weights that multiply hidden activations)
+template <typename T>
+void pack_a(const double *W, int R, int C, int Rp, int Cp, bool transpose, T *out, bool interleaved = false) {
     const int RT = Rp / 16, CT = Cp / 16;
     for (int rt = 0; rt < RT; ++rt)
         for (int ct = 0; ct < CT; ++ct)
             for (int l = 0; l < 64; ++l)
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * rt + (l & 15), c = 16 * ct + 4 * (l >> 4) + i;
+                    const int r = 16 * rt + (l & 15);
+                    const int c = interleaved ? 16 * ct + 4 * i + (l >> 4) : 16 * ct + 4 * (l >> 4) + i;
                     double v = 0.0;
                     if (r < R && c < C) v = transpose ? W[(size_t)c * R + r] : W[(size_t)r * C + c];
-                    out[(((size_t)rt * CT + ct) * 64 + l) * 4 + i] = (float)v;
+                    out[(((size_t)rt * CT + ct) * 64 + l) * 4 + i] = (T)v;
                 }
 }
 
@@ -339,30 +494,42 @@ Status pack_weights(Context &cx, const double *mlp) {
     nl.b2 = o; o += H;
     nl.b3 = o; o += 16;
     nl.stride = (o + 63) / 64 * 64;
-    std::vector<float> host((size_t)cx.T * cx.S * nl.stride, 0.0f);
-    const double *p = mlp;
-    for (int t = 0; t < cx.T; ++t) {
-        const int out = t < cx.T - 1 ? K : 1;
-        for (int s = 0; s < cx.S; ++s) {
-            float *blk = host.data() + ((size_t)t * cx.S + s) * nl.stride;
-            const double *W1 = p, *b1 = W1 + (size_t)H * D, *W2 = b1 + H, *b2 = W2 + (size_t)H * H;
-            const double *W3 = b2 + H, *b3 = W3 + (size_t)out * H;
-            p = b3 + out;
-            pack_a(W1, H, D, H, DP, false, blk + nl.W1);
-            pack_a(W2, H, H, H, H, false, blk + nl.W2);
-            pack_a(W3, out, H, 16, H, false, blk + nl.W3);
-            pack_a(W1, D, H, DP, H, true, blk + nl.W1t);
-            pack_a(W2, H, H, H, H, true, blk + nl.W2t);
-            pack_a(W3, H, out, H, 16, true, blk + nl.W3t);
-            for (int h = 0; h < H; ++h) {
-                blk[nl.b1 + h] = (float)b1[h];
-                blk[nl.b2 + h] = (float)b2[h];
+    auto fill = [&](auto *host) {
+        using T = std::remove_pointer_t<decltype(host)>;
+        constexpr bool il = std::is_same<T, double>::value;   // fp64 weights: interleaved order
+        const double *p = mlp;
+        for (int t = 0; t < cx.T; ++t) {
+            const int out = t < cx.T - 1 ? K : 1;
+            for (int s = 0; s < cx.S; ++s) {
+                T *blk = host + ((size_t)t * cx.S + s) * nl.stride;
+                const double *W1 = p, *b1 = W1 + (size_t)H * D, *W2 = b1 + H, *b2 = W2 + (size_t)H * H;
+                const double *W3 = b2 + H, *b3 = W3 + (size_t)out * H;
+                p = b3 + out;
+                pack_a(W1, H, D, H, DP, false, blk + nl.W1);
+                pack_a(W2, H, H, H, H, false, blk + nl.W2, il);
+                pack_a(W3, out, H, 16, H, false, blk + nl.W3, il);
+                pack_a(W1, D, H, DP, H, true, blk + nl.W1t, il);
+                pack_a(W2, H, H, H, H, true, blk + nl.W2t, il);
+                pack_a(W3, H, out, H, 16, true, blk + nl.W3t, il);
+                for (int h = 0; h < H; ++h) {
+                    blk[nl.b1 + h] = (T)b1[h];
+                    blk[nl.b2 + h] = (T)b2[h];
+                }
+                for (int k = 0; k < out; ++k) blk[nl.b3 + k] = (T)b3[k];
             }
-            for (int k = 0; k < out; ++k) blk[nl.b3 + k] = (float)b3[k];
         }
-    }
+    };
+    const size_t count = (size_t)cx.T * cx.S * nl.stride;
+    std::vector<float> host(count, 0.0f);
+    fill(host.data());
     MPNN_TRY(cx.grow(cx.weights, host.size() * sizeof(float)));
     MPNN_HIP(hipMemcpy(cx.weights.p, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice));
+    if (cx.precision) {
+        std::vector<double> host64(count, 0.0);
+        fill(host64.data());
+        MPNN_TRY(cx.grow(cx.weights64, host64.size() * sizeof(double)));
+        MPNN_HIP(hipMemcpy(cx.weights64.p, host64.data(), host64.size() * sizeof(double), hipMemcpyHostToDevice));
+    }
     return Status::ok();
 }
 

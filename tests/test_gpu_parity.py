@@ -21,14 +21,25 @@ CASES = {
     "water60_T3": (2, lambda: systems.water_molecules(60, 17.0)),
     "HEA432_K12L3": (3, lambda: systems.hea(6)),
     "CHON4002_K12L3": (5, lambda: I.make_system(5, reduced=True)),
+    # the other arithmetic mode on the same systems: fp64 orbital sums and networks for K=8,
+    # fp32 for the CHON model (whose default is fp64)
+    "Ag4000_cfg4model_fp64": (4, lambda: systems.ag(10, seed=4), 1),
+    "CHON4002_K12L3_fp32": (5, lambda: I.make_system(5, reduced=True), 0),
 }
+
+
+def _params(name):
+    cfg, _, *prec = CASES[name]
+    p = I.make_params(cfg)
+    if prec:
+        p.spec.precision = prec[0]
+    return p
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_pairs_bit_exact(name):
-    cfg, make = CASES[name]
-    s = make()
-    p = I.make_params(cfg)
+    s = CASES[name][1]()
+    p = _params(name)
     say(f"[pairs] {name} n={s.n}")
     m = gpu_model(p, s)
     gi, gj, gs = (t.cpu().numpy() for t in m.get_pairs())
@@ -42,9 +53,8 @@ def test_pairs_bit_exact(name):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_energy_forces(name):
-    cfg, make = CASES[name]
-    s = make()
-    p = I.make_params(cfg)
+    s = CASES[name][1]()
+    p = _params(name)
     say(f"[ef] {name} n={s.n}")
     m = gpu_model(p, s)
     E, F, Ei = m.energy_forces(atom_energy=True)
