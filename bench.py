@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--ef-evals", type=int, default=10)
+    ap.add_argument("--precision", type=int, choices=(0, 1), default=None,
+                    help="arithmetic mode (0 fp32 orbital sums/networks, 1 fp64); default: the workload's")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +185,8 @@ def main():
     t_setup = time.perf_counter()
     s = I.make_system(cfg)
     p = I.make_params(cfg)
+    if args.precision is not None:
+        p.spec.precision = args.precision
     m = binding.MPNN(p, dev)
     pos = torch.tensor(s.pos, device=dev)
     m.build_neighbors(pos, torch.tensor(s.types, device=dev), s.box)
@@ -254,7 +258,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64" if p.spec.precision else "f32",
         "data": "synthetic",
         "config": {"workload": f"{s.name}: {s.n} atoms + {info['n_ghost']} ghosts, T={p.spec.T}, "
                                f"K={p.spec.K}, L={p.spec.L}, MLP 2x{p.spec.H}, rc={p.spec.rc}, "
