@@ -7,6 +7,8 @@
 //
 // Every reduction has a fixed order (one thread owns one output row and walks its list), so
 // results are bitwise reproducible and no floating-point atomics are used.
+#include <algorithm>
+#include <cmath>
 #include <utility>
 
 #include "impl.h"
@@ -245,25 +247,35 @@ __device__ __forceinline__ void assemble_go_row(const float *__restrict__ grho, 
 // expression as the build), compacted in row order into the row's leading slots (sender node of
 // active entry a at slot base + 64 a), plus the map from every Verlet slot to its active slot
 // (-1: outside rc).  Per-edge outputs live in active slots, so the row kernels write them
-// coalesced and the sender-major gathers find them through the map.
+// coalesced and the sender-major gathers find them through the map.  The test first uses the
+// fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of the fp64 value
+// (a bound from the coordinate range, see compact_active), so only entries inside
+// rc^2 -/+ band, a vanishing fraction, repeat it in fp64.
 __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
+                                                 const float4 *__restrict__ pos32,
                                                  const int64_t *__restrict__ slab_off,
                                                  const int32_t *__restrict__ len,
-                                                 const int32_t *__restrict__ nbr, double rc2,
+                                                 const int32_t *__restrict__ nbr, double rc2, float lo, float hi,
                                                  int32_t *__restrict__ amap, int32_t *__restrict__ act_n,
                                                  int32_t *__restrict__ nact) {
     const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const float4 pi = pos32[i];
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
     int o = 0;
     for (int j = 0; j < nl; ++j) {
         const int64_t e = b + kSlab * j;
         const int64_t v = nbr[e];
-        const double d2 = d2_exact(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi),
-                                   __dsub_rn(pos[3 * v + 2], zi));
-        if (d2 < rc2) {
+        const float4 pv = pos32[v];
+        const float dx = pv.x - pi.x, dy = pv.y - pi.y, dz = pv.z - pi.z;
+        const float d2f = dx * dx + dy * dy + dz * dz;
+        bool act = d2f < lo;
+        if (!act && d2f < hi) {
+            const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+            act = d2_exact(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi)) < rc2;
+        }
+        if (act) {
             act_n[b + kSlab * o] = (int32_t)v;
             amap[e] = (int32_t)(b + kSlab * o);
             ++o;
@@ -600,8 +612,18 @@ __global__ __launch_bounds__(256) void k_assemble_go(int64_t n, int64_t np, cons
 Status compact_active(Context &cx) {
     ProfScope ps_(cx, kProfCompact);
     if (cx.n == 0) return Status::ok();
-    k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
-                                                        cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(), cx.rc * cx.rc, cx.amap.as<int32_t>(),
+    // |d^2(fp32 positions) - d^2(fp64)| bound: coordinates stay within [-c, c], c = largest box
+    // edge + rc + 2 skin (ghost shell and drift), so each rounded coordinate is off by at most
+    // eps = c 2^-24, a difference by 2 eps + 2^-24 |dx|, and d^2 <= rc^2 by
+    // 4 sqrt(3) eps rc + 4 2^-23 rc^2 (+ second-order terms); the band is twice that.
+    const double c = std::max(cx.box[0], std::max(cx.box[1], cx.box[2])) + cx.rc + 2.0 * cx.skin;
+    const double eps = c * std::ldexp(1.0, -24);
+    const double band = 2.0 * (4.0 * std::sqrt(3.0) * eps * cx.rc + 4.0 * std::ldexp(1.0, -23) * cx.rc * cx.rc) + 1e-9;
+    const double rc2 = cx.rc * cx.rc;
+    const float lo = (float)(rc2 - band), hi = (float)(rc2 + band);
+    k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(),
+                                                        cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
+                                                        cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amap.as<int32_t>(),
                                                         cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     return Status::ok();

@@ -87,6 +87,7 @@ struct Context {
     // per-atom / per-node state (sorted, locals first then ghosts)
     Buf perm, inv_perm;             // int32 [n]: sorted -> caller, caller -> sorted
     Buf pos;                        // double [NN][3]
+    Buf pos32;                      // float4 [NN]: positions rounded to fp32 (active-edge pre-test)
     Buf vel;                        // double [n][3]
     Buf ref;                        // double [n][3], positions at the last build
     Buf types;                      // int32 [NN]

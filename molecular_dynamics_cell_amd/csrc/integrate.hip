@@ -4,6 +4,8 @@
 #include <cmath>
 #include <cstring>
 
+#include <algorithm>
+
 #include "impl.h"
 
 namespace mpnn {
@@ -78,14 +80,19 @@ int64_t red_blocks(int64_t n) {
 }
 
 // v += (dt/2) a F / m; x += dt v; flag an atom that moved more than skin/2 since the build.
-__global__ void k_kick_drift(int64_t n, double dt, double half_skin2, const int32_t *__restrict__ types,
-                             const ModelDev *__restrict__ md, const double *__restrict__ F,
-                             double *__restrict__ vel, double *__restrict__ pos, const double *__restrict__ ref,
-                             unsigned long long *__restrict__ flag) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    double d2 = 0.0;
-    if (i < n) {
+// First half-kick and drift of every atom, and the largest displacement since the last build
+// (grid-stride loop; one atomic per block, so a 2M-atom step issues about 2K atomics instead of
+// one per wave on the same word).
+__global__ __launch_bounds__(256) void k_kick_drift(int64_t n, double dt, double half_skin2,
+                                                    const int32_t *__restrict__ types,
+                                                    const ModelDev *__restrict__ md, const double *__restrict__ F,
+                                                    double *__restrict__ vel, double *__restrict__ pos,
+                                                    const double *__restrict__ ref,
+                                                    unsigned long long *__restrict__ flag) {
+    double d2max = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const double a = 0.5 * dt * kAccel / md->mass[types[i]];
+        double d2 = 0.0;
         for (int c = 0; c < 3; ++c) {
             const double v = vel[3 * i + c] + a * F[3 * i + c];
             vel[3 * i + c] = v;
@@ -94,14 +101,20 @@ __global__ void k_kick_drift(int64_t n, double dt, double half_skin2, const int3
             const double dd = x - ref[3 * i + c];
             d2 += dd * dd;
         }
+        // a NaN displacement must trip the rebuild test: map it to +inf
+        d2max = fmax(d2max, d2 == d2 ? d2 : INFINITY);
     }
-    // one atomic per wave: wave maximum of d2 (non-negative doubles order like their bits)
-    unsigned long long bits = (unsigned long long)__double_as_longlong(d2);
+    // block maximum (non-negative doubles order like their bit patterns)
+    unsigned long long bits = (unsigned long long)__double_as_longlong(d2max);
     for (int o = 32; o > 0; o >>= 1) {
         const unsigned long long other = __shfl_xor(bits, o);
         bits = other > bits ? other : bits;
     }
-    if ((threadIdx.x & 63) == 0) {
+    __shared__ unsigned long long wmax[kBlock / 64];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = bits;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) bits = wmax[w] > bits ? wmax[w] : bits;
         if (__longlong_as_double((long long)bits) > half_skin2) atomicOr(&flag[0], 1ull);
         atomicMax(&flag[1], bits);
     }
@@ -186,7 +199,8 @@ Status kick_drift(Context &cx, double dt) {
     ProfScope ps_(cx, kProfKickDrift);
     if (cx.n == 0) return Status::ok();
     const double hs = 0.5 * cx.skin;
-    k_kick_drift<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, dt, hs * hs, cx.types.as<int32_t>(),
+    const unsigned blocks = (unsigned)std::min<int64_t>((cx.n + kBlock - 1) / kBlock, 2048);
+    k_kick_drift<<<blocks, kBlock, 0, cx.stream>>>(cx.n, dt, hs * hs, cx.types.as<int32_t>(),
                                                            cx.model.as<ModelDev>(), cx.F.as<double>(),
                                                            cx.vel.as<double>(), cx.pos.as<double>(),
                                                            cx.ref.as<double>(), cx.flag.as<unsigned long long>());

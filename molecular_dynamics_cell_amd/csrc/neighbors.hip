@@ -207,6 +207,13 @@ __global__ void k_ghost_pos(int64_t G, int64_t n, const int32_t *__restrict__ ow
     if (types) types[n + k] = types[o];
 }
 
+// fp32 copy of every node's position for the active-edge pre-test
+__global__ void k_pos32(int64_t NN, const double *__restrict__ pos, float4 *__restrict__ pos32) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= NN) return;
+    pos32[v] = float4{(float)pos[3 * v], (float)pos[3 * v + 1], (float)pos[3 * v + 2], 0.0f};
+}
+
 __device__ __forceinline__ int ext_cell(double x, double h, int n) {
     int c = (int)floor(__ddiv_rn(x, h)) + 1;
     return c < 0 ? 0 : (c > n + 1 ? n + 1 : c);
@@ -605,6 +612,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.feat, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.grho, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.pos32, sizeof(float4) * NN1));
     MPNN_TRY(cx.grow(cx.amap, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
@@ -625,12 +633,17 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
 
 Status refresh_ghost_positions(Context &cx) {
     ProfScope ps_(cx, kProfGhostPos);
-    if (cx.G == 0) return Status::ok();
-    const Grid g = make_grid(cx);
-    k_ghost_pos<<<grid_for(cx.G), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.ghost_owner.as<int32_t>(),
-                                                           cx.ghost_code.as<int32_t>(), g, cx.pos.as<double>(),
-                                                           nullptr);
-    MPNN_HIP(hipGetLastError());
+    if (cx.G > 0) {
+        const Grid g = make_grid(cx);
+        k_ghost_pos<<<grid_for(cx.G), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.ghost_owner.as<int32_t>(),
+                                                               cx.ghost_code.as<int32_t>(), g, cx.pos.as<double>(),
+                                                               nullptr);
+        MPNN_HIP(hipGetLastError());
+    }
+    if (cx.NN > 0) {
+        k_pos32<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.pos.as<double>(), cx.pos32.as<float4>());
+        MPNN_HIP(hipGetLastError());
+    }
     return Status::ok();
 }
 
