@@ -264,23 +264,35 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
     int o = 0;
-    for (int j = 0; j < nl; ++j) {
-        const int64_t e = b + kSlab * j;
-        const int64_t v = nbr[e];
-        const float4 pv = pos32[v];
-        const float dx = pv.x - pi.x, dy = pv.y - pi.y, dz = pv.z - pi.z;
-        const float d2f = dx * dx + dy * dy + dz * dz;
-        bool act = d2f < lo;
-        if (!act && d2f < hi) {
-            const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
-            act = d2_exact(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi)) < rc2;
-        }
-        if (act) {
-            act_n[b + kSlab * o] = (int32_t)v;
-            amap[e] = (int32_t)(b + kSlab * o);
-            ++o;
-        } else {
-            amap[e] = -1;
+    // four entries per step: their index and position loads are all in flight together
+    constexpr int U = 4;
+    for (int j0 = 0; j0 < nl; j0 += U) {
+        int32_t v[U];
+        float4 pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = j0 + u < nl ? nbr[b + kSlab * (j0 + u)] : (int32_t)i;
+#pragma unroll
+        for (int u = 0; u < U; ++u) pv[u] = pos32[v[u]];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (j0 + u >= nl) break;
+            const float dx = pv[u].x - pi.x, dy = pv[u].y - pi.y, dz = pv[u].z - pi.z;
+            const float d2f = dx * dx + dy * dy + dz * dz;
+            bool act = d2f < lo;
+            if (!act && d2f < hi) {
+                const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+                const int64_t w = v[u];
+                act = d2_exact(__dsub_rn(pos[3 * w], xi), __dsub_rn(pos[3 * w + 1], yi),
+                               __dsub_rn(pos[3 * w + 2], zi)) < rc2;
+            }
+            const int64_t e = b + kSlab * (j0 + u);
+            if (act) {
+                act_n[b + kSlab * o] = v[u];
+                amap[e] = (int32_t)(b + kSlab * o);
+                ++o;
+            } else {
+                amap[e] = -1;
+            }
         }
     }
     nact[i] = o;
@@ -494,18 +506,35 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
     for (int k = 0; k < K; ++k) acc[k] = 0.0f;
     if (ok) {
         const int64_t s1 = t_off[v + 1];
-        for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-            int32_t a;
+        // two entries per lane per step, so both lookups are in flight together
+        for (int64_t s = t_off[v] + q; s < s1; s += 2 * kGatherLanes) {
+            const bool two = s + kGatherLanes < s1;
+            int32_t a0, a1 = -1;
             if (BUILD) {
-                a = amap[t_eid[s]];
-                t_act[s] = a;
+                const int32_t e0 = t_eid[s], e1 = two ? t_eid[s + kGatherLanes] : 0;
+                a0 = amap[e0];
+                if (two) a1 = amap[e1];
+                t_act[s] = a0;
+                if (two) t_act[s + kGatherLanes] = a1;
             } else {
-                a = t_act[s];
+                a0 = t_act[s];
+                if (two) a1 = t_act[s + kGatherLanes];
             }
-            if (a < 0) continue;
-            const float *we = w + (int64_t)a * K;
+            float w0[K], w1[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k) acc[k] += we[k];
+            for (int k = 0; k < K; ++k) w0[k] = w1[k] = 0.0f;
+            if (a0 >= 0) {
+                const float *p = w + (int64_t)a0 * K;
+#pragma unroll
+                for (int k = 0; k < K; ++k) w0[k] = p[k];
+            }
+            if (a1 >= 0) {
+                const float *p = w + (int64_t)a1 * K;
+#pragma unroll
+                for (int k = 0; k < K; ++k) w1[k] = p[k];
+            }
+#pragma unroll
+            for (int k = 0; k < K; ++k) acc[k] += w0[k] + w1[k];
         }
     }
 #pragma unroll
@@ -562,13 +591,15 @@ __global__ __launch_bounds__(256) void k_force_gather(int64_t n, const int32_t *
         for (int64_t vv = -1; vv < g1 - g0; ++vv) {       // the atom itself, then its ghost images
             const int64_t v = vv < 0 ? i : n + g0 + vv;
             const int64_t s1 = t_off[v + 1];
-            for (int64_t s = t_off[v] + q; s < s1; s += kGatherLanes) {
-                const int32_t a = t_act[s];
-                if (a < 0) continue;
-                const float *ge = gedge + 3 * (int64_t)a;
-                f[0] -= (double)ge[0];
-                f[1] -= (double)ge[1];
-                f[2] -= (double)ge[2];
+            for (int64_t s = t_off[v] + q; s < s1; s += 2 * kGatherLanes) {
+                const bool two = s + kGatherLanes < s1;
+                const int32_t a0 = t_act[s], a1 = two ? t_act[s + kGatherLanes] : -1;
+                float g0[3] = {0.f, 0.f, 0.f}, g1[3] = {0.f, 0.f, 0.f};
+                if (a0 >= 0)
+                    for (int c = 0; c < 3; ++c) g0[c] = gedge[3 * (int64_t)a0 + c];
+                if (a1 >= 0)
+                    for (int c = 0; c < 3; ++c) g1[c] = gedge[3 * (int64_t)a1 + c];
+                for (int c = 0; c < 3; ++c) f[c] -= (double)g0[c] + (double)g1[c];
             }
         }
     }
