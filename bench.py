@@ -37,41 +37,47 @@ def kernel_model(fam, g):
     written, per-edge outputs); gathered neighbour data (positions, messages) is counted once
     per node, not per edge.  Flops count the contractions of the method per active edge or
     per atom (multiply-add = 2), not the basis transcendentals.  N local atoms, NN nodes,
-    EL Verlet entries, EA active entries (d < rc)."""
+    EL Verlet entries, EA active entries (d < rc); per-atom rows are padded to 16 floats
+    (KMP = pad16(K M) orbital coefficients, DP = pad16(D) density features)."""
     N, NN, EL, EA = g["N"], g["NN"], g["EL"], g["EA"]
     K, M, D, H, T = g["K"], g["M"], g["D"], g["H"], g["T"]
     KM = K * M
+    KMP, DP = (KM + 15) // 16 * 16, (D + 15) // 16 * 16
     if fam == "compact":
-        b = 8 * (N + 1) + 4 * EL + 24 * NN + 8 * EA + 4 * N + (EL - EA) * (12 + 4 * K)
+        # row lengths, neighbour ids, fp32 positions (per node), active map and list, counts
+        b = 4 * N + 4 * EL + 16 * NN + 4 * EL + 4 * EA + 4 * N
         return b, 8 * EL, "hbm"
     if fam == "aggregate":
-        b = 8 * (N + 1) + 4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * KM * N
+        # counts, active list, positions and messages (per node); O and feature rows out
+        b = 4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * KMP * N + 4 * DP * N
         f = EA * (2 * KM + 2 * K)
         return b, f, "alu"
     if fam == "backward_layer":
         w_frac = (T - 1) / T                       # layers that emit dE/dc edge terms
-        g_rw = (12 + 24 * (T - 1)) / T             # first layer writes, later ones accumulate
-        b = (8 * (N + 1) + 4 * N + 8 * EA + 24 * NN + 4 * K * NN + 4 * KM * N
+        g_rw = (12 + 24 * (T - 1)) / T             # first layer writes dE/dr, later ones accumulate
+        b = (4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * DP * N + 4 * KMP * N
              + w_frac * 4 * K * EA + g_rw * EA + 24 * N * (2 * T - 1) / T)
         f = EA * (4 * KM + 6 * K + 6 * M)
         return b, f, "alu"
     if fam == "message_grad":
-        b = 8 * (NN + 1) + 4 * EL + 4 * K * EL + 4 * K * NN
-        return b, K * EL, "hbm"
+        build = 4 * EL + 4 * EL + 4 * EL           # transposed ids, active map (random), t_act out
+        rest = 4 * EL                              # t_act in
+        b = 8 * NN + (build + (T - 2) * rest) / max(T - 1, 1) + 4 * K * EA + 4 * K * NN
+        return b, K * EA, "hbm"
     if fam == "force_gather":
-        b = 8 * (NN + 1) + 8 * (N + 1) + 4 * EL + 12 * EL + 24 * N + 48 * N
-        return b, 3 * EL, "hbm"
+        b = 8 * NN + 4 * EL + 12 * EA + 8 * N + 24 * N + 48 * N
+        return b, 3 * EA, "hbm"
     if fam == "net_forward":
-        b = 4 * KM * N + 4 * K * N
+        b = 4 * DP * N + 4 * K * N
         f = N * 2 * (H * D + H * H + K * H)
         return b, f, "mfma"
     if fam == "net_energy":
-        b = 8 * KM * N + 4 * N
-        f = N * 2 * (2 * H * D + 2 * H * H + 2 * H) + N * 2 * K * KM
+        b = 4 * DP * N + 4 * N + 4 * DP * N
+        f = N * 2 * (2 * H * D + 2 * H * H + 2 * H)
         return b, f, "mfma"
     if fam == "net_backward":
-        b = 8 * KM * N + 4 * K * N
-        f = N * 2 * (2 * H * D + 2 * H * H + K * H + K * H) + N * 2 * K * KM
+        b = 4 * DP * N + 4 * K * N + 4 * DP * N
+        f = N * 2 * (2 * H * D + 2 * H * H + K * H + K * H)
         return b, f, "mfma"
     return None
 
