@@ -44,8 +44,8 @@ def kernel_model(fam, g):
     KM = K * M
     KMP, DP = (KM + 15) // 16 * 16, (D + 15) // 16 * 16
     if fam == "compact":
-        # row lengths, neighbour ids, fp32 positions (per node), active map and list, counts
-        b = 4 * N + 4 * EL + 16 * NN + 4 * EL + 4 * EA + 4 * N
+        # row lengths, neighbour ids, fp32 positions (per node), activity bits, active list, counts
+        b = 4 * N + 4 * EL + 16 * NN + EL / 8 + 4 * EA + 4 * N
         return b, 8 * EL, "hbm"
     if fam == "aggregate":
         # counts, active list, positions and messages (per node); O and feature rows out
@@ -60,7 +60,7 @@ def kernel_model(fam, g):
         f = EA * (4 * KM + 6 * K + 6 * M)
         return b, f, "alu"
     if fam == "message_grad":
-        build = 4 * EL + 4 * EL + 4 * EL           # transposed ids, active map (random), t_act out
+        build = 4 * EL + 4 * EL + EL / 8 + 4 * EL  # transposed ids and receivers, activity bits, t_act out
         rest = 4 * EL                              # t_act in
         b = 8 * NN + (build + (T - 2) * rest) / max(T - 1, 1) + 4 * K * EA + 4 * K * NN
         return b, K * EA, "hbm"

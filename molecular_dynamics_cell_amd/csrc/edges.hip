@@ -245,18 +245,19 @@ __device__ __forceinline__ void assemble_go_row(const float *__restrict__ grho, 
 
 // Per-step active list: the Verlet entries of each row with d^2 < rc^2 (fp64, the same
 // expression as the build), compacted in row order into the row's leading slots (sender node of
-// active entry a at slot base + 64 a), plus the map from every Verlet slot to its active slot
-// (-1: outside rc).  Per-edge outputs live in active slots, so the row kernels write them
-// coalesced and the sender-major gathers find them through the map.  The test first uses the
-// fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of the fp64 value
-// (a bound from the coordinate range, see compact_active), so only entries inside
+// active entry a at slot base + 64 a), plus one activity bit per Verlet entry (word j/32, bit j%32
+// of the row's mask).  Per-edge outputs live in active slots, so the row kernels write them
+// coalesced; a sender-major gather finds the active slot of an entry by counting the set bits
+// before it (the masks are 32x smaller than a per-entry slot map and stay in cache).  The test
+// first uses the fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of
+// the fp64 value (a bound from the coordinate range, see compact_active), so only entries inside
 // rc^2 -/+ band, a vanishing fraction, repeat it in fp64.
 __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
                                                  const float4 *__restrict__ pos32,
                                                  const int64_t *__restrict__ slab_off,
                                                  const int32_t *__restrict__ len,
                                                  const int32_t *__restrict__ nbr, double rc2, float lo, float hi,
-                                                 int32_t *__restrict__ amap, int32_t *__restrict__ act_n,
+                                                 uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
                                                  int32_t *__restrict__ nact) {
     const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
     int o = 0;
+    uint32_t bits = 0;
     // four entries per step: their index and position loads are all in flight together
     constexpr int U = 4;
     for (int j0 = 0; j0 < nl; j0 += U) {
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
         for (int u = 0; u < U; ++u) pv[u] = pos32[v[u]];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (j0 + u >= nl) break;
+            const int j = j0 + u;
+            if (j >= nl) break;
             const float dx = pv[u].x - pi.x, dy = pv[u].y - pi.y, dz = pv[u].z - pi.z;
             const float d2f = dx * dx + dy * dy + dz * dz;
             bool act = d2f < lo;
@@ -285,17 +288,32 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
                 act = d2_exact(__dsub_rn(pos[3 * w], xi), __dsub_rn(pos[3 * w + 1], yi),
                                __dsub_rn(pos[3 * w + 2], zi)) < rc2;
             }
-            const int64_t e = b + kSlab * (j0 + u);
             if (act) {
                 act_n[b + kSlab * o] = v[u];
-                amap[e] = (int32_t)(b + kSlab * o);
                 ++o;
-            } else {
-                amap[e] = -1;
+                bits |= 1u << (j & 31);
+            }
+            if ((j & 31) == 31 || j == nl - 1) {
+                amask[(int64_t)(j >> 5) * n + i] = bits;
+                bits = 0;
             }
         }
     }
     nact[i] = o;
+}
+
+// Active slot of Verlet slot e of receiver row i this step (-1: d >= rc): the row's slab base
+// plus 64 times the number of active entries before entry j = (e - base) / 64.
+__device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64_t *__restrict__ slab_off,
+                                               const uint32_t *__restrict__ amask, int64_t n) {
+    const int64_t b = sell_base(slab_off, i);
+    const int j = (int)((e - b) / kSlab);
+    const int w = j >> 5, bit = j & 31;
+    const uint32_t word = amask[(int64_t)w * n + i];
+    if (!((word >> bit) & 1u)) return -1;
+    int a = __popc(word & ((1u << bit) - 1u));
+    for (int q = 0; q < w; ++q) a += __popc(amask[(int64_t)q * n + i]);
+    return (int32_t)(b + (int64_t)kSlab * a);
 }
 
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
@@ -494,8 +512,10 @@ __device__ __forceinline__ T group_sum16(T x) {
 // slot of each transposed entry through the per-step map and records it in t_act, so the later
 // gathers read it sequentially.
 template <int K, bool BUILD>
-__global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__restrict__ t_off,
-                                                  const int32_t *__restrict__ t_eid, const int32_t *__restrict__ amap,
+__global__ __launch_bounds__(256) void k_gather_w(int64_t NN, int64_t n, const int64_t *__restrict__ t_off,
+                                                  const int32_t *__restrict__ t_eid, const int32_t *__restrict__ t_recv,
+                                                  const int64_t *__restrict__ slab_off,
+                                                  const uint32_t *__restrict__ amask,
                                                   int32_t *__restrict__ t_act, const float *__restrict__ w,
                                                   float *__restrict__ Gc) {
     const int64_t v = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
@@ -512,8 +532,9 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
             int32_t a0, a1 = -1;
             if (BUILD) {
                 const int32_t e0 = t_eid[s], e1 = two ? t_eid[s + kGatherLanes] : 0;
-                a0 = amap[e0];
-                if (two) a1 = amap[e1];
+                const int32_t r0 = t_recv[s], r1 = two ? t_recv[s + kGatherLanes] : 0;
+                a0 = active_slot(r0, e0, slab_off, amask, n);
+                if (two) a1 = active_slot(r1, e1, slab_off, amask, n);
                 t_act[s] = a0;
                 if (two) t_act[s + kGatherLanes] = a1;
             } else {
@@ -545,11 +566,13 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
 }
 
 // t_act alone (evaluations without message layers, where no gather builds it).
-__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, const int32_t *__restrict__ t_eid,
-                                                          const int32_t *__restrict__ amap,
+__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, const int32_t *__restrict__ t_eid,
+                                                          const int32_t *__restrict__ t_recv,
+                                                          const int64_t *__restrict__ slab_off,
+                                                          const uint32_t *__restrict__ amask,
                                                           int32_t *__restrict__ t_act) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < E) t_act[s] = amap[t_eid[s]];
+    if (s < E) t_act[s] = active_slot(t_recv[s], t_eid[s], slab_off, amask, n);
 }
 
 // Ghost -> owner sum of dE/dc (the reverse ghost exchange), ghosts of an owner in order.
@@ -654,7 +677,7 @@ Status compact_active(Context &cx) {
     const float lo = (float)(rc2 - band), hi = (float)(rc2 + band);
     k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(),
                                                         cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-                                                        cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amap.as<int32_t>(),
+                                                        cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(),
                                                         cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     return Status::ok();
@@ -742,8 +765,9 @@ Status assemble_go(Context &cx, int t, float *out) {
 
 Status transpose_active(Context &cx) {
     if (cx.E == 0) return Status::ok();
-    k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.stream>>>(cx.E, cx.t_eid.as<int32_t>(), cx.amap.as<int32_t>(),
-                                                                 cx.t_act.as<int32_t>());
+    k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.stream>>>(cx.E, cx.n, cx.t_eid.as<int32_t>(),
+                                                                 cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
+                                                                 cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
@@ -757,13 +781,13 @@ Status backward_messages(Context &cx, int t) {
         const bool build = (t == cx.T - 1);
 #define MPNN_GW(KK)                                                                                           \
     if (build)                                                                                                \
-        k_gather_w<KK, true><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
-                                                           cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),      \
-                                                           cx.w.as<float>(), Gct);                             \
+        k_gather_w<KK, true><<<gg, kBlock, 0, cx.stream>>>(                                                   \
+            cx.NN, cx.n, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(),               \
+            cx.slab_off.as<int64_t>(), cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>(), cx.w.as<float>(), Gct);  \
     else                                                                                                      \
-        k_gather_w<KK, false><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), \
-                                                            cx.amap.as<int32_t>(), cx.t_act.as<int32_t>(),     \
-                                                            cx.w.as<float>(), Gct)
+        k_gather_w<KK, false><<<gg, kBlock, 0, cx.stream>>>(                                                  \
+            cx.NN, cx.n, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(),               \
+            cx.slab_off.as<int64_t>(), cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>(), cx.w.as<float>(), Gct)
         switch (cx.K) {
             case 2: MPNN_GW(2); break;
             case 4: MPNN_GW(4); break;

@@ -76,6 +76,7 @@ struct Context {
     bool forces_valid = false;  // F_sorted matches the current positions
     int64_t n = 0, G = 0, NN = 0, E = 0, E_sell = 0;
     int64_t np = 0;             // n rounded up to whole 256-row blocks (column-tiled vectors)
+    int mw = 1;                 // activity-mask words per row (longest row / 32, rounded up)
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
     int nc[3] = {0, 0, 0};      // interior cells per axis
@@ -108,7 +109,7 @@ struct Context {
     Buf Gc;       // float [T][NN][K]  dE/dc^t (layers 1..T-1)
     Buf gedge;    // float [E][3]  dE/dr_e summed over layers
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
-    Buf amap;     // int32 [E]: active slot of each Verlet slot this step (-1: d >= rc)
+    Buf amask;    // uint32 [mw][n]: bit j%32 of word j/32 = entry j of the row is active (d < rc)
     Buf act_n;    // int32 [E]: sender node of each active slot
     Buf t_act;    // int32 [E]: active slot of each transposed entry this step (-1: d >= rc)
     Buf nact;     // int32 [n] active entries per row

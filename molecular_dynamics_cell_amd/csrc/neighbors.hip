@@ -10,6 +10,9 @@
 //   -> receiver rows (count / scan / fill over the 27-cell stencil, fp64 distance test)
 //   -> sender-major transpose (count / scan / fill / per-segment sort by edge id)
 //   -> per-species atom lists for the atomic networks.
+#include <algorithm>
+#include <vector>
+
 #include "impl.h"
 
 namespace mpnn {
@@ -535,6 +538,17 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.slab_off, sizeof(int64_t) * (size_t)(nslab + 2)));
     k_slab_width<<<grid_for(nslab), kBlock, 0, cx.stream>>>(n, nslab, cx.row_len.as<int32_t>(), cnt);
     MPNN_HIP(hipGetLastError());
+    {
+        // longest row -> words of the per-step activity mask
+        std::vector<int32_t> widths((size_t)nslab);
+        if (nslab > 0) {
+            MPNN_HIP(hipMemcpyAsync(widths.data(), cnt, sizeof(int32_t) * nslab, hipMemcpyDeviceToHost, cx.stream));
+            MPNN_HIP(hipStreamSynchronize(cx.stream));
+        }
+        int64_t longest = 0;
+        for (int32_t w : widths) longest = std::max<int64_t>(longest, w / kSlab);
+        cx.mw = (int)std::max<int64_t>(1, (longest + 31) / 32);
+    }
     MPNN_TRY(exclusive_scan(cx, cnt, nslab, cx.slab_off.as<int64_t>()));
     int64_t Es = 0;
     MPNN_TRY(fetch(cx, cx.slab_off.as<int64_t>() + nslab, &Es));
@@ -613,7 +627,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.grho, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
     MPNN_TRY(cx.grow(cx.pos32, sizeof(float4) * NN1));
-    MPNN_TRY(cx.grow(cx.amap, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.amask, sizeof(uint32_t) * (size_t)cx.mw * n1));
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
