@@ -419,7 +419,8 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
     auto run = [&]() -> Status {
         switch (which) {
             case 0:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.c.as<float>() + (int64_t)t * cx.NN * cx.K, cx.K, 0, out));
+                MPNN_TRY(mpnn::unpermute_rows(cx, cx.c.as<float>() + (int64_t)t * cx.NN * mpnn::rec_stride(cx.K) + mpnn::kRecC,
+                                              cx.K, mpnn::rec_stride(cx.K), out));
                 break;
             case 1:
                 MPNN_TRY(mpnn::unpermute_float(cx, cx.O.as<float>() + (int64_t)t * cx.np * mpnn::pad16(KM), KM, cx.np, out));

@@ -103,6 +103,12 @@ constexpr FeatIdx feat_idx(int K, int q) {
 // 64 contiguous bytes per atom.
 // ------------------------------------------------------------------------------------------
 constexpr int pad16(int w) { return (w + 15) / 16 * 16; }
+
+// Node records: per node and layer, the position (3 doubles in an 8-float header) followed by the
+// K message coefficients, padded to a multiple of 8 floats (64 bytes for K <= 8), so one
+// neighbour's position and messages share a cache line in the row kernels' gathers.
+constexpr int rec_stride(int K) { return 8 + (K + 7) / 8 * 8; }
+constexpr int kRecC = 8;   // float offset of c inside a record
 inline int64_t pad_rows(int64_t n) { return (n + kBlock - 1) / kBlock * kBlock; }
 __host__ __device__ __forceinline__ int64_t tiled(int64_t np, int64_t i, int q) {
     return ((int64_t)(q >> 4) * np + i) * 16 + (q & 15);

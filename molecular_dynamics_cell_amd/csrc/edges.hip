@@ -342,7 +342,9 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
             BasisHP<K, L> b;
-            b.eval(pos[3 * v] - xi, pos[3 * v + 1] - yi, pos[3 * v + 2] - zi, c + v * K, md);
+            const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+            const double *pv = reinterpret_cast<const double *>(rv);
+            b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
 #pragma unroll
             for (int k = 0; k < K; ++k)
 #pragma unroll
@@ -383,7 +385,9 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
             BasisHP<K, L, double> b;
-            b.eval(pos[3 * v] - xi, pos[3 * v + 1] - yi, pos[3 * v + 2] - zi, c + v * K, md);
+            const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+            const double *pv = reinterpret_cast<const double *>(rv);
+            b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
 #pragma unroll
             for (int k = 0; k < KB; ++k)
 #pragma unroll
@@ -451,9 +455,11 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
     for (int a = 0; a < na; ++a) {
         const int64_t e = b0 + kSlab * a;   // active slot: per-edge outputs are stored here
         const int64_t v = act_n[e];
+        const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+        const double *pv = reinterpret_cast<const double *>(rv);
         Basis<K, L, true> b;
-        b.eval(__dsub_rn(pos[3 * v], xi), __dsub_rn(pos[3 * v + 1], yi), __dsub_rn(pos[3 * v + 2], zi), md, mu);
-        const float *cv = c + v * K;
+        b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
+        const float *cv = rv + kRecC;
         float s = 0.0f, Q[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) Q[m] = 0.0f;
@@ -589,12 +595,13 @@ __global__ void k_fold_ghost_grad(int64_t n, int K, const int64_t *__restrict__ 
 
 // Owner -> ghost copy of the messages c^t (the forward ghost exchange).
 __global__ void k_ghost_feat(int64_t G, int64_t n, int K, const int32_t *__restrict__ owner,
-                             float *__restrict__ c) {
+                             float *__restrict__ rec) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= G * K) return;
     const int64_t g = q / K;
     const int k = (int)(q - g * K);
-    c[(n + g) * K + k] = c[(int64_t)owner[g] * K + k];
+    const int rs = rec_stride(K);
+    rec[(n + g) * rs + kRecC + k] = rec[(int64_t)owner[g] * rs + kRecC + k];
 }
 
 // F_i = sum_{edges received by i} dE/dr_e - sum_{active edges sent by i or by its ghost images}
@@ -686,7 +693,7 @@ Status compact_active(Context &cx) {
 Status aggregate(Context &cx, int t) {
     ProfScope ps_(cx, kProfAggregate);
     if (cx.n == 0) return Status::ok();
-    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
+    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     if (cx.precision == 0) {
@@ -725,7 +732,7 @@ Status aggregate(Context &cx, int t) {
 Status refresh_ghost_features(Context &cx, int t) {
     ProfScope ps_(cx, kProfGhostFeat);
     if (cx.G == 0) return Status::ok();
-    float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
+    float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
     k_ghost_feat<<<grid_for(cx.G * cx.K), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.K, cx.ghost_owner.as<int32_t>(), ct);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
@@ -734,7 +741,7 @@ Status refresh_ghost_features(Context &cx, int t) {
 Status backward_layer(Context &cx, int t) {
     ProfScope ps_(cx, kProfBackwardLayer);
     if (cx.n == 0) return Status::ok();
-    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * cx.K;
+    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
     const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
     const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     const bool first = (t == cx.T - 1), want_w = (t >= 1);

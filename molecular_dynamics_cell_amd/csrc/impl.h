@@ -102,7 +102,7 @@ struct Context {
     Buf sp_list, sp_off;            // int32 [n], int64 [S+1]
 
     // per-evaluation buffers
-    Buf c;        // float [T][NN][K]
+    Buf c;        // float [T][NN][rec_stride(K)]: node records (position, then c^t)
     Buf O;        // float [T] x column-tiled [np][pad16(K*M)]: orbital coefficients O^t
     Buf feat;     // float [T] x column-tiled [np][DP]: density features rho^t / s_t
     Buf grho;     // float [T] x column-tiled [np][DP]: dE/drho^t
@@ -191,5 +191,7 @@ Status unpermute_vec3(Context &cx, const double *sorted, double *caller);
 Status permute_in_vec3(Context &cx, const double *caller, double *sorted);
 // sorted rows of `width` floats (row-major, or column-tiled with row count np when np > 0)
 Status unpermute_float(Context &cx, const float *sorted, int width, int64_t np, double *caller);
+// sorted rows of `width` floats at a row stride of `stride` floats
+Status unpermute_rows(Context &cx, const float *sorted, int width, int stride, double *caller);
 
 }  // namespace mpnn

@@ -256,6 +256,23 @@ Status permute_in_vec3(Context &cx, const double *caller, double *sorted) {
     return Status::ok();
 }
 
+__global__ void k_unpermute_rows(int64_t n, int width, int stride, const int32_t *__restrict__ perm,
+                                 const float *__restrict__ in, double *__restrict__ out) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n * width) return;
+    const int64_t s = q / width;
+    const int w = (int)(q - s * width);
+    out[(int64_t)perm[s] * width + w] = (double)in[s * stride + w];
+}
+
+Status unpermute_rows(Context &cx, const float *sorted, int width, int stride, double *caller) {
+    if (cx.n == 0) return Status::ok();
+    k_unpermute_rows<<<grid_for(cx.n * width), kBlock, 0, cx.stream>>>(cx.n, width, stride, cx.perm.as<int32_t>(),
+                                                                      sorted, caller);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
 Status unpermute_float(Context &cx, const float *sorted, int width, int64_t np, double *caller) {
     if (cx.n == 0) return Status::ok();
     k_unpermute_float<<<grid_for(cx.n * width), kBlock, 0, cx.stream>>>(cx.n, width, np, cx.perm.as<int32_t>(),

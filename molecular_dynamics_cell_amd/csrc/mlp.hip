@@ -91,7 +91,7 @@ struct NetArgs {
     const int32_t *sp_list;
     int64_t sp_off[kMaxSpecies + 1];
     int32_t tile_start[kMaxSpecies + 1];
-    float *c_next;         // forward: c^{t+1} [*][K]
+    float *c_next;         // forward: c^{t+1} of node v at c_next[v * rec_stride(K) + k]
     float *Ei;             // energy: E_i [n]
     const float *Gc;       // backward: dE/dc^{t+1} [*][K]
     float *Grho;           // energy/backward: dE/drho^t, column-tiled [np][DP]
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(64, (H == 128 && MODE == kBackward) ? 1 : 2) void k
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int k = 4 * grp + i;
-                    if (k < K) a.c_next[me[c] * K + k] = (float)y[0][c][i];
+                    if (k < K) a.c_next[me[c] * rec_stride(K) + k] = (float)y[0][c][i];
                 }
             } else {
                 if (grp == 0) a.Ei[me[c]] = (float)((double)a.e_scale * y[0][c][0]);
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int k = grp + 4 * i;
-                    if (k < K) a.c_next[me * K + k] = (float)y[0][i];
+                    if (k < K) a.c_next[me * rec_stride(K) + k] = (float)y[0][i];
                 }
             } else {
                 if (grp == 0) a.Ei[me] = (float)((double)a.e_scale * y[0][0]);
@@ -536,7 +536,7 @@ Status pack_weights(Context &cx, const double *mlp) {
 Status mlp_forward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetForward);
     NetArgs a = make_args(cx, t);
-    a.c_next = cx.c.as<float>() + (int64_t)(t + 1) * cx.NN * cx.K;
+    a.c_next = cx.c.as<float>() + (int64_t)(t + 1) * cx.NN * rec_stride(cx.K) + kRecC;
     MPNN_DISPATCH_NET(kForward, a);
     return Status::ok();
 }

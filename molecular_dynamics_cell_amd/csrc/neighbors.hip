@@ -210,11 +210,18 @@ __global__ void k_ghost_pos(int64_t G, int64_t n, const int32_t *__restrict__ ow
     if (types) types[n + k] = types[o];
 }
 
-// fp32 copy of every node's position for the active-edge pre-test
-__global__ void k_pos32(int64_t NN, const double *__restrict__ pos, float4 *__restrict__ pos32) {
+// fp32 copy of every node's position for the active-edge pre-test, and the fp64 position into the
+// node record of every layer
+__global__ void k_pos32(int64_t NN, int T, int rs, const double *__restrict__ pos, float4 *__restrict__ pos32,
+                        float *__restrict__ rec) {
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (v >= NN) return;
-    pos32[v] = float4{(float)pos[3 * v], (float)pos[3 * v + 1], (float)pos[3 * v + 2], 0.0f};
+    const double x = pos[3 * v], y = pos[3 * v + 1], z = pos[3 * v + 2];
+    pos32[v] = float4{(float)x, (float)y, (float)z, 0.0f};
+    for (int t = 0; t < T; ++t) {
+        double *r = reinterpret_cast<double *>(rec + ((int64_t)t * NN + v) * rs);
+        r[0] = x; r[1] = y; r[2] = z;
+    }
 }
 
 __device__ __forceinline__ int ext_cell(double x, double h, int n) {
@@ -333,11 +340,12 @@ __global__ void k_species_scatter(int64_t n, const int32_t *__restrict__ types, 
 }
 
 __global__ void k_c0(int64_t NN, int K, const int32_t *__restrict__ types, const ModelDev *__restrict__ md,
-                     float *__restrict__ c) {
+                     float *__restrict__ rec) {
     int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (v >= NN) return;
     int s = types[v];
-    for (int k = 0; k < K; ++k) c[v * K + k] = md->c0[s * K + k];
+    const int rs = rec_stride(K);
+    for (int k = 0; k < K; ++k) rec[v * rs + kRecC + k] = md->c0[s * K + k];
 }
 
 __global__ void k_validate(int64_t n, const double *__restrict__ p, const int32_t *__restrict__ types, int S,
@@ -619,7 +627,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
 
     // ---- per-evaluation buffers and layer-0 messages ----
     const int KM = cx.K * cx.M;
-    MPNN_TRY(cx.grow(cx.c, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
+    MPNN_TRY(cx.grow(cx.c, sizeof(float) * (size_t)cx.T * NN1 * rec_stride(cx.K)));
     cx.np = pad_rows(cx.n);
     const size_t np1 = (size_t)(cx.np > 0 ? cx.np : kBlock);
     MPNN_TRY(cx.grow(cx.O, sizeof(float) * (size_t)cx.T * np1 * pad16(KM)));
@@ -655,7 +663,8 @@ Status refresh_ghost_positions(Context &cx) {
         MPNN_HIP(hipGetLastError());
     }
     if (cx.NN > 0) {
-        k_pos32<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.pos.as<double>(), cx.pos32.as<float4>());
+        k_pos32<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.T, rec_stride(cx.K), cx.pos.as<double>(),
+                                                            cx.pos32.as<float4>(), cx.c.as<float>());
         MPNN_HIP(hipGetLastError());
     }
     return Status::ok();
