@@ -37,9 +37,10 @@ __device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-
 template <int RT, int CT>
 __device__ __forceinline__ void gemm_step(const float4 *__restrict__ W, int KT, int kt, const float (&x)[CT][4],
                                           double (&acc)[RT][CT][4], int lane) {
-    // one scheduling region per chunk column: keeps the compiler from hoisting the weight loads of
-    // every column at once (hundreds of registers for the 128-wide networks)
-    __builtin_amdgcn_sched_barrier(0);
+    // 128-wide networks: one scheduling region per chunk column, which keeps the compiler from
+    // hoisting the weight loads of every column at once (hundreds of registers); the 64-wide
+    // ones may prefetch the next column's weights
+    if constexpr (RT >= 8) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const float4 w = W[(rt * KT + kt) * 64 + lane];
@@ -406,8 +407,8 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
     }
 }
 
-// atom tiles per wave: one (16 atoms); two would let each weight load feed two tiles, but the
-// fp64 chunk accumulators then exceed the register budget
+// atom tiles per wave: one (16 atoms).  Two tiles let each weight load feed two tiles but were
+// measured no faster (the reverse network loses occupancy to the larger accumulators).
 constexpr int tiles_per_wave(int) { return 1; }
 
 NetArgs make_args(Context &cx, int t) {
@@ -420,7 +421,7 @@ NetArgs make_args(Context &cx, int t) {
     a.ob1 = cx.net.b1; a.ob2 = cx.net.b2; a.ob3 = cx.net.b3;
     a.S = cx.S;
     a.sp_list = cx.sp_list.as<int32_t>();
-    const int per = 16 * tiles_per_wave(cx.H);
+    const int per = 16 * (cx.precision ? 1 : tiles_per_wave(cx.H));   // the fp64 kernel takes one tile
     int64_t off = 0;
     int32_t tiles = 0;
     for (int s = 0; s <= cx.S; ++s) {
