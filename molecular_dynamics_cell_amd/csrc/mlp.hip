@@ -27,7 +27,14 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+// logistic function from the hardware exp2 of a two-part product z log2(e) (so the argument carries
+// no rounding bias) and the hardware reciprocal with one Newton step
+__device__ __forceinline__ float sigmoid(float z) {
+    const float y = fmaf(z, -1.44269502f, z * -1.92596299e-8f);
+    const float d = 1.0f + __builtin_amdgcn_exp2f(y);
+    const float r = __builtin_amdgcn_rcpf(d);
+    return fmaf(fmaf(-d, r, 1.0f), r, r);
+}
 
 // acc[rt][c] += W[rt][kt] x[c] for every row tile rt of a matrix packed with KT column tiles:
 // one float4 of weights per lane feeds 4 k-steps of each of the CT atom tiles.  The matrix cores
