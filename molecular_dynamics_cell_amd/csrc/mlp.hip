@@ -28,9 +28,11 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 }
 
 // logistic function from the hardware exp2 of a two-part product z log2(e) (so the argument carries
-// no rounding bias) and the hardware reciprocal with one Newton step
+// no rounding bias) and the hardware reciprocal with one Newton step.  The exponent is capped at
+// 126 so 1 + 2^y stays finite (the Newton step would turn an infinite one into NaN); below
+// z = -87 the result is then 2^-126 instead of e^z, both zero for every use here.
 __device__ __forceinline__ float sigmoid(float z) {
-    const float y = fmaf(z, -1.44269502f, z * -1.92596299e-8f);
+    const float y = fminf(fmaf(z, -1.44269502f, z * -1.92596299e-8f), 126.0f);
     const float d = 1.0f + __builtin_amdgcn_exp2f(y);
     const float r = __builtin_amdgcn_rcpf(d);
     return fmaf(fmaf(-d, r, 1.0f), r, r);

@@ -107,3 +107,21 @@ def test_state_round_trip_and_new_positions():
     s3 = I.System(s.name, far.cpu().numpy(), s.types, s.box, s.vel, s.species, s.masses)
     Eo, Fo, _ = oracle_ef(p, s3)
     check_ef(E2, F2.cpu().numpy(), Eo, Fo, label="one atom moved 0.9 A")
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_saturated_activations(precision):
+    """First-layer weights scaled so hidden pre-activations reach several hundred: SiLU saturates at
+    both ends (e^-z overflows fp32 for z < -88); energies and forces must stay finite and match."""
+    s = I.make_system(1)
+    p = I.make_params(1)
+    p.spec.precision = precision
+    for w in p.mlp[0]:
+        w["W1"] = w["W1"] * 256.0
+        w["b1"] = w["b1"] * 256.0
+    m = gpu_model(p, s)
+    E, F, _ = m.energy_forces()
+    F = F.cpu().numpy()
+    assert np.isfinite(E) and np.isfinite(F).all()
+    Eo, Fo, _ = oracle_ef(p, s)
+    check_ef(E, F, Eo, Fo, label=f"saturated SiLU (precision {precision})")
