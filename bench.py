@@ -162,6 +162,60 @@ def cpu_baseline(cfg, budget_s=12.0):
             "sample": f"{sample}; {steps} velocity-Verlet steps (E+F each step) in {el:.1f} s"}
 
 
+def t_sweep(max_t=6, evals=10):
+    """Cost of one E+F evaluation against the number of message-passing layers T (the pages' claim
+    of a cost linear in T), on the 2.05M-atom Ag subdomain with random-init models of each depth,
+    and the per-layer ghost-refresh volume against subdomain size (surface, not volume, scaling)."""
+    import torch
+    from dataclasses import replace
+    from molecular_dynamics_cell_amd import binding, inputs as I
+    dev = torch.device("cuda:0")
+    s = I.make_system(4)
+    base = I.make_params(4)
+    scales = list(base.layer_scale)
+    rows = []
+    for T in range(1, max_t + 1):
+        spec = replace(base.spec, T=T)
+        ls = [scales[min(t, len(scales) - 1)] for t in range(T)]
+        p = I.random_params(spec, 1204, base.masses, ls, base.e_scale)
+        m = binding.MPNN(p, dev)
+        m.build_neighbors(torch.tensor(s.pos, device=dev), torch.tensor(s.types, device=dev), s.box)
+        m.energy_forces(energy=False)
+        ts = []
+        for _ in range(evals):
+            torch.cuda.synchronize()
+            a0 = time.perf_counter()
+            m.energy_forces(energy=False)
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - a0)
+        ms = float(np.median(ts)) * 1e3
+        rows.append({"T": T, "ef_ms": round(ms, 3), "atom_steps_per_s": round(s.n / ms * 1e3, 1)})
+        print(f"T={T}: {ms:.3f} ms per E+F", file=sys.stderr, flush=True)
+        m.close()
+        torch.cuda.empty_cache()
+    # linear fit ms = a + b T
+    Ts = np.array([r["T"] for r in rows], float)
+    ys = np.array([r["ef_ms"] for r in rows])
+    b, a = np.polyfit(Ts, ys, 1)
+    resid = float(np.max(np.abs(ys - (a + b * Ts)) / ys))
+    halo = []
+    p = I.make_params(4)
+    for cells in (20, 40, 80):
+        g = I.ag(cells, 1004, 1104, name=f"Ag{cells}")
+        m = binding.MPNN(p, dev)
+        m.build_neighbors(torch.tensor(g.pos, device=dev), torch.tensor(g.types, device=dev), g.box)
+        info = m.info()
+        halo.append({"fcc_cells": cells, "atoms": g.n, "ghosts": info["n_ghost"],
+                     "ghost_fraction": round(info["n_ghost"] / g.n, 4),
+                     "refresh_bytes_per_layer": info["n_ghost"] * p.spec.K * 4})
+        m.close()
+        torch.cuda.empty_cache()
+    return {"sweep": "E+F cost vs layers T, Ag 2,048,000 atoms (random-init models, K=8, L=2, H=64)",
+            "rows": rows, "fit_ms": {"fixed": round(float(a), 3), "per_layer": round(float(b), 3),
+                                     "max_rel_residual": round(resid, 4)},
+            "halo": halo}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,12 +230,18 @@ def main():
                     help="arithmetic mode (0 fp32 orbital sums/networks, 1 fp64); default: the workload's")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--t-sweep", action="store_true",
+                    help="instead of the benchmark line: E+F cost vs layers T and ghost volume vs size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the multi-GPU halo exchange is designed, "
               "not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.t_sweep:
+        print(json.dumps(t_sweep()))
+        return
 
     import torch
     from molecular_dynamics_cell_amd import binding, inputs as I
