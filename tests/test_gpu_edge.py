@@ -125,3 +125,19 @@ def test_saturated_activations(precision):
     assert np.isfinite(E) and np.isfinite(F).all()
     Eo, Fo, _ = oracle_ef(p, s)
     check_ef(E, F, Eo, Fo, label=f"saturated SiLU (precision {precision})")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_layer_counts(T):
+    """T = 1 (no message layers: the embedded-atom case, where the transposed active map is built
+    without a message gather) and T = 4 against the oracle."""
+    from dataclasses import replace
+    s = I.make_system(1)
+    base = I.make_params(1)
+    spec = replace(base.spec, T=T)
+    ls = [base.layer_scale[min(t, len(base.layer_scale) - 1)] for t in range(T)]
+    p = I.random_params(spec, 1301, base.masses, ls, base.e_scale)
+    m = gpu_model(p, s)
+    E, F, _ = m.energy_forces()
+    Eo, Fo, _ = oracle_ef(p, s)
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"Ag108, T={T}")
