@@ -230,6 +230,8 @@ def main():
                     help="arithmetic mode (0 fp32 orbital sums/networks, 1 fp64); default: the workload's")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--graph-replay", type=int, default=None,
+                    help="MD steps per captured replay (0: eager; default: 8 below 1,000 atoms, else 0)")
     ap.add_argument("--t-sweep", action="store_true",
                     help="instead of the benchmark line: E+F cost vs layers T and ghost volume vs size")
     args = ap.parse_args()
@@ -282,16 +284,28 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    # replayed chunks pay off where launch latency dominates (the 108-atom cell); the 4,608-atom
+    # water run is short and rebuilds inside it, so a rolled-back chunk and re-recording cost more
+    replay = args.graph_replay if args.graph_replay is not None else (8 if s.n < 1_000 else 0)
+    m.set_graph_replay(replay)
     E0, _, _ = m.energy_forces()
-    m.md_step(c["dt"], args.warmup, c["rebuild_every"], stats=False)
+    # warm-up covers at least one full replayed chunk, so its recording is not timed
+    m.md_step(c["dt"], max(args.warmup, replay), c["rebuild_every"], stats=False)
     torch.cuda.synchronize()
-    if not args.no_profile:
+    # the event profiler times each kernel family inside the timed steps; replayed chunks cannot
+    # carry it, so with replay the per-kernel times come from extra profiled steps afterwards
+    profile_inline = not args.no_profile and replay == 0
+    if profile_inline:
         m.set_profiling(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     st = m.md_step(c["dt"], args.steps, c["rebuild_every"], stats=False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if not args.no_profile and not profile_inline:
+        m.set_profiling(True)
+        m.md_step(c["dt"], max(1, min(args.steps, 20)), c["rebuild_every"], stats=False)
+        torch.cuda.synchronize()
     prof = m.profile() if not args.no_profile else {}
     m.set_profiling(False)
     st = m.md_step(c["dt"], 0, c["rebuild_every"])      # energies at the end of the run
@@ -338,7 +352,7 @@ def main():
                                f"K={p.spec.K}, L={p.spec.L}, MLP 2x{p.spec.H}, rc={p.spec.rc}, "
                                f"skin={p.spec.skin}, dt={c['dt']} fs, rebuild every {c['rebuild_every']}",
                    "atoms": s.n, "ghosts": info["n_ghost"], "verlet_entries": info["n_edges"],
-                   "active_edges": EA, "parallelism": "single GPU"},
+                   "active_edges": EA, "parallelism": "single GPU", "graph_replay_steps": replay},
         "roofline": roof,
         "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,
         "md": {"epot_start": E0, "epot_end": st["epot"], "ekin_end": st["ekin"],

@@ -166,6 +166,16 @@ mpnn_status mpnn_set_profiling(mpnn_ctx *ctx, int32_t enable);
 mpnn_status mpnn_get_profile(mpnn_ctx *ctx, int32_t idx, const char **name, double *total_ms,
                              int64_t *launches);
 
+/* Replay of mpnn_md_step in captured chunks: steps_per_replay > 0 records up to that many
+ * velocity-Verlet steps (kick-drift, evaluation, kick) as one HIP graph and replays it, with one
+ * host synchronisation per chunk instead of one per step and no per-kernel launch cost; 0 (the
+ * default) runs every step eagerly.  Results are bitwise identical to the eager path.  A chunk
+ * ends before every step whose list is rebuilt on schedule; when an atom moves more than skin/2
+ * inside a chunk, the chunk is rolled back (positions, velocities, forces) and redone step by
+ * step, rebuilding where needed.  The graph is recorded again after every rebuild and whenever
+ * dt or the chunk length changes; chunks are not used while the event profiler is on. */
+mpnn_status mpnn_set_graph_replay(mpnn_ctx *ctx, int32_t steps_per_replay);
+
 /* Text of the last error on this context ("" if none); valid until the next call. */
 const char *mpnn_last_error(const mpnn_ctx *ctx);
 

@@ -72,6 +72,7 @@ def lib():
             "mpnn_get_pairs": ([p, i64, C.POINTER(C.c_int64), p, p, p], st),
             "mpnn_get_intermediate": ([p, i32, i32, p], st),
             "mpnn_get_info": ([p, C.POINTER(Info)], st),
+            "mpnn_set_graph_replay": ([p, i32], st),
             "mpnn_set_profiling": ([p, i32], st),
             "mpnn_get_profile": ([p, i32, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                   C.POINTER(C.c_int64)], st),
@@ -191,6 +192,10 @@ class MPNN:
         out = torch.empty((self.n, width), dtype=torch.float64, device=self.device)
         self._check(lib().mpnn_get_intermediate(self.h, int(which), int(t), _dptr(out)))
         return out
+
+    def set_graph_replay(self, steps_per_replay: int):
+        """Replay MD in captured chunks of up to this many steps (0: eager)."""
+        self._check(lib().mpnn_set_graph_replay(self.h, int(steps_per_replay)))
 
     def set_profiling(self, enable: bool):
         self._check(lib().mpnn_set_profiling(self.h, 1 if enable else 0))

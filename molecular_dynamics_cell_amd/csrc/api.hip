@@ -5,6 +5,8 @@
 #include <new>
 #include <vector>
 
+#include <algorithm>
+
 #include "impl.h"
 
 struct mpnn_ctx {
@@ -104,7 +106,12 @@ Context::~Context() {
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
-                  &types_caller, &stage_pos, &stage_vel};
+                  &types_caller, &stage_pos, &stage_vel, &bak_pos, &bak_vel, &bak_F};
+    for (const Chunk &c : graphs) (void)hipGraphExecDestroy(c.exec);
+    if (cap_stream) (void)hipStreamSynchronize(cap_stream);
+    for (hipEvent_t e : cap_ev)
+        if (e) (void)hipEventDestroy(e);
+    if (cap_stream) (void)hipStreamDestroy(cap_stream);
     for (Buf *b : all) release(*b);
     prof_harvest();
     for (hipEvent_t e : prof_pool) (void)hipEventDestroy(e);
@@ -302,6 +309,107 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
     return mpnn::finish(ctx, s);
 }
 
+namespace mpnn {
+
+Status drop_graphs(Context &cx) {
+    for (const Context::Chunk &c : cx.graphs) MPNN_HIP(hipGraphExecDestroy(c.exec));
+    cx.graphs.clear();
+    cx.graph_valid = true;
+    return Status::ok();
+}
+
+// Record k steps (state backup, then kick-drift / evaluation / kick per step) as one graph.
+Status capture_chunk(Context &cx, double dt, int k, hipGraphExec_t *out) {
+    const size_t bytes = sizeof(double) * 3 * (size_t)(cx.n > 0 ? cx.n : 1);
+    MPNN_TRY(cx.grow(cx.bak_pos, bytes));       // every allocation happens before the capture
+    MPNN_TRY(cx.grow(cx.bak_vel, bytes));
+    MPNN_TRY(cx.grow(cx.bak_F, bytes));
+    if (!cx.cap_stream) MPNN_HIP(hipStreamCreateWithFlags(&cx.cap_stream, hipStreamNonBlocking));
+    for (hipEvent_t &e : cx.cap_ev)
+        if (!e) MPNN_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    MPNN_HIP(hipStreamSynchronize(cx.stream));
+    // the launchers use cx.stream: point it at the capture stream while recording
+    const hipStream_t user = cx.stream;
+    cx.stream = cx.cap_stream;
+    const hipError_t eb = hipStreamBeginCapture(cx.stream, hipStreamCaptureModeThreadLocal);
+    if (eb != hipSuccess) {
+        cx.stream = user;
+        MPNN_HIP(eb);
+    }
+    auto body = [&]() -> Status {
+        const size_t b = sizeof(double) * 3 * (size_t)cx.n;
+        if (cx.n > 0) {
+            MPNN_HIP(hipMemcpyAsync(cx.bak_pos.p, cx.pos.p, b, hipMemcpyDeviceToDevice, cx.stream));
+            MPNN_HIP(hipMemcpyAsync(cx.bak_vel.p, cx.vel.p, b, hipMemcpyDeviceToDevice, cx.stream));
+            MPNN_HIP(hipMemcpyAsync(cx.bak_F.p, cx.F.p, b, hipMemcpyDeviceToDevice, cx.stream));
+        }
+        for (int j = 0; j < k; ++j) {
+            MPNN_TRY(kick_drift(cx, dt));
+            MPNN_TRY(evaluate(cx, nullptr));
+            MPNN_TRY(kick(cx, dt));
+        }
+        return Status::ok();
+    };
+    const Status st = body();
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(cx.stream, &g);
+    cx.stream = user;
+    if (st.bad()) {
+        if (g) (void)hipGraphDestroy(g);
+        return st;
+    }
+    MPNN_HIP(e);
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    MPNN_HIP(ei);
+    cx.graphs.push_back({k, dt, exec});
+    *out = exec;
+    return Status::ok();
+}
+
+// Run k steps as one replay.  *done = false: an atom crossed skin/2 inside the chunk; the state
+// is restored to the chunk's start (the displacement flag recomputed for it) for an eager redo.
+Status replay_chunk(Context &cx, double dt, int k, bool *done, double *max_disp) {
+    if (!cx.graph_valid) MPNN_TRY(drop_graphs(cx));
+    hipGraphExec_t exec = nullptr;
+    for (const Context::Chunk &c : cx.graphs)
+        if (c.k == k && c.dt == dt) exec = c.exec;
+    if (!exec) MPNN_TRY(capture_chunk(cx, dt, k, &exec));
+    // replay on the capture stream, ordered after and before the work of the context's stream
+    MPNN_HIP(hipEventRecord(cx.cap_ev[0], cx.stream));
+    MPNN_HIP(hipStreamWaitEvent(cx.cap_stream, cx.cap_ev[0], 0));
+    MPNN_HIP(hipGraphLaunch(exec, cx.cap_stream));
+    MPNN_HIP(hipEventRecord(cx.cap_ev[1], cx.cap_stream));
+    MPNN_HIP(hipStreamWaitEvent(cx.stream, cx.cap_ev[1], 0));
+    bool ex = false;
+    MPNN_TRY(read_skin_flag(cx, &ex, max_disp));
+    if (!ex) {
+        *done = true;
+        return Status::ok();
+    }
+    const size_t b = sizeof(double) * 3 * (size_t)cx.n;
+    if (cx.n > 0) {
+        MPNN_HIP(hipMemcpyAsync(cx.pos.p, cx.bak_pos.p, b, hipMemcpyDeviceToDevice, cx.stream));
+        MPNN_HIP(hipMemcpyAsync(cx.vel.p, cx.bak_vel.p, b, hipMemcpyDeviceToDevice, cx.stream));
+        MPNN_HIP(hipMemcpyAsync(cx.F.p, cx.bak_F.p, b, hipMemcpyDeviceToDevice, cx.stream));
+    }
+    MPNN_TRY(reset_skin_flag(cx));
+    MPNN_TRY(skin_check(cx));
+    *done = false;
+    return Status::ok();
+}
+
+}  // namespace mpnn
+
+mpnn_status mpnn_set_graph_replay(mpnn_ctx *ctx, int32_t steps_per_replay) {
+    if (!ctx || steps_per_replay < 0) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    cx.graph_steps = steps_per_replay;
+    cx.graph_valid = false;
+    return mpnn::finish(ctx, Status::ok());
+}
+
 mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t rebuild_every,
                          mpnn_md_stats *stats) {
     if (!ctx) return MPNN_E_INVALID_ARG;
@@ -314,7 +422,29 @@ mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t r
         double max_disp = 0.0;
         if (!cx.forces_valid) MPNN_TRY(mpnn::evaluate(cx, nullptr));
         MPNN_TRY(mpnn::reset_skin_flag(cx));
+        int eager_left = 0;   // after a rolled-back chunk, its steps run eagerly
         for (int32_t s = 0; s < n_steps; ++s) {
+            // a replayed chunk of k steps, ending before the next scheduled rebuild
+            int k = 0;
+            if (eager_left > 0) {
+                --eager_left;
+            } else if (cx.graph_steps > 0 && !cx.prof_on && cx.n > 0) {
+                k = std::min<int32_t>(cx.graph_steps, n_steps - s);
+                if (rebuild_every > 0) k = std::min(k, rebuild_every - 1 - cx.since_build);
+            }
+            if (k > 0) {
+                bool done = false;
+                double md = 0.0;
+                MPNN_TRY(mpnn::replay_chunk(cx, dt_fs, k, &done, &md));
+                if (done) {
+                    max_disp = md > max_disp ? md : max_disp;
+                    cx.since_build += k;
+                    cx.step += k;
+                    s += k - 1;
+                    continue;
+                }
+                eager_left = k - 1;
+            }
             MPNN_TRY(mpnn::kick_drift(cx, dt_fs));
             ++cx.since_build;
             bool need = rebuild_every > 0 && cx.since_build >= rebuild_every;

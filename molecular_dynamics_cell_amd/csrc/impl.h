@@ -125,6 +125,20 @@ struct Context {
 
     // ---- event profiler ----
     bool prof_on = false;
+
+    // ---- graph replay of MD chunks ----
+    int graph_steps = 0;                 // requested chunk length (0: eager)
+    struct Chunk {
+        int k;
+        double dt;
+        hipGraphExec_t exec;
+    };
+    std::vector<Chunk> graphs;           // recorded chunks by (length, dt)
+    bool graph_valid = false;            // false after a rebuild: every recorded chunk is stale
+    Buf bak_pos, bak_vel, bak_F;         // state at the start of a replayed chunk
+    hipStream_t cap_stream = nullptr;    // own (non-default, default-priority) stream: graphs are
+                                         // captured and replayed there, ordered by events
+    hipEvent_t cap_ev[2] = {nullptr, nullptr};
     double prof_ms[kProfCount] = {};
     int64_t prof_launches[kProfCount] = {};
     std::vector<hipEvent_t> prof_pool;

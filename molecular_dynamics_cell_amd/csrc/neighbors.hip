@@ -430,6 +430,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
                        const double box[3], double skin, const double *vel_caller) {
     cx.built = false;
     cx.forces_valid = false;
+    cx.graph_valid = false;   // buffers and launch shapes may change
     const double w = cx.rc + skin;
     for (int a = 0; a < 3; ++a) {
         if (!(box[a] > w)) return Status::err(MPNN_E_BOX, "box edge must exceed rc + skin");
