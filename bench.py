@@ -27,6 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_VALU_TFLOPS = 157.3       # MI355X published fp32 vector peak
 FP32_MFMA_TFLOPS = 157.3       # MI355X published dense fp32 matrix peak
+MFMA_PEAK_TFLOPS = {0: FP32_MFMA_TFLOPS, 1: 78.6, 2: 2500.0}   # by arithmetic mode: fp32, fp64, bf16
+DTYPE = {0: "f32", 1: "f64", 2: "f32 (bf16 MLP operands)"}
 METRIC = "atom-steps/s (E+F, T=3) on 2.05M-atom Ag subdomain, 1 MI355X; % HBM roof"
 
 
@@ -98,10 +100,11 @@ def csrc_digest():
     return h.hexdigest()
 
 
-def measured_traffic(fam, cfg):
+def measured_traffic(fam, cfg, precision=0):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE readings (scaled
-    by the copy-kernel calibration), or None if absent or taken on different kernel sources."""
-    if cfg != 4 or not os.path.exists(TRAFFIC_FILE):
+    by the copy-kernel calibration; taken on the 2.05M-atom Ag workload in fp32 mode), or None if
+    absent, taken on different kernel sources or for another workload or mode."""
+    if cfg != 4 or precision != 0 or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
@@ -111,19 +114,20 @@ def measured_traffic(fam, cfg):
     return int((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024)
 
 
-def roofline_for(fam, ms_avg, g, cfg=4):
+def roofline_for(fam, ms_avg, g, cfg=4, precision=0):
     bytes_, flops, kind = kernel_model(fam, g)
-    traffic = measured_traffic(fam, cfg)
+    traffic = measured_traffic(fam, cfg, precision)
     t = ms_avg * 1e-3
     gbs = bytes_ / t / 1e9
     tfs = flops / t / 1e12
     t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
-    t_cmp = flops / ((FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS) * 1e12)
+    mfma_peak = MFMA_PEAK_TFLOPS[precision]
+    t_cmp = flops / ((mfma_peak if kind == "mfma" else FP32_VALU_TFLOPS) * 1e12)
     if kind == "hbm" or t_hbm >= t_cmp:
         return {"kernel": fam, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": int(bytes_), "avg_ms": round(ms_avg, 4)}
-    peak = FP32_MFMA_TFLOPS if kind == "mfma" else FP32_VALU_TFLOPS
+    peak = mfma_peak if kind == "mfma" else FP32_VALU_TFLOPS
     return {"kernel": fam, "bound": "mfma" if kind == "mfma" else "alu", "achieved": round(tfs, 2),
             "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": traffic,
             "algorithmic_flops": int(flops), "algorithmic_bytes": int(bytes_),
@@ -226,12 +230,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--ef-evals", type=int, default=10)
-    ap.add_argument("--precision", type=int, choices=(0, 1), default=None,
-                    help="arithmetic mode (0 fp32 orbital sums/networks, 1 fp64); default: the workload's")
+    ap.add_argument("--precision", type=int, choices=(0, 1, 2), default=None,
+                    help="arithmetic mode (0 fp32 orbital sums/networks, 1 fp64, 2 fp32 sums with bf16 "
+                         "network operands); default: the workload's")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also launch one device copy of this many MiB (counter calibration)")
     ap.add_argument("--graph-replay", type=int, default=None,
                     help="MD steps per captured replay (0: eager; default: 8 below 1,000 atoms, else 0)")
+    ap.add_argument("--subdomains", type=str, default="1,1,1",
+                    help="px,py,pz virtual subdomains (per-layer ghost refresh between them)")
     ap.add_argument("--t-sweep", action="store_true",
                     help="instead of the benchmark line: E+F cost vs layers T and ghost volume vs size")
     args = ap.parse_args()
@@ -264,6 +271,8 @@ def main():
     if args.precision is not None:
         p.spec.precision = args.precision
     m = binding.MPNN(p, dev)
+    sub = tuple(int(x) for x in args.subdomains.split(","))
+    m.set_subdomains(*sub)
     pos = torch.tensor(s.pos, device=dev)
     m.build_neighbors(pos, torch.tensor(s.types, device=dev), s.box)
     m.set_state(vel=torch.tensor(s.vel, device=dev))
@@ -331,9 +340,9 @@ def main():
     modeled = [k for k in kernels if kernel_model(k, g) is not None]
     if modeled:
         dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
-        roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg)
+        roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg, p.spec.precision)
     for k in modeled:
-        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg)
+        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg, p.spec.precision)
 
     out = {
         "metric": METRIC,
@@ -346,13 +355,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64" if p.spec.precision else "f32",
+        "dtype": DTYPE[p.spec.precision],
         "data": "synthetic",
         "config": {"workload": f"{s.name}: {s.n} atoms + {info['n_ghost']} ghosts, T={p.spec.T}, "
                                f"K={p.spec.K}, L={p.spec.L}, MLP 2x{p.spec.H}, rc={p.spec.rc}, "
                                f"skin={p.spec.skin}, dt={c['dt']} fs, rebuild every {c['rebuild_every']}",
                    "atoms": s.n, "ghosts": info["n_ghost"], "verlet_entries": info["n_edges"],
-                   "active_edges": EA, "parallelism": "single GPU", "graph_replay_steps": replay},
+                   "active_edges": EA, "parallelism": "single GPU" if sub == (1, 1, 1) else
+                   "single GPU, {}x{}x{} virtual subdomains".format(*sub), "graph_replay_steps": replay},
         "roofline": roof,
         "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,
         "md": {"epot_start": E0, "epot_end": st["epot"], "ekin_end": st["ekin"],

@@ -70,7 +70,12 @@ typedef struct {
     int32_t hidden;             /* width H of both hidden layers */
     int32_t precision;          /* 0: fp32 orbital sums and fp32 networks (fp64 accumulation of
                                    16-product chunks); 1: fp64 orbital sums and fp64 networks,
-                                   for force distributions with heavy tails (slower) */
+                                   for force distributions with heavy tails (slower); 2: fp32
+                                   orbital sums, networks on the bf16 matrix cores with fp32
+                                   accumulation, every operand (features, weights, hidden
+                                   activations) carried as a pair of bf16 values; only for
+                                   hidden = 64 and D <= 128 (MPNN_E_INVALID_ARG otherwise); forces
+                                   within 2e-3 of the RMS force of the fp64 model */
     double rc;                  /* cutoff radius, A */
     double sigma;               /* Gaussian standard deviation, A */
     const double *mu;           /* [K] radial centres, A */
@@ -175,6 +180,19 @@ mpnn_status mpnn_get_profile(mpnn_ctx *ctx, int32_t idx, const char **name, doub
  * step, rebuilding where needed.  The graph is recorded again after every rebuild and whenever
  * dt or the chunk length changes; chunks are not used while the event profiler is on. */
 mpnn_status mpnn_set_graph_replay(mpnn_ctx *ctx, int32_t steps_per_replay);
+
+/* Virtual spatial decomposition (paper, "Parallelization Algorithm", Fig. 3b and Fig. 4): from the
+ * next mpnn_build_neighbors on, the box is split into px x py x pz equal subdomains (1 x 1 x 1, the
+ * default, is the undecomposed box).  Each subdomain holds the atoms inside it plus its own ghost
+ * shell: every image (another subdomain's atom, or a periodic image) within rc + skin of the
+ * subdomain; its atoms' neighbour rows reference only its own atoms and ghosts, and after every
+ * layer each ghost's messages are refreshed from its owner, the one-device stand-in for the
+ * exchange between processes.  Energies and forces equal the undecomposed ones up to the order of
+ * fp summation; only the ghost count (memory, refresh volume) grows.  Each of px, py, pz must be
+ * in 1..16 (MPNN_E_INVALID_ARG otherwise); the build fails with MPNN_E_BOX when box / p is not
+ * larger than rc + skin along an axis.  Invalidates the current list (MPNN_E_STATE until the
+ * next build). */
+mpnn_status mpnn_set_subdomains(mpnn_ctx *ctx, int32_t px, int32_t py, int32_t pz);
 
 /* Text of the last error on this context ("" if none); valid until the next call. */
 const char *mpnn_last_error(const mpnn_ctx *ctx);

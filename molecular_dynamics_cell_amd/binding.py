@@ -73,6 +73,7 @@ def lib():
             "mpnn_get_intermediate": ([p, i32, i32, p], st),
             "mpnn_get_info": ([p, C.POINTER(Info)], st),
             "mpnn_set_graph_replay": ([p, i32], st),
+            "mpnn_set_subdomains": ([p, i32, i32, i32], st),
             "mpnn_set_profiling": ([p, i32], st),
             "mpnn_get_profile": ([p, i32, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                   C.POINTER(C.c_int64)], st),
@@ -196,6 +197,10 @@ class MPNN:
     def set_graph_replay(self, steps_per_replay: int):
         """Replay MD in captured chunks of up to this many steps (0: eager)."""
         self._check(lib().mpnn_set_graph_replay(self.h, int(steps_per_replay)))
+
+    def set_subdomains(self, px: int, py: int, pz: int):
+        """Split the box into px x py x pz virtual subdomains from the next build on."""
+        self._check(lib().mpnn_set_subdomains(self.h, int(px), int(py), int(pz)))
 
     def set_profiling(self, enable: bool):
         self._check(lib().mpnn_set_profiling(self.h, 1 if enable else 0))

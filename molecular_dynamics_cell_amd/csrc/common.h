@@ -44,18 +44,42 @@ template <int L>
 struct Mono {
     static constexpr int M = n_mono(L);
     int lx[M], ly[M], lz[M], l[M];
+    int mx[M], my[M], mz[M];   // index of the monomial with one power of x (y, z) fewer, or -1
     float w[M];
-    constexpr Mono() : lx(), ly(), lz(), l(), w() {
+    // position of x^a y^b z^c in the order below: degree, then a descending, then b descending
+    static constexpr int index(int a, int b, int c) {
+        const int ll = a + b + c;
+        return ll * (ll + 1) * (ll + 2) / 6 + (ll - a) * (ll - a + 1) / 2 + (ll - a - b);
+    }
+    constexpr Mono() : lx(), ly(), lz(), l(), mx(), my(), mz(), w() {
         int m = 0;
         for (int ll = 0; ll <= L; ++ll)
             for (int x = ll; x >= 0; --x)
                 for (int y = ll - x; y >= 0; --y) {
-                    lx[m] = x; ly[m] = y; lz[m] = ll - x - y; l[m] = ll;
-                    w[m] = (float)(fact(ll) / (fact(x) * fact(y) * fact(ll - x - y)));
+                    const int z = ll - x - y;
+                    lx[m] = x; ly[m] = y; lz[m] = z; l[m] = ll;
+                    mx[m] = x ? index(x - 1, y, z) : -1;
+                    my[m] = y ? index(x, y - 1, z) : -1;
+                    mz[m] = z ? index(x, y, z - 1) : -1;
+                    w[m] = (float)(fact(ll) / (fact(x) * fact(y) * fact(z)));
                     ++m;
                 }
     }
 };
+
+template <int L>
+constexpr bool mono_index_consistent() {
+    constexpr Mono<L> mo;
+    for (int m = 0; m < Mono<L>::M; ++m) {
+        if (Mono<L>::index(mo.lx[m], mo.ly[m], mo.lz[m]) != m) return false;
+        if (mo.lx[m] && mo.lx[mo.mx[m]] != mo.lx[m] - 1) return false;
+        if (mo.ly[m] && mo.ly[mo.my[m]] != mo.ly[m] - 1) return false;
+        if (mo.lz[m] && mo.lz[mo.mz[m]] != mo.lz[m] - 1) return false;
+    }
+    return true;
+}
+static_assert(mono_index_consistent<1>() && mono_index_consistent<2>() && mono_index_consistent<3>(),
+              "monomial index map");
 
 // Feature q <-> (a, b, l): q = l*K(K+1)/2 + row-major rank of (a, b), a <= b, in the upper
 // triangle.  first[l] = first monomial of angular momentum l.

@@ -35,19 +35,17 @@ __device__ __forceinline__ void sincos_half_pi(float v, float &s, float &c) {
 // f_c = (1 + cos(pi v))/2 = cos^2(pi v/2), f_c' = -(pi/rc) sin(pi v/2) cos(pi v/2), which has no
 // cancellation near rc.  (The hardware sqrt and cos/sin shifted the total energy by several
 // 1e-6 relative.)
-template <int K, int L, bool DERIV>
+template <int K, int L>
 struct Basis {
     static constexpr int M = n_mono(L);
-    float R[K], dR[DERIV ? K : 1], fc, dfc, A[M];
-    float d, inv_d, v;  // v = d / rc
-    float rx, ry, rz;
-    float ux[L + 1], uy[L + 1], uz[L + 1];
+    float Rf[K], Rd[K], A[M];   // R_k f_c, its derivative along d, monomials of r / rc
+    float inv_d, rx, ry, rz;
 
     __device__ __forceinline__ void eval(double dx, double dy, double dz, const ModelDev *__restrict__ md,
                                          const float *mu) {
         constexpr Mono<L> mono;
         rx = (float)dx; ry = (float)dy; rz = (float)dz;
-        d = sqrtf(rx * rx + ry * ry + rz * rz);
+        const float d = sqrtf(rx * rx + ry * ry + rz * rz);
         inv_d = 1.0f / d;
         // x / rc as a refined quotient (no bias from rounding 1/rc)
         const float rc = md->rc, ir = md->inv_rc;
@@ -55,19 +53,21 @@ struct Basis {
             const float q = x * ir;
             return fmaf(fmaf(-q, rc, x), ir, q);
         };
-        v = div_rc(d);
         float sh, ch;
-        sincos_half_pi(v, sh, ch);
-        fc = ch * ch;
-        if (DERIV) dfc = 2.0f * md->dfc_scale * sh * ch;
-        const float c2 = md->exp2_coef, is2 = md->inv_s2;
+        sincos_half_pi(div_rc(d), sh, ch);
+        const float fc = ch * ch;
+        const float dfc = 2.0f * md->dfc_scale * sh * ch;
+        const float c2 = md->exp2_coef, is2fc = md->inv_s2 * fc;
 #pragma unroll
         for (int k = 0; k < K; ++k) {
+            // dR_k/dd = -(d - mu_k) R_k / s^2
             const float x = d - mu[k];
-            R[k] = __builtin_amdgcn_exp2f(c2 * x * x);
-            if (DERIV) dR[k] = -x * is2 * R[k];
+            const float R = __builtin_amdgcn_exp2f(c2 * x * x);
+            Rf[k] = R * fc;
+            Rd[k] = R * fmaf(-x, is2fc, dfc);
         }
         const float qx = div_rc(rx), qy = div_rc(ry), qz = div_rc(rz);
+        float ux[L + 1], uy[L + 1], uz[L + 1];
         ux[0] = uy[0] = uz[0] = 1.0f;
 #pragma unroll
         for (int p = 1; p <= L; ++p) {
@@ -457,7 +457,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
         const int64_t v = act_n[e];
         const float *rv = c + v * rec_stride(K);   // node record: position, then messages
         const double *pv = reinterpret_cast<const double *>(rv);
-        Basis<K, L, true> b;
+        Basis<K, L> b;
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
         const float *cv = rv + kRecC;
         float s = 0.0f, Q[M];
@@ -468,22 +468,24 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
             float u = 0.0f;
 #pragma unroll
             for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
-            const float Rf = b.R[k] * b.fc;
-            if (WANT_W) w[e * K + k] = u * Rf;
-            s += cv[k] * u * (b.dR[k] * b.fc + b.R[k] * b.dfc);
-            const float P = cv[k] * Rf;
+            if (WANT_W) w[e * K + k] = u * b.Rf[k];
+            s = fmaf(cv[k] * u, b.Rd[k], s);
+            const float P = cv[k] * b.Rf[k];
 #pragma unroll
             for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
         }
-        // radial part along r/d, angular part through dA_m/dr
-        float g[3] = {s * b.rx * b.inv_d, s * b.ry * b.inv_d, s * b.rz * b.inv_d};
+        // angular part: dA_m/dx = lx x^(lx-1) y^ly z^lz / rc^lx..., i.e. lx times the monomial
+        // with one power of x fewer, over rc (likewise y, z)
+        float ga[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-            const int lx = mono.lx[m], ly = mono.ly[m], lz = mono.lz[m];
-            if (lx) g[0] += Q[m] * (float)lx * b.ux[lx - 1] * b.uy[ly] * b.uz[lz] * ir;
-            if (ly) g[1] += Q[m] * (float)ly * b.ux[lx] * b.uy[ly - 1] * b.uz[lz] * ir;
-            if (lz) g[2] += Q[m] * (float)lz * b.ux[lx] * b.uy[ly] * b.uz[lz - 1] * ir;
+            if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
+            if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
+            if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
         }
+        // plus the radial part along r / d
+        const float sd = s * b.inv_d;
+        float g[3] = {fmaf(sd, b.rx, ga[0] * ir), fmaf(sd, b.ry, ga[1] * ir), fmaf(sd, b.rz, ga[2] * ir)};
         float *ge = gedge + 3 * e;
         if (FIRST) {
             ge[0] = g[0]; ge[1] = g[1]; ge[2] = g[2];
@@ -696,7 +698,7 @@ Status aggregate(Context &cx, int t) {
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
-    if (cx.precision == 0) {
+    if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
         MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
                                           cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
                                           cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(),

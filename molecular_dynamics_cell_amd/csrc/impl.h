@@ -62,12 +62,15 @@ struct NetLayout {
 struct Context {
     // ---- model ----
     int S = 0, K = 0, L = 0, T = 0, H = 0, M = 0, D = 0, DP = 0;
-    int precision = 0;  // 0: fp32 orbital sums / fp32 networks; 1: fp64 orbital sums and networks
+    int precision = 0;  // 0: fp32 orbital sums / fp32 networks; 1: fp64 orbital sums and networks;
+                        // 2: fp32 orbital sums, bf16-operand networks with fp32 accumulation
     double rc = 0, sigma = 0, e_scale = 0;
     std::vector<double> mass;
     NetLayout net{};
     Buf weights;        // float, T*S blocks of net.stride
     Buf weights64;      // the same in fp64 (precision 1)
+    NetLayout net16{};  // bf16 operand blocks (precision 2): W1, W2, W3, W1t, W2t and stride
+    Buf weights16;      // bf16 bits, T*S blocks of net16.stride
     Buf model;          // ModelDev
     hipStream_t stream = nullptr;
 
@@ -79,7 +82,8 @@ struct Context {
     int mw = 1;                 // activity-mask words per row (longest row / 32, rounded up)
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
-    int nc[3] = {0, 0, 0};      // interior cells per axis
+    int sub[3] = {1, 1, 1};     // virtual subdomains per axis (the next build applies them)
+    int nc[3] = {0, 0, 0};      // interior cells per axis of one subdomain
     double hcell[3] = {0, 0, 0};
     int64_t step = 0;
     int since_build = 0;
@@ -93,6 +97,7 @@ struct Context {
     Buf ref;                        // double [n][3], positions at the last build
     Buf types;                      // int32 [NN]
     Buf ghost_owner, ghost_code;    // int32 [G]
+    Buf ghost_sub;                  // int32 [G]: subdomain whose shell holds the ghost
     Buf ghost_off;                  // int64 [n+1] ghosts of each owner
     Buf row_off;                    // int64 [n+1] prefix of row lengths (canonical pair order)
     Buf row_len;                    // int32 [n] Verlet entries per row

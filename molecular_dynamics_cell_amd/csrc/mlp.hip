@@ -12,6 +12,7 @@
 // per column tile; the VJP leaves dE/drho in the same layout for the reverse edge pass, which forms
 // dE/dO from it.
 #include <cmath>
+#include <cstring>
 #include <type_traits>
 #include <vector>
 
@@ -94,6 +95,8 @@ struct NetArgs {
     const float *F;        // rho^t / s_t, column-tiled [np][DP]
     const float *W;        // packed weights of (t, species 0); species s at W + s*stride
     const double *W64;     // the same in fp64 (accurate mode)
+    const uint16_t *W16;   // bf16 operand blocks of (t, species 0) (bf16 mode); species s at W16 + s*stride16
+    int64_t stride16, o16W1, o16W2, o16W3, o16W1t, o16W2t, o16lo;
     int64_t stride;
     int64_t oW1, oW2, oW3, oW1t, oW2t, oW3t, ob1, ob2, ob3;
     int S;
@@ -416,21 +419,267 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
     }
 }
 
+// ---- bf16 mode: bf16 operands, fp32 accumulation on v_mfma_f32_16x16x32_bf16 ----
+// Every fp32 operand (features, hidden activations, weights) enters as a pair of bf16 values, its
+// rounding and the rounding of the remainder, and each product takes three instructions; one bf16
+// per operand leaves errors of about 1e-2 of the atomic energies and forces on random networks.
+// One instruction contracts 32 inputs, 8 per lane for each operand; a lane supplies the same 8
+// input indices to A and B, so the products pair up whatever order the hardware sums them in.
+// Lane group g = l/16 takes inputs 32 q + 4 g + j (j < 4) and 32 q + 16 + 4 g + (j - 4) (j >= 4) of
+// block q: these are the accumulator items the lane holds for the 16-row tiles 2q and 2q+1, so
+// hidden activations feed the next product without leaving the lane, and the stored features are
+// two float4 loads (column tiles 2q and 2q+1).  Weights are packed in that order, 8 bf16 per lane.
+// Features and activations are rounded to bf16 (to nearest even) where they enter a product;
+// biases, accumulators, activation functions and every stored result stay fp32.  The output
+// layer's VJP (16 inputs: the messages or the energy) runs in fp32, as in the fp32 networks.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ floatx4 mfma_bf16(const bf16x8 &a, const bf16x8 &b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float (&lo)[4], const float (&hi)[4]) {
+    return bf16x8{(__bf16)lo[0], (__bf16)lo[1], (__bf16)lo[2], (__bf16)lo[3],
+                  (__bf16)hi[0], (__bf16)hi[1], (__bf16)hi[2], (__bf16)hi[3]};
+}
+
+// One operand of 8 inputs as a bf16 pair: h = bf16(x), l = bf16(x - h), so x = h + l to about
+// 2^-17 relative.
+struct BOp {
+    bf16x8 h;
+    bf16x8 l;
+};
+
+__device__ __forceinline__ BOp make_op(const float (&lo)[4], const float (&hi)[4]) {
+    BOp o;
+    o.h = to_bf16x8(lo, hi);
+    float rl[4], rh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        rl[i] = lo[i] - (float)o.h[i];
+        rh[i] = hi[i] - (float)o.h[4 + i];
+    }
+    o.l = to_bf16x8(rl, rh);
+    return o;
+}
+
+// acc[rt][c] += W[rt][q] x[c] for a matrix packed with QT blocks of 32 columns, as
+// Wl xh + Wh xl + Wh xh (the weights' remainder plane sits lo_off elements after the leading one;
+// the dropped Wl xl term is below 2^-16 of the product)
+template <int RT, int CT>
+__device__ __forceinline__ void gemm_bf16(const uint16_t *__restrict__ W, int64_t lo_off, int QT, int q,
+                                          const BOp (&x)[CT], floatx4 (&acc)[RT][CT], int lane) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const size_t o = ((size_t)(rt * QT + q) * 64 + lane) * 8;
+        const bf16x8 wh = *reinterpret_cast<const bf16x8 *>(W + o);
+        const bf16x8 wl = *reinterpret_cast<const bf16x8 *>(W + lo_off + o);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            acc[rt][c] = mfma_bf16(wl, x[c].h, acc[rt][c]);
+            acc[rt][c] = mfma_bf16(wh, x[c].l, acc[rt][c]);
+            acc[rt][c] = mfma_bf16(wh, x[c].h, acc[rt][c]);
+        }
+    }
+}
+
+template <int RT, int CT>
+__device__ __forceinline__ void init_bias4(floatx4 (&acc)[RT][CT], const float *__restrict__ b, int grp) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = b ? b[16 * rt + 4 * grp + i] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) acc[rt][c][i] = v;
+        }
+}
+
+template <int K, int L, int H, int MODE, int CT>
+__global__ __launch_bounds__(64) void k_net16(const NetArgs a) {
+    constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
+    constexpr int DT = DP / 16, HT = H / 16, DQ = (DT + 1) / 2, HQ = H / 32;
+    const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
+    const int tile = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.S && tile >= a.tile_start[s + 1]) ++s;
+    const int64_t base = (int64_t)(tile - a.tile_start[s]) * (16 * CT);
+    const int64_t cnt = a.sp_off[s + 1] - a.sp_off[s];
+    const int32_t *list = a.sp_list + a.sp_off[s];
+    int64_t me[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) me[c] = (base + 16 * c + col < cnt) ? (int64_t)list[base + 16 * c + col] : -1;
+    const float *Wf = a.W + (int64_t)s * a.stride;        // biases and the fp32 output-layer VJP
+    const uint16_t *Wb = a.W16 + (int64_t)s * a.stride16;
+
+    // layer 1: Z1 = W1 rho~ + b1
+    floatx4 z1[HT][CT];
+    init_bias4(z1, Wf + a.ob1, grp);
+#pragma unroll 1
+    for (int q = 0; q < DQ; ++q) {
+        BOp x[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+            if (me[c] >= 0) {
+                const float4 f = *reinterpret_cast<const float4 *>(a.F + tiled(a.np, me[c], 32 * q + 4 * grp));
+                lo[0] = f.x; lo[1] = f.y; lo[2] = f.z; lo[3] = f.w;
+                if (2 * q + 1 < DT) {
+                    const float4 h = *reinterpret_cast<const float4 *>(a.F + tiled(a.np, me[c], 32 * q + 16 + 4 * grp));
+                    hi[0] = h.x; hi[1] = h.y; hi[2] = h.z; hi[3] = h.w;
+                }
+            }
+            x[c] = make_op(lo, hi);
+        }
+        gemm_bf16<HT, CT>(Wb + a.o16W1, a.o16lo, DQ, q, x, z1, lane);
+    }
+    __shared__ float sd1[MODE == kForward ? 1 : HT * CT * 4][64];
+    float h1[HT][CT][4];
+#pragma unroll
+    for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float z = z1[rt][c][i];
+                const float sg = sigmoid(z);
+                h1[rt][c][i] = z * sg;
+                if constexpr (MODE != kForward) sd1[(rt * CT + c) * 4 + i][lane] = sg * (1.0f + z * (1.0f - sg));
+            }
+    // layer 2
+    floatx4 z2[HT][CT];
+    init_bias4(z2, Wf + a.ob2, grp);
+#pragma unroll
+    for (int q = 0; q < HQ; ++q) {
+        BOp x[CT];
+#pragma unroll
+        for (int c = 0; c < CT; ++c) x[c] = make_op(h1[2 * q][c], h1[2 * q + 1][c]);
+        gemm_bf16<HT, CT>(Wb + a.o16W2, a.o16lo, HQ, q, x, z2, lane);
+    }
+    float h2[HT][CT][4], d2[MODE == kForward ? 1 : HT][CT][4];
+#pragma unroll
+    for (int rt = 0; rt < HT; ++rt)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float z = z2[rt][c][i];
+                const float sg = sigmoid(z);
+                h2[rt][c][i] = z * sg;
+                if constexpr (MODE != kForward) d2[rt][c][i] = sg * (1.0f + z * (1.0f - sg));
+            }
+
+    if constexpr (MODE != kBackward) {
+        floatx4 y[1][CT];
+        init_bias4(y, Wf + a.ob3, grp);
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) {
+            BOp x[CT];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) x[c] = make_op(h2[2 * q][c], h2[2 * q + 1][c]);
+            gemm_bf16<1, CT>(Wb + a.o16W3, a.o16lo, HQ, q, x, y, lane);
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            if (me[c] < 0) continue;
+            if constexpr (MODE == kForward) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int k = 4 * grp + i;
+                    if (k < K) a.c_next[me[c] * rec_stride(K) + k] = y[0][c][i];
+                }
+            } else {
+                if (grp == 0) a.Ei[me[c]] = a.e_scale * y[0][c][0];
+            }
+        }
+    }
+    if constexpr (MODE != kForward) {
+        float gy[CT][4];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 4 * grp + i;
+                if constexpr (MODE == kEnergy) gy[c][i] = (k == 0) ? a.e_scale : 0.0f;
+                else gy[c][i] = (k < K && me[c] >= 0) ? a.Gc[me[c] * K + k] : 0.0f;
+            }
+        float gz2[HT][CT][4];
+        {
+            const float4 *W3t = reinterpret_cast<const float4 *>(Wf + a.oW3t);
+#pragma unroll
+            for (int rt = 0; rt < HT; ++rt) {
+                const float4 w = W3t[rt * 64 + lane];
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    floatx4 t = mfma4(w.x, gy[c][0], floatx4{0.f, 0.f, 0.f, 0.f});
+                    t = mfma4(w.y, gy[c][1], t);
+                    t = mfma4(w.z, gy[c][2], t);
+                    t = mfma4(w.w, gy[c][3], t);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gz2[rt][c][i] = t[i] * d2[rt][c][i];
+                }
+            }
+        }
+        floatx4 g1[HT][CT];
+        init_bias4<HT, CT>(g1, nullptr, grp);
+#pragma unroll
+        for (int q = 0; q < HQ; ++q) {
+            BOp x[CT];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) x[c] = make_op(gz2[2 * q][c], gz2[2 * q + 1][c]);
+            gemm_bf16<HT, CT>(Wb + a.o16W2t, a.o16lo, HQ, q, x, g1, lane);
+        }
+        BOp xb[HQ][CT];
+#pragma unroll
+        for (int q = 0; q < HQ; ++q)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                float lo[4], hi[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lo[i] = g1[2 * q][c][i] * sd1[((2 * q) * CT + c) * 4 + i][lane];
+                    hi[i] = g1[2 * q + 1][c][i] * sd1[((2 * q + 1) * CT + c) * 4 + i][lane];
+                }
+                xb[q][c] = make_op(lo, hi);
+            }
+        // dE/drho = (W1^T dE/dZ1) / s_t, one 16-row tile at a time
+#pragma unroll 1
+        for (int rt = 0; rt < DT; ++rt) {
+            floatx4 gr[1][CT];
+            init_bias4<1, CT>(gr, nullptr, grp);
+#pragma unroll
+            for (int q = 0; q < HQ; ++q)
+                gemm_bf16<1, CT>(Wb + a.o16W1t + (size_t)rt * HQ * 64 * 8, a.o16lo, HQ, q, xb[q], gr, lane);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                if (me[c] >= 0)
+                    *reinterpret_cast<float4 *>(a.Grho + tiled(a.np, me[c], 16 * rt + 4 * grp)) =
+                        float4{gr[0][c][0] * a.inv_scale, gr[0][c][1] * a.inv_scale, gr[0][c][2] * a.inv_scale,
+                               gr[0][c][3] * a.inv_scale};
+        }
+    }
+}
+
 // atom tiles per wave: one (16 atoms).  Two tiles let each weight load feed two tiles but were
 // measured no faster (the reverse network loses occupancy to the larger accumulators).
 constexpr int tiles_per_wave(int) { return 1; }
+constexpr int kBf16Tiles = 2;   // atom tiles per wave of the bf16 networks (measured: 1 and 4 slower)
 
 NetArgs make_args(Context &cx, int t) {
     NetArgs a{};
     a.W = cx.weights.as<float>() + (int64_t)t * cx.S * cx.net.stride;
-    a.W64 = cx.precision ? cx.weights64.as<double>() + (int64_t)t * cx.S * cx.net.stride : nullptr;
+    a.W64 = cx.precision == 1 ? cx.weights64.as<double>() + (int64_t)t * cx.S * cx.net.stride : nullptr;
     a.stride = (int64_t)cx.net.stride;
+    a.W16 = cx.precision == 2 ? cx.weights16.as<uint16_t>() + (int64_t)t * cx.S * cx.net16.stride : nullptr;
+    a.stride16 = (int64_t)cx.net16.stride;
+    a.o16W1 = cx.net16.W1; a.o16W2 = cx.net16.W2; a.o16W3 = cx.net16.W3;
+    a.o16W1t = cx.net16.W1t; a.o16W2t = cx.net16.W2t; a.o16lo = cx.net16.b1;
     a.oW1 = cx.net.W1; a.oW2 = cx.net.W2; a.oW3 = cx.net.W3;
     a.oW1t = cx.net.W1t; a.oW2t = cx.net.W2t; a.oW3t = cx.net.W3t;
     a.ob1 = cx.net.b1; a.ob2 = cx.net.b2; a.ob3 = cx.net.b3;
     a.S = cx.S;
     a.sp_list = cx.sp_list.as<int32_t>();
-    const int per = 16 * (cx.precision ? 1 : tiles_per_wave(cx.H));   // the fp64 kernel takes one tile
+    const int per = 16 * (cx.precision == 0 ? tiles_per_wave(cx.H) : cx.precision == 2 ? kBf16Tiles : 1);
     int64_t off = 0;
     int32_t tiles = 0;
     for (int s = 0; s <= cx.S; ++s) {
@@ -451,7 +700,8 @@ NetArgs make_args(Context &cx, int t) {
 
 #define MPNN_NET(K_, L_, H_, MODE_, A_)                                                          \
     do {                                                                                         \
-        if (cx.precision) k_net64<K_, L_, H_, MODE_><<<tiles, 64, 0, cx.stream>>>(A_);          \
+        if (cx.precision == 1) k_net64<K_, L_, H_, MODE_><<<tiles, 64, 0, cx.stream>>>(A_);     \
+        else if (cx.precision == 2) k_net16<K_, L_, H_, MODE_, kBf16Tiles><<<tiles, 64, 0, cx.stream>>>(A_); \
         else k_net<K_, L_, H_, MODE_, tiles_per_wave(H_)><<<tiles, 64, 0, cx.stream>>>(A_);      \
     } while (0)
 
@@ -485,6 +735,40 @@ void pack_a(const double *W, int R, int C, int Rp, int Cp, bool transpose, T *ou
                     double v = 0.0;
                     if (r < R && c < C) v = transpose ? W[(size_t)c * R + r] : W[(size_t)r * C + c];
                     out[(((size_t)rt * CT + ct) * 64 + l) * 4 + i] = (T)v;
+                }
+}
+
+// bf16 operand packing of W [R][C] for the bf16 networks: for row tile rt, 32-column block q,
+// lane l, element j: W[16 rt + l%16][32 q + 16 (j/4) + 4 (l/16) + j%4] (zero outside R x C),
+// rounded to the nearest bf16 (ties to even; the weights are finite)
+uint16_t bf16_bits(double v) {
+    const float f = (float)v;
+    uint32_t u;
+    std::memcpy(&u, &f, sizeof(u));
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// part 0: the bf16 rounding of each weight; part 1: the bf16 rounding of what part 0 leaves
+void pack_bf16(const double *W, int R, int C, int Rp, int Cp, bool transpose, uint16_t *out, int part) {
+    const int RT = Rp / 16, QT = Cp / 32;
+    for (int rt = 0; rt < RT; ++rt)
+        for (int q = 0; q < QT; ++q)
+            for (int l = 0; l < 64; ++l)
+                for (int j = 0; j < 8; ++j) {
+                    const int r = 16 * rt + (l & 15);
+                    const int c = 32 * q + 16 * (j >> 2) + 4 * (l >> 4) + (j & 3);
+                    double v = 0.0;
+                    if (r < R && c < C) v = transpose ? W[(size_t)c * R + r] : W[(size_t)r * C + c];
+                    const uint16_t hb = bf16_bits(v);
+                    uint16_t bits = hb;
+                    if (part == 1) {
+                        const uint32_t u = (uint32_t)hb << 16;
+                        float h;
+                        std::memcpy(&h, &u, sizeof(h));
+                        bits = bf16_bits(v - (double)h);
+                    }
+                    out[(((size_t)rt * QT + q) * 64 + l) * 8 + j] = bits;
                 }
 }
 
@@ -534,7 +818,40 @@ Status pack_weights(Context &cx, const double *mlp) {
     fill(host.data());
     MPNN_TRY(cx.grow(cx.weights, host.size() * sizeof(float)));
     MPNN_HIP(hipMemcpy(cx.weights.p, host.data(), host.size() * sizeof(float), hipMemcpyHostToDevice));
-    if (cx.precision) {
+    if (cx.precision == 2) {
+        NetLayout &nb = cx.net16;
+        const int DQ32 = (DP + 31) / 32 * 32;
+        size_t q = 0;
+        nb.W1 = q; q += (size_t)H * DQ32;
+        nb.W2 = q; q += (size_t)H * H;
+        nb.W3 = q; q += (size_t)16 * H;
+        nb.W1t = q; q += (size_t)DP * H;
+        nb.W2t = q; q += (size_t)H * H;
+        nb.b1 = (q + 63) / 64 * 64;                       // offset of the remainder plane
+        nb.stride = 2 * nb.b1;
+        std::vector<uint16_t> host16((size_t)cx.T * cx.S * nb.stride, 0);
+        const double *p = mlp;
+        for (int t = 0; t < cx.T; ++t) {
+            const int out = t < cx.T - 1 ? K : 1;
+            for (int s = 0; s < cx.S; ++s) {
+                uint16_t *blk = host16.data() + ((size_t)t * cx.S + s) * nb.stride;
+                const double *W1 = p, *b1 = W1 + (size_t)H * D, *W2 = b1 + H, *b2 = W2 + (size_t)H * H;
+                const double *W3 = b2 + H, *b3 = W3 + (size_t)out * H;
+                p = b3 + out;
+                for (int part = 0; part < 2; ++part) {
+                    uint16_t *b = blk + part * nb.b1;
+                    pack_bf16(W1, H, D, H, DQ32, false, b + nb.W1, part);
+                    pack_bf16(W2, H, H, H, H, false, b + nb.W2, part);
+                    pack_bf16(W3, out, H, 16, H, false, b + nb.W3, part);
+                    pack_bf16(W1, D, H, DP, H, true, b + nb.W1t, part);
+                    pack_bf16(W2, H, H, H, H, true, b + nb.W2t, part);
+                }
+            }
+        }
+        MPNN_TRY(cx.grow(cx.weights16, host16.size() * sizeof(uint16_t)));
+        MPNN_HIP(hipMemcpy(cx.weights16.p, host16.data(), host16.size() * sizeof(uint16_t), hipMemcpyHostToDevice));
+    }
+    if (cx.precision == 1) {
         std::vector<double> host64(count, 0.0);
         fill(host64.data());
         MPNN_TRY(cx.grow(cx.weights64, host64.size() * sizeof(double)));

@@ -1,8 +1,12 @@
 // Neighbour build for one GPU's subdomain (paper, section "Parallelization Algorithm",
 // Fig. 3a: each process holds its local atoms (LAs) with full neighbour lists plus ghost atoms
 // (GAs) inside the cutoff of its LAs; Fig. 2: one list, built once, is reused by all T layers).
-// On one GPU the subdomain is the whole periodic box and the ghost shell is made of periodic
-// images within rc + skin of the box (a Verlet skin lets the list live for several steps).
+// On one GPU the subdomain is by default the whole periodic box and the ghost shell is made of
+// periodic images within rc + skin of the box (a Verlet skin lets the list live for several
+// steps).  The box can also be split into px x py x pz equal virtual subdomains: every subdomain
+// then holds its own atoms plus its own shell of images (atoms of the other subdomains and periodic
+// images) within rc + skin, its atoms' rows reference only those nodes, and the per-layer ghost
+// refresh plays the part of the exchange between subdomains (Fig. 3b and Fig. 4 of the paper).
 //
 // Pipeline (all on the device; the host reads three counts to size arrays):
 //   wrap + cell key -> counting sort by Morton cell code (ties by caller id) -> sorted state
@@ -30,9 +34,35 @@ __device__ __forceinline__ uint32_t spread3(uint32_t v) {  // 10 bits -> every t
 
 struct Grid {
     double L[3], h[3];
-    int n[3];
-    int morton;  // 1: Morton code of the interior cell, 0: linear index
+    double Ls[3];   // subdomain edge L / P
+    int n[3];       // interior cells per axis of one subdomain
+    int P[3];       // subdomains per axis
+    int morton;     // 1: Morton code of the interior cell, 0: linear index
+    int64_t krange; // cell keys per subdomain
+    int64_t next;   // extended cells per subdomain
 };
+
+// Subdomain slot along axis a of a wrapped coordinate (0 with one subdomain per axis), and the
+// faces of slot p (0 and L with one subdomain).
+__device__ __forceinline__ int sub_slot(double x, const Grid &g, int a) {
+    if (g.P[a] == 1) return 0;
+    int p = (int)floor(__ddiv_rn(x, g.Ls[a]));
+    return p < 0 ? 0 : (p >= g.P[a] ? g.P[a] - 1 : p);
+}
+
+__device__ __forceinline__ double sub_lo(int p, const Grid &g, int a) { return (double)p * g.Ls[a]; }
+
+__device__ __forceinline__ double sub_hi(int p, const Grid &g, int a) {
+    return p == g.P[a] - 1 ? g.L[a] : (double)(p + 1) * g.Ls[a];
+}
+
+__device__ __forceinline__ int sub_index(const int (&p)[3], const Grid &g) { return (p[0] * g.P[1] + p[1]) * g.P[2] + p[2]; }
+
+__device__ __forceinline__ void sub_coords(int q, const Grid &g, int (&p)[3]) {
+    p[0] = q / (g.P[1] * g.P[2]);
+    p[1] = (q / g.P[2]) % g.P[1];
+    p[2] = q % g.P[2];
+}
 
 __device__ __forceinline__ double wrap1(double r, double L) {
     double f = floor(__ddiv_rn(r, L));
@@ -48,14 +78,17 @@ __global__ void k_wrap_key(int64_t n, const double *__restrict__ pos_in, Grid g,
                            double *__restrict__ pos_w, int32_t *__restrict__ key) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    int c[3];
+    int c[3], p[3];
     for (int a = 0; a < 3; ++a) {
         double x = wrap1(pos_in[3 * i + a], g.L[a]);
         pos_w[3 * i + a] = x;
-        c[a] = interior_cell(x, g.h[a], g.n[a]);
+        p[a] = sub_slot(x, g, a);
+        c[a] = interior_cell(__dsub_rn(x, sub_lo(p[a], g, a)), g.h[a], g.n[a]);
     }
-    key[i] = g.morton ? (int32_t)(spread3(c[0]) << 2 | spread3(c[1]) << 1 | spread3(c[2]))
-                      : (int32_t)((c[0] * g.n[1] + c[1]) * g.n[2] + c[2]);
+    // subdomain-major, then the cell order inside the subdomain
+    const int64_t k = g.morton ? (int64_t)(spread3(c[0]) << 2 | spread3(c[1]) << 1 | spread3(c[2]))
+                               : (int64_t)((c[0] * g.n[1] + c[1]) * g.n[2] + c[2]);
+    key[i] = (int32_t)(sub_index(p, g) * g.krange + k);
 }
 
 __global__ void k_count(int64_t n, const int32_t *__restrict__ key, int32_t *__restrict__ cnt) {
@@ -159,42 +192,56 @@ __global__ void k_gather_sorted(int64_t n, const int32_t *__restrict__ perm,
     }
 }
 
-// An image x + s*L (s = -1, 0, 1 per axis) belongs to the ghost shell when every component
-// lies in [-w, L + w).
-__device__ __forceinline__ bool in_shell(const double *x, int code, const double *L, double w) {
-    int s[3];
+// An image x + s*L (s = -1, 0, 1 per axis) belongs to the shell of subdomain q when every
+// component lies in [lo_q - w, hi_q + w), unless it is the atom itself in its own subdomain
+// (s = 0 and q the atom's subdomain).  With one subdomain: [-w, L + w), every s except 0.
+__device__ __forceinline__ bool in_shell(const double *x, int code, int q, int own, const Grid &g, double w) {
+    if (code == 13 && q == own) return false;
+    int s[3], p[3];
     shift_of(code, s[0], s[1], s[2]);
+    sub_coords(q, g, p);
     for (int a = 0; a < 3; ++a) {
-        double y = __dadd_rn(x[a], (double)s[a] * L[a]);
-        if (!(y >= -w && y < L[a] + w)) return false;
+        double y = __dadd_rn(x[a], (double)s[a] * g.L[a]);
+        if (!(y >= __dsub_rn(sub_lo(p[a], g, a), w) && y < __dadd_rn(sub_hi(p[a], g, a), w))) return false;
     }
     return true;
+}
+
+__device__ __forceinline__ int own_sub(const double (&x)[3], const Grid &g) {
+    int p[3];
+    for (int a = 0; a < 3; ++a) p[a] = sub_slot(x[a], g, a);
+    return sub_index(p, g);
 }
 
 __global__ void k_ghost_count(int64_t n, const double *__restrict__ pos, Grid g, double w,
                               int32_t *__restrict__ cnt) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    const double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    const int own = own_sub(x, g), nsub = g.P[0] * g.P[1] * g.P[2];
     int c = 0;
-    for (int code = 0; code < 27; ++code)
-        if (code != 13 && in_shell(x, code, g.L, w)) ++c;
+    for (int q = 0; q < nsub; ++q)
+        for (int code = 0; code < 27; ++code)
+            if (in_shell(x, code, q, own, g, w)) ++c;
     cnt[i] = c;
 }
 
 __global__ void k_ghost_fill(int64_t n, const double *__restrict__ pos, Grid g, double w,
                              const int64_t *__restrict__ off, int32_t *__restrict__ owner,
-                             int32_t *__restrict__ code_out) {
+                             int32_t *__restrict__ code_out, int32_t *__restrict__ sub_out) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    const double x[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+    const int own = own_sub(x, g), nsub = g.P[0] * g.P[1] * g.P[2];
     int64_t o = off[i];
-    for (int code = 0; code < 27; ++code)
-        if (code != 13 && in_shell(x, code, g.L, w)) {
-            owner[o] = (int32_t)i;
-            code_out[o] = code;
-            ++o;
-        }
+    for (int q = 0; q < nsub; ++q)
+        for (int code = 0; code < 27; ++code)
+            if (in_shell(x, code, q, own, g, w)) {
+                owner[o] = (int32_t)i;
+                code_out[o] = code;
+                sub_out[o] = q;
+                ++o;
+            }
 }
 
 // Ghost g = image of its owner: position owner + s*L (exactly as in the distance test).
@@ -229,13 +276,22 @@ __device__ __forceinline__ int ext_cell(double x, double h, int n) {
     return c < 0 ? 0 : (c > n + 1 ? n + 1 : c);
 }
 
-__global__ void k_ext_key(int64_t NN, const double *__restrict__ pos, Grid g, int32_t *__restrict__ key) {
+// Extended cell of a node in the grid of subdomain q (a local atom's own subdomain, a ghost's
+// shell), subdomain-major.
+__device__ __forceinline__ int64_t ext_key(const double (&x)[3], int q, const Grid &g) {
+    int p[3], c[3];
+    sub_coords(q, g, p);
+    for (int a = 0; a < 3; ++a) c[a] = ext_cell(__dsub_rn(x[a], sub_lo(p[a], g, a)), g.h[a], g.n[a]);
+    return (int64_t)q * g.next + ((int64_t)c[0] * (g.n[1] + 2) + c[1]) * (g.n[2] + 2) + c[2];
+}
+
+__global__ void k_ext_key(int64_t NN, int64_t n, const double *__restrict__ pos, const int32_t *__restrict__ gsub,
+                          Grid g, int32_t *__restrict__ key) {
     int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (v >= NN) return;
-    int cx = ext_cell(pos[3 * v], g.h[0], g.n[0]);
-    int cy = ext_cell(pos[3 * v + 1], g.h[1], g.n[1]);
-    int cz = ext_cell(pos[3 * v + 2], g.h[2], g.n[2]);
-    key[v] = (int32_t)((cx * (g.n[1] + 2) + cy) * (g.n[2] + 2) + cz);
+    const double x[3] = {pos[3 * v], pos[3 * v + 1], pos[3 * v + 2]};
+    const int q = v < n ? own_sub(x, g) : gsub[v - n];
+    key[v] = (int32_t)ext_key(x, q, g);
 }
 
 // Receiver rows: every node v != i of the 27 extended cells around local atom i with
@@ -249,10 +305,16 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
-    const int cx = ext_cell(xi, g.h[0], g.n[0]);
-    const int cy = ext_cell(yi, g.h[1], g.n[1]);
-    const int cz = ext_cell(zi, g.h[2], g.n[2]);
+    // the stencil lives in the receiver's own subdomain grid, which holds only its nodes
+    const double xv[3] = {xi, yi, zi};
+    const int q = own_sub(xv, g);
+    int p[3];
+    sub_coords(q, g, p);
+    const int cx = ext_cell(__dsub_rn(xi, sub_lo(p[0], g, 0)), g.h[0], g.n[0]);
+    const int cy = ext_cell(__dsub_rn(yi, sub_lo(p[1], g, 1)), g.h[1], g.n[1]);
+    const int cz = ext_cell(__dsub_rn(zi, sub_lo(p[2], g, 2)), g.h[2], g.n[2]);
     const int ny = g.n[1] + 2, nz = g.n[2] + 2;
+    const int64_t cell0 = (int64_t)q * g.next;
     const int64_t base = FILL ? sell_base(slab_off, i) : 0;
     int64_t o = 0;
     int32_t c = 0;
@@ -265,7 +327,7 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
             for (int dz = -1; dz <= 1; ++dz) {
                 int z = cz + dz;
                 if (z < 0 || z > g.n[2] + 1) continue;
-                int64_t cell = ((int64_t)x * ny + y) * nz + z;
+                int64_t cell = cell0 + ((int64_t)x * ny + y) * nz + z;
                 for (int64_t p = coff[cell]; p < coff[cell + 1]; ++p) {
                     int32_t v = cnodes[p];
                     if (v == (int32_t)i) continue;
@@ -382,6 +444,8 @@ Grid make_grid(const Context &cx) {
         g.L[a] = cx.box[a];
         g.h[a] = cx.hcell[a];
         g.n[a] = cx.nc[a];
+        g.P[a] = cx.sub[a];
+        g.Ls[a] = cx.box[a] / cx.sub[a];
     }
     int mx = cx.nc[0] > cx.nc[1] ? cx.nc[0] : cx.nc[1];
     mx = mx > cx.nc[2] ? mx : cx.nc[2];
@@ -389,17 +453,15 @@ Grid make_grid(const Context &cx) {
     while ((1 << bits) < mx) ++bits;
     int64_t cells = (int64_t)cx.nc[0] * cx.nc[1] * cx.nc[2];
     g.morton = bits <= 10 && ((int64_t)1 << (3 * bits)) <= 8 * cells;
+    g.krange = g.morton ? (int64_t)1 << (3 * bits) : cells;
+    g.next = (int64_t)(cx.nc[0] + 2) * (cx.nc[1] + 2) * (cx.nc[2] + 2);
     return g;
 }
 
-int64_t key_range(const Grid &g) {
-    if (!g.morton) return (int64_t)g.n[0] * g.n[1] * g.n[2];
-    int mx = g.n[0] > g.n[1] ? g.n[0] : g.n[1];
-    mx = mx > g.n[2] ? mx : g.n[2];
-    int bits = 0;
-    while ((1 << bits) < mx) ++bits;
-    return (int64_t)1 << (3 * bits);
-}
+int64_t n_sub(const Context &cx) { return (int64_t)cx.sub[0] * cx.sub[1] * cx.sub[2]; }
+
+// cell keys over all subdomains
+int64_t key_range(const Grid &g) { return g.krange * g.P[0] * g.P[1] * g.P[2]; }
 
 template <class T>
 Status fetch(Context &cx, const T *dev, T *host) {
@@ -433,11 +495,12 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     cx.graph_valid = false;   // buffers and launch shapes may change
     const double w = cx.rc + skin;
     for (int a = 0; a < 3; ++a) {
-        if (!(box[a] > w)) return Status::err(MPNN_E_BOX, "box edge must exceed rc + skin");
-        int c = (int)floor(box[a] / (w + 1e-8));
-        if (c < 1) return Status::err(MPNN_E_BOX, "box edge must exceed rc + skin");
+        const double Ls = box[a] / cx.sub[a];   // subdomain edge (the box itself by default)
+        if (!(Ls > w)) return Status::err(MPNN_E_BOX, "box edge / subdomains must exceed rc + skin");
+        int c = (int)floor(Ls / (w + 1e-8));
+        if (c < 1) return Status::err(MPNN_E_BOX, "box edge / subdomains must exceed rc + skin");
         cx.nc[a] = c;
-        cx.hcell[a] = box[a] / c;
+        cx.hcell[a] = Ls / c;
         cx.box[a] = box[a];
     }
     cx.skin = skin;
@@ -445,7 +508,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     cx.n = n;
     const Grid g = make_grid(cx);
     const int64_t nkeys = key_range(g);
-    const int64_t next = (int64_t)(cx.nc[0] + 2) * (cx.nc[1] + 2) * (cx.nc[2] + 2);
+    const int64_t next = g.next * n_sub(cx);   // extended cells over all subdomains
     const int64_t n1 = n > 0 ? n : 1;
 
     // ---- wrap, Morton order, sorted state ----
@@ -503,13 +566,15 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     const int64_t NN1 = cx.NN > 0 ? cx.NN : 1;
     MPNN_TRY(cx.grow(cx.ghost_owner, sizeof(int32_t) * (G > 0 ? G : 1)));
     MPNN_TRY(cx.grow(cx.ghost_code, sizeof(int32_t) * (G > 0 ? G : 1)));
+    MPNN_TRY(cx.grow(cx.ghost_sub, sizeof(int32_t) * (G > 0 ? G : 1)));
     {
         // keep sorted local state while the node arrays grow
         MPNN_TRY(cx.grow_keep(cx.pos, sizeof(double) * 3 * NN1, sizeof(double) * 3 * n1));
         MPNN_TRY(cx.grow_keep(cx.types, sizeof(int32_t) * NN1, sizeof(int32_t) * n1));
     }
     k_ghost_fill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, wg, cx.ghost_off.as<int64_t>(),
-                                                        cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>());
+                                                        cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>(),
+                                                        cx.ghost_sub.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     k_ghost_pos<<<grid_for(G), kBlock, 0, cx.stream>>>(G, n, cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>(),
                                                        g, cx.pos.as<double>(), cx.types.as<int32_t>());
@@ -522,7 +587,8 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.tmp_b, sizeof(int32_t) * (size_t)(NN1 > next ? NN1 : next) * 2));
     key = cx.tmp_b.as<int32_t>();
     int32_t *cnodes = key + (NN1 > next ? NN1 : next);
-    k_ext_key<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.pos.as<double>(), g, key);
+    k_ext_key<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, n, cx.pos.as<double>(), cx.ghost_sub.as<int32_t>(),
+                                                         g, key);
     MPNN_HIP(hipGetLastError());
     MPNN_TRY(counting_sort(cx, key, cx.NN, next, off, cnodes, cnt));
 

@@ -14,9 +14,11 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_model(params, s, skin=None):
+def gpu_model(params, s, skin=None, subdomains=None):
     dev = torch.device("cuda:0")
     m = binding.MPNN(params, dev)
+    if subdomains is not None:
+        m.set_subdomains(*subdomains)
     m.build_neighbors(torch.tensor(s.pos, device=dev), torch.tensor(s.types, device=dev), s.box,
                       skin=skin)
     return m
