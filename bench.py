@@ -166,6 +166,32 @@ def cpu_baseline(cfg, budget_s=12.0):
             "sample": f"{sample}; {steps} velocity-Verlet steps (E+F each step) in {el:.1f} s"}
 
 
+def bandwidth(gib=4, reps=10):
+    """Practical HBM rates of plain device copies (torch kernels): the ceiling the
+    memory-bound kernels can approach, next to the 8 TB/s published peak."""
+    import torch
+    d = torch.device("cuda:0")
+    a = torch.ones(gib * (1 << 28), dtype=torch.float32, device=d)
+    b = torch.empty_like(a)
+    nbytes = a.numel() * 4
+
+    def rate(f, moved):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(moved / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9, 1)
+
+    return {"unit": "GB/s", "bytes": nbytes, "peak": HBM_PEAK_GBS,
+            "copy_read_plus_write": rate(lambda: b.copy_(a), 2 * nbytes),
+            "fill_write": rate(lambda: b.fill_(1.0), nbytes),
+            "sum_read": rate(lambda: a.sum(), nbytes)}
+
+
 def t_sweep(max_t=6, evals=10):
     """Cost of one E+F evaluation against the number of message-passing layers T (the pages' claim
     of a cost linear in T), on the 2.05M-atom Ag subdomain with random-init models of each depth,
@@ -239,6 +265,8 @@ def main():
                     help="MD steps per captured replay (0: eager; default: 8 below 1,000 atoms, else 0)")
     ap.add_argument("--subdomains", type=str, default="1,1,1",
                     help="px,py,pz virtual subdomains (per-layer ghost refresh between them)")
+    ap.add_argument("--bandwidth", action="store_true",
+                    help="instead of the benchmark line: device copy / fill / read rates (practical HBM ceiling)")
     ap.add_argument("--t-sweep", action="store_true",
                     help="instead of the benchmark line: E+F cost vs layers T and ghost volume vs size")
     args = ap.parse_args()
@@ -250,6 +278,9 @@ def main():
 
     if args.t_sweep:
         print(json.dumps(t_sweep()))
+        return
+    if args.bandwidth:
+        print(json.dumps(bandwidth()))
         return
 
     import torch
