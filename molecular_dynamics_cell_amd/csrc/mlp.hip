@@ -114,7 +114,7 @@ struct NetArgs {
 enum { kForward = 0, kEnergy = 1, kBackward = 2 };
 
 template <int K, int L, int H, int MODE, int CT>
-__global__ __launch_bounds__(64, (H == 128 && MODE == kBackward) ? 1 : 2) void k_net(const NetArgs a) {
+__global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
     constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
     constexpr int DT = DP / 16, HT = H / 16;
     const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
@@ -314,7 +314,7 @@ __device__ __forceinline__ void init64(doublex4 (&acc)[RT], const double *__rest
 }
 
 template <int K, int L, int H, int MODE>
-__global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
+__global__ __launch_bounds__(64, 2) void k_net64(const NetArgs a) {
     constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
     constexpr int DT = DP / 16, HT = H / 16;
     const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
@@ -325,8 +325,9 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
     const int64_t cnt = a.sp_off[s + 1] - a.sp_off[s];
     const int64_t me = (base + col < cnt) ? (int64_t)a.sp_list[a.sp_off[s] + base + col] : -1;
     const double *W = a.W64 + (int64_t)s * a.stride;
-    // silu' of both hidden layers, parked in LDS for the reverse pass
-    __shared__ double sd[MODE == kForward ? 1 : 2 * HT * 4][64];
+    // silu' of the first hidden layer, parked in LDS for the reverse pass (the second stays in
+    // registers), so two waves fit per SIMD
+    __shared__ double sd[MODE == kForward ? 1 : HT * 4][64];
 
     doublex4 z1[HT];
     init64(z1, W + a.ob1, grp);
@@ -351,14 +352,14 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
     init64(z2, W + a.ob2, grp);
 #pragma unroll
     for (int kt = 0; kt < HT; ++kt) gemm64_step<HT>(W + a.oW2, HT, kt, h1[kt], z2, lane);
-    double h2[HT][4];
+    double h2[HT][4], d2[MODE == kForward ? 1 : HT][4];
 #pragma unroll
     for (int rt = 0; rt < HT; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const double z = z2[rt][i], sg = 1.0 / (1.0 + exp(-z));
             h2[rt][i] = z * sg;
-            if constexpr (MODE != kForward) sd[(HT + rt) * 4 + i][lane] = sg * (1.0 + z * (1.0 - sg));
+            if constexpr (MODE != kForward) d2[rt][i] = sg * (1.0 + z * (1.0 - sg));
         }
     if constexpr (MODE != kBackward) {
         doublex4 y[1];
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(64, 1) void k_net64(const NetArgs a) {
 #pragma unroll
         for (int rt = 0; rt < HT; ++rt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) gz2[rt][i] = g2[rt][i] * sd[(HT + rt) * 4 + i][lane];
+            for (int i = 0; i < 4; ++i) gz2[rt][i] = g2[rt][i] * d2[rt][i];
         doublex4 g1[HT];
         init64<HT>(g1, nullptr, grp);
 #pragma unroll
