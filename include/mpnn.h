@@ -39,6 +39,7 @@
 #ifndef MPNN_H
 #define MPNN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -113,6 +114,16 @@ void mpnn_destroy(mpnn_ctx *ctx);
 /* Stream for every later call (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream);
  * NULL selects the null stream. */
 mpnn_status mpnn_set_stream(mpnn_ctx *ctx, void *hip_stream);
+
+/* Device memory source for the buffers allocated from now on: alloc(bytes, user) returns device
+ * memory usable on the context's stream (NULL = out of memory, MPNN_E_OOM), release(ptr, user)
+ * takes back a pointer it returned; e.g. a framework's caching allocator.  Both NULL restores
+ * hipMalloc / hipFree.  Buffers that already exist are kept and go back, when they are replaced
+ * or the context is destroyed, to the allocator that made them, so the hooks and `user` must stay
+ * valid until then.  The library synchronises its stream before handing a buffer back.  Passing
+ * only one of the two hooks is MPNN_E_INVALID_ARG. */
+mpnn_status mpnn_set_allocator(mpnn_ctx *ctx, void *(*alloc)(size_t bytes, void *user),
+                               void (*release)(void *ptr, void *user), void *user);
 
 /* Neighbour build for n atoms at `pos` ([n][3] fp64, device) with species `types` ([n] int32,
  * device) in the orthorhombic periodic box `box` (host, A).  Wraps positions into the box,

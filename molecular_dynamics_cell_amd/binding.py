@@ -35,6 +35,11 @@ class _Params(C.Structure):
                 ("e_scale", C.c_double), ("mass", C.POINTER(C.c_double))]
 
 
+# device allocator hooks of mpnn_set_allocator
+_ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p)
+_FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p)
+
+
 class MDStats(C.Structure):
     _fields_ = [("epot", C.c_double), ("ekin", C.c_double), ("temp", C.c_double),
                 ("rebuilds", C.c_int64), ("max_disp", C.c_double), ("steps", C.c_int64)]
@@ -74,6 +79,7 @@ def lib():
             "mpnn_get_info": ([p, C.POINTER(Info)], st),
             "mpnn_set_graph_replay": ([p, i32], st),
             "mpnn_set_subdomains": ([p, i32, i32, i32], st),
+            "mpnn_set_allocator": ([p, _ALLOC_FN, _FREE_FN, p], st),
             "mpnn_set_profiling": ([p, i32], st),
             "mpnn_get_profile": ([p, i32, C.POINTER(C.c_char_p), C.POINTER(C.c_double),
                                   C.POINTER(C.c_int64)], st),
@@ -138,7 +144,25 @@ class MPNN:
             pass
 
     def set_stream(self, stream: torch.cuda.Stream):
+        self._stream = stream
         self._check(lib().mpnn_set_stream(self.h, C.c_void_p(stream.cuda_stream)))
+
+    def use_torch_allocator(self):
+        """Take the context's later device buffers from torch's caching allocator, on the
+        context's stream (existing buffers stay where they are)."""
+        dev, stream = self.device, self._stream
+
+        def alloc(nbytes, user):
+            try:
+                return torch.cuda.caching_allocator_alloc(int(nbytes), dev, stream)
+            except RuntimeError:
+                return None   # NULL: the library reports out of memory
+
+        def release(ptr, user):
+            torch.cuda.caching_allocator_delete(ptr)
+
+        self._hooks = (_ALLOC_FN(alloc), _FREE_FN(release))   # alive as long as the context
+        self._check(lib().mpnn_set_allocator(self.h, self._hooks[0], self._hooks[1], None))
 
     def build_neighbors(self, pos: torch.Tensor, types: torch.Tensor, box, rc=None, skin=None):
         pos = pos.to(self.device, torch.float64).contiguous()

@@ -24,9 +24,18 @@ Status Context::grow(Buf &b, size_t bytes) {
     }
     size_t want = bytes + bytes / 8;
     void *p = nullptr;
-    if (hipMalloc(&p, want) != hipSuccess) {
-        (void)hipGetLastError();
-        return Status::err(MPNN_E_OOM, "hipMalloc of " + std::to_string(want) + " bytes failed");
+    if (alloc_fn) {
+        p = alloc_fn(want, alloc_user);
+        if (!p) return Status::err(MPNN_E_OOM, "allocator hook returned NULL for " + std::to_string(want) + " bytes");
+        b.free_fn = free_fn;
+        b.free_user = alloc_user;
+    } else {
+        if (hipMalloc(&p, want) != hipSuccess) {
+            (void)hipGetLastError();
+            return Status::err(MPNN_E_OOM, "hipMalloc of " + std::to_string(want) + " bytes failed");
+        }
+        b.free_fn = nullptr;
+        b.free_user = nullptr;
     }
     b.p = p;
     b.bytes = want;
@@ -93,16 +102,19 @@ void Context::prof_harvest() {
 
 void Context::release(Buf &b) {
     if (b.p) {
-        (void)hipFree(b.p);
+        if (b.free_fn) b.free_fn(b.p, b.free_user);
+        else (void)hipFree(b.p);
         device_bytes -= b.bytes;
     }
     b.p = nullptr;
     b.bytes = 0;
+    b.free_fn = nullptr;
+    b.free_user = nullptr;
 }
 
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
-    Buf *all[] = {&weights, &weights64, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
+    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
@@ -410,6 +422,18 @@ mpnn_status mpnn_set_graph_replay(mpnn_ctx *ctx, int32_t steps_per_replay) {
     mpnn::Context &cx = ctx->cx;
     cx.graph_steps = steps_per_replay;
     cx.graph_valid = false;
+    return mpnn::finish(ctx, Status::ok());
+}
+
+mpnn_status mpnn_set_allocator(mpnn_ctx *ctx, void *(*alloc)(size_t, void *), void (*release)(void *, void *),
+                               void *user) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    if ((alloc == nullptr) != (release == nullptr))
+        return mpnn::finish(ctx, Status::err(MPNN_E_INVALID_ARG, "allocator and release hooks go together"));
+    mpnn::Context &cx = ctx->cx;
+    cx.alloc_fn = alloc;
+    cx.free_fn = release;
+    cx.alloc_user = user;
     return mpnn::finish(ctx, Status::ok());
 }
 

@@ -49,6 +49,8 @@ extern const char *const kProfNames[kProfCount];
 struct Buf {
     void *p = nullptr;
     size_t bytes = 0;
+    void (*free_fn)(void *, void *) = nullptr;   // the caller's release hook that owns p, if any
+    void *free_user = nullptr;
     template <class T> T *as() const { return static_cast<T *>(p); }
 };
 
@@ -127,6 +129,10 @@ struct Context {
 
     std::string last_error;
     size_t device_bytes = 0;
+    // caller-supplied device allocator (mpnn_set_allocator); hipMalloc / hipFree when null
+    void *(*alloc_fn)(size_t, void *) = nullptr;
+    void (*free_fn)(void *, void *) = nullptr;
+    void *alloc_user = nullptr;
 
     // ---- event profiler ----
     bool prof_on = false;

@@ -141,3 +141,43 @@ def test_layer_counts(T):
     E, F, _ = m.energy_forces()
     Eo, Fo, _ = oracle_ef(p, s)
     check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"Ag108, T={T}")
+
+
+def test_torch_allocator():
+    """mpnn_set_allocator routed to torch's caching allocator: the buffers come from torch
+    (its allocated-bytes counter grows by them and falls back at destroy), rebuilds hand
+    buffers back and take new ones through the hooks, and the results are bitwise those of
+    hipMalloc'd buffers."""
+    from tests import systems
+    s = systems.ag(6, seed=3)
+    p = I.make_params(4)
+    pos = torch.tensor(s.pos, device=DEV)
+    types = torch.tensor(s.types, device=DEV)
+    vel = torch.tensor(s.vel, device=DEV)
+    results = []
+    for hook in (False, True):
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated(DEV)
+        m = binding.MPNN(p, DEV)
+        if hook:
+            m.use_torch_allocator()
+        m.build_neighbors(pos, types, s.box)
+        m.set_state(vel=vel)
+        held = torch.cuda.memory_allocated(DEV) - before
+        st = m.md_step(1.0, 4, 2)          # two rebuilds: buffers released and taken again
+        E, F, _ = m.energy_forces()
+        results.append((E, F.cpu().numpy(), st["rebuilds"]))
+        info = m.info()
+        del F
+        m.close()
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated(DEV) - before
+        if hook:
+            # everything but the weights (allocated at create, before the hook) is torch's
+            assert held > 0.5 * info["bytes_device"], (held, info["bytes_device"])
+            assert after == 0, after
+        else:
+            assert held == 0
+    assert results[0][2] == results[1][2] >= 2
+    assert results[0][0] == results[1][0]
+    assert np.array_equal(results[0][1], results[1][1])
