@@ -661,12 +661,12 @@ __global__ __launch_bounds__(64) void k_net16(const NetArgs a) {
     }
 }
 
-// atom tiles per wave: one (16 atoms).  Two tiles let each weight load feed two tiles but were
-// measured no faster (the reverse network loses occupancy to the larger accumulators).
-constexpr int tiles_per_wave(int) { return 1; }
+// atom tiles per wave: two for the 64-wide forward network (each weight load feeds both); one
+// elsewhere (measured: the reverse networks lose more to occupancy than they gain)
+constexpr int tiles_per_wave(int H, int mode) { return (mode == kForward && H == 64) ? 2 : 1; }
 constexpr int kBf16Tiles = 2;   // atom tiles per wave of the bf16 networks (measured: 1 and 4 slower)
 
-NetArgs make_args(Context &cx, int t) {
+NetArgs make_args(Context &cx, int t, int mode) {
     NetArgs a{};
     a.W = cx.weights.as<float>() + (int64_t)t * cx.S * cx.net.stride;
     a.W64 = cx.precision == 1 ? cx.weights64.as<double>() + (int64_t)t * cx.S * cx.net.stride : nullptr;
@@ -680,7 +680,7 @@ NetArgs make_args(Context &cx, int t) {
     a.ob1 = cx.net.b1; a.ob2 = cx.net.b2; a.ob3 = cx.net.b3;
     a.S = cx.S;
     a.sp_list = cx.sp_list.as<int32_t>();
-    const int per = 16 * (cx.precision == 0 ? tiles_per_wave(cx.H) : cx.precision == 2 ? kBf16Tiles : 1);
+    const int per = 16 * (cx.precision == 0 ? tiles_per_wave(cx.H, mode) : cx.precision == 2 ? kBf16Tiles : 1);
     int64_t off = 0;
     int32_t tiles = 0;
     for (int s = 0; s <= cx.S; ++s) {
@@ -703,7 +703,7 @@ NetArgs make_args(Context &cx, int t) {
     do {                                                                                         \
         if (cx.precision == 1) k_net64<K_, L_, H_, MODE_><<<tiles, 64, 0, cx.stream>>>(A_);     \
         else if (cx.precision == 2) k_net16<K_, L_, H_, MODE_, kBf16Tiles><<<tiles, 64, 0, cx.stream>>>(A_); \
-        else k_net<K_, L_, H_, MODE_, tiles_per_wave(H_)><<<tiles, 64, 0, cx.stream>>>(A_);      \
+        else k_net<K_, L_, H_, MODE_, tiles_per_wave(H_, MODE_)><<<tiles, 64, 0, cx.stream>>>(A_); \
     } while (0)
 
 #define MPNN_DISPATCH_NET(MODE_, A_)                                                                    \
@@ -863,7 +863,7 @@ Status pack_weights(Context &cx, const double *mlp) {
 
 Status mlp_forward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetForward);
-    NetArgs a = make_args(cx, t);
+    NetArgs a = make_args(cx, t, kForward);
     a.c_next = cx.c.as<float>() + (int64_t)(t + 1) * cx.NN * rec_stride(cx.K) + kRecC;
     MPNN_DISPATCH_NET(kForward, a);
     return Status::ok();
@@ -871,7 +871,7 @@ Status mlp_forward(Context &cx, int t) {
 
 Status mlp_energy(Context &cx) {
     ProfScope ps_(cx, kProfNetEnergy);
-    NetArgs a = make_args(cx, cx.T - 1);
+    NetArgs a = make_args(cx, cx.T - 1, kEnergy);
     a.Ei = cx.Ei.as<float>();
     MPNN_DISPATCH_NET(kEnergy, a);
     return Status::ok();
@@ -879,7 +879,7 @@ Status mlp_energy(Context &cx) {
 
 Status mlp_backward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetBackward);
-    NetArgs a = make_args(cx, t);
+    NetArgs a = make_args(cx, t, kBackward);
     a.Gc = cx.Gc.as<float>() + (int64_t)(t + 1) * cx.NN * cx.K;
     MPNN_DISPATCH_NET(kBackward, a);
     return Status::ok();
