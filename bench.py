@@ -397,7 +397,9 @@ def main():
         "roofline": roof,
         "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,
         "md": {"epot_start": E0, "epot_end": st["epot"], "ekin_end": st["ekin"],
-               "temp_end": st["temp"], "steps_total": st["steps"]},
+               "temp_end": st["temp"], "steps_total": st["steps"],
+               # neighbour rebuilds among the profiled steps (scheduled or displacement-triggered)
+               "rebuilds_profiled": kernels.get("build_rows", {}).get("launches", 0) if kernels else None},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

@@ -47,8 +47,16 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    # a stand-alone C++ user of the C ABI (no Python), linked against the library
+    drv = os.path.join(HERE, "abi_driver")
+    cmd = [HIPCC, "-O2", "-std=c++17", "--offload-arch=gfx950", "-I" + os.path.join(ROOT, "include"),
+           os.path.join(HERE, "abi_driver.cpp"), "-L" + HERE, "-lmpnn", "-Wl,-rpath,$ORIGIN", "-o", drv + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"abi_driver build failed:\n{r.stderr}")
+    os.replace(drv + ".tmp", drv)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", drv)
     return LIB
 
 
