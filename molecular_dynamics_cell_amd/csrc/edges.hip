@@ -88,10 +88,12 @@ struct Basis {
 // one exponential E = exp(delta d / s^2) times 1 + (delta_k - delta) d / s^2 (the next term is below
 // 1e-11), so an edge needs two fp64 exponentials.  The cutoff is cos^2(pi d / (2 rc)) from the
 // Taylor series of cos to the t^18 term (truncation below 1e-14 on [0, pi/2]).
-template <int K, int L, typename S = float>
+// K0, KB: only the radial channels K0 .. K0 + KB - 1 (the chain starts from a direct
+// exponential at mu_K0).
+template <int K, int L, typename S = float, int K0 = 0, int KB = K>
 struct BasisHP {
     static constexpr int M = n_mono(L);
-    S P[K];  // c_k R_k f_c
+    S P[KB];  // c_k R_k f_c, k = K0 + index
     S A[M];
 
     __device__ __forceinline__ void eval(double dx, double dy, double dz, const float *__restrict__ cv,
@@ -110,13 +112,14 @@ struct BasisHP {
         cs = fma(cs, t2, -0.5);
         cs = fma(cs, t2, 1.0);
         const double fc = cs * cs;
-        const double x0 = d - md->mu64[0];
+        const double x0 = d - md->mu64[K0];
         double R = exp(md->g_a0 * x0 * x0);
         const double E = exp(md->g_e * d);
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-            P[k] = (S)((double)cv[k] * R * fc);
-            if (k + 1 < K) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
+        for (int j = 0; j < KB; ++j) {
+            const int k = K0 + j;
+            P[j] = (S)((double)cv[k] * R * fc);
+            if (j + 1 < KB) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
         }
         const double ux = dx * md->inv_rc64, uy = dy * md->inv_rc64, uz = dz * md->inv_rc64;
         double px[L + 1], py[L + 1], pz[L + 1];
@@ -384,14 +387,14 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L, double> b;
+            BasisHP<K, L, double, P * KB, KB> b;   // this pass's radial channels only
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
             const double *pv = reinterpret_cast<const double *>(rv);
             b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
 #pragma unroll
             for (int k = 0; k < KB; ++k)
 #pragma unroll
-                for (int m = 0; m < M; ++m) acc[k][m] = fma(b.P[P * KB + k], b.A[m], acc[k][m]);
+                for (int m = 0; m < M; ++m) acc[k][m] = fma(b.P[k], b.A[m], acc[k][m]);
         }
     }
 #pragma unroll
