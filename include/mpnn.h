@@ -100,10 +100,13 @@ typedef struct {
 
 typedef struct {
     int64_t n_local;            /* atoms */
-    int64_t n_ghost;            /* periodic-image ghosts in the shell of width rc + skin */
+    int64_t n_ghost;            /* ghost images in the shell(s) of width rc + skin */
     int64_t n_edges;            /* Verlet-list entries (d < rc + skin), receivers local */
-    int64_t cells[3];           /* interior cells per axis (side >= rc + skin) */
+    int64_t cells[3];           /* interior cells per axis of one subdomain (side >= rc + skin) */
     int64_t bytes_device;       /* device memory held by the context */
+    int64_t row_bucketing;      /* 1: the neighbour slabs are less than 90 % full (ragged rows), so
+                                   every step the row kernels take each 256-row block's rows in
+                                   descending active count; 0: in order */
 } mpnn_info;
 
 /* Validates and copies the parameters, uploads the weights in the matrix-core layout.

@@ -114,7 +114,7 @@ void Context::release(Buf &b) {
 
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
-    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
+    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
@@ -623,6 +623,7 @@ mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info) {
     info->n_edges = cx.E;
     for (int a = 0; a < 3; ++a) info->cells[a] = cx.nc[a];
     info->bytes_device = (int64_t)cx.device_bytes;
+    info->row_bucketing = cx.bucket ? 1 : 0;
     return mpnn::finish(ctx, Status::ok());
 }
 

@@ -163,9 +163,10 @@ __device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], flo
 // One 16-column tile of the block's 256 rows: thread t holds the 16 values of row i0 + t; the
 // tile is staged through LDS (rows padded to 80 bytes) and written as one contiguous 16 KB run,
 // 1 KB per store instruction.  All threads of the block call it.
-__device__ __forceinline__ void store_tile(const float (&v)[16], float4 *__restrict__ lds, float *__restrict__ dst) {
+__device__ __forceinline__ void store_tile(const float (&v)[16], float4 *__restrict__ lds, float *__restrict__ dst,
+                                           int slot) {
     const int t = threadIdx.x;
-    float4 *row = lds + 5 * t;
+    float4 *row = lds + 5 * slot;   // the row's place in the block (rows may be held out of order)
     row[0] = float4{v[0], v[1], v[2], v[3]};
     row[1] = float4{v[4], v[5], v[6], v[7]};
     row[2] = float4{v[8], v[9], v[10], v[11]};
@@ -181,7 +182,7 @@ __device__ __forceinline__ void store_tile(const float (&v)[16], float4 *__restr
 }
 
 template <int K, int L, int KT>
-__device__ __forceinline__ void store_o_tile(const float (&O)[K][n_mono(L)], float4 *lds, float *dst) {
+__device__ __forceinline__ void store_o_tile(const float (&O)[K][n_mono(L)], float4 *lds, float *dst, int slot) {
     constexpr int M = n_mono(L);
     float v[16];
 #pragma unroll
@@ -189,26 +190,27 @@ __device__ __forceinline__ void store_o_tile(const float (&O)[K][n_mono(L)], flo
         const int q = 16 * KT + j;
         v[j] = q < K * M ? O[q / M][q % M] : 0.0f;
     }
-    store_tile(v, lds, dst);
+    store_tile(v, lds, dst, slot);
 }
 
 template <int K, int L, int... KT>
 __device__ __forceinline__ void store_o_rows(const float (&O)[K][n_mono(L)], float4 *lds, float *base, int64_t np,
-                                             std::integer_sequence<int, KT...>) {
-    (store_o_tile<K, L, KT>(O, lds, base + (int64_t)KT * np * 16), ...);
+                                             int slot, std::integer_sequence<int, KT...>) {
+    (store_o_tile<K, L, KT>(O, lds, base + (int64_t)KT * np * 16, slot), ...);
 }
 
 template <int K, int L, int KT>
-__device__ __forceinline__ void store_feature_tile(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *dst) {
+__device__ __forceinline__ void store_feature_tile(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *dst,
+                                                   int slot) {
     float v[16];
     feature_tile<K, L, KT>(O, s, v, std::make_integer_sequence<int, 16>{});
-    store_tile(v, lds, dst);
+    store_tile(v, lds, dst, slot);
 }
 
 template <int K, int L, int... KT>
 __device__ __forceinline__ void store_feature_rows(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *base,
-                                                   int64_t np, std::integer_sequence<int, KT...>) {
-    (store_feature_tile<K, L, KT>(O, s, lds, base + (int64_t)KT * np * 16), ...);
+                                                   int64_t np, int slot, std::integer_sequence<int, KT...>) {
+    (store_feature_tile<K, L, KT>(O, s, lds, base + (int64_t)KT * np * 16, slot), ...);
 }
 
 // Chain rule through the features: dE/dO[c,m] = w_m sum_b (1 + [b == c]) dE/drho[(b,c), l_m] O[b,m],
@@ -255,15 +257,20 @@ __device__ __forceinline__ void assemble_go_row(const float *__restrict__ grho, 
 // first uses the fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of
 // the fp64 value (a bound from the coordinate range, see compact_active), so only entries inside
 // rc^2 -/+ band, a vanishing fraction, repeat it in fp64.
-__global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
-                                                 const float4 *__restrict__ pos32,
-                                                 const int64_t *__restrict__ slab_off,
-                                                 const int32_t *__restrict__ len,
-                                                 const int32_t *__restrict__ nbr, double rc2, float lo, float hi,
-                                                 uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
-                                                 int32_t *__restrict__ nact) {
-    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
-    if (i >= n) return;
+// Row taken by this thread of a 256-row block starting at i0: with row bucketing (row_perm set),
+// the block's rows in descending active count, else in order; positions past the last row keep
+// their own index, which the caller skips.
+__device__ __forceinline__ int64_t block_row(int64_t i0, int64_t n, const int32_t *__restrict__ row_perm) {
+    const int64_t i = i0 + threadIdx.x;
+    return (row_perm && i < n) ? (int64_t)row_perm[i] : i;
+}
+
+// Compaction of row i (see k_compact below); returns its active count.
+__device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *__restrict__ pos,
+                                           const float4 *__restrict__ pos32, const int64_t *__restrict__ slab_off,
+                                           const int32_t *__restrict__ len, const int32_t *__restrict__ nbr,
+                                           double rc2, float lo, float hi, uint32_t *__restrict__ amask,
+                                           int32_t *__restrict__ act_n) {
     const float4 pi = pos32[i];
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
@@ -302,7 +309,34 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
             }
         }
     }
-    nact[i] = o;
+    return o;
+}
+
+__global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
+                                                 const float4 *__restrict__ pos32,
+                                                 const int64_t *__restrict__ slab_off,
+                                                 const int32_t *__restrict__ len,
+                                                 const int32_t *__restrict__ nbr, double rc2, float lo, float hi,
+                                                 uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
+                                                 int32_t *__restrict__ nact, int32_t *__restrict__ row_perm) {
+    const int64_t i0 = xcd_block() * blockDim.x, i = i0 + threadIdx.x;
+    const int na = i < n ? compact_row(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n) : -1;
+    if (i < n) nact[i] = na;
+    if (row_perm) {
+        // the block's rows by descending active count (ties by row), so the waves of the row
+        // kernels take rows of similar length; rank = rows that come before this one
+        __shared__ int32_t cnt[kBlock];
+        cnt[threadIdx.x] = na;
+        __syncthreads();
+        if (i < n) {
+            int r = 0;
+            for (int j = 0; j < kBlock; ++j) {
+                const int x = cnt[j];
+                r += (x > na) || (x == na && j < (int)threadIdx.x);
+            }
+            row_perm[i0 + r] = (int32_t)i;
+        }
+    }
 }
 
 // Active slot of Verlet slot e of receiver row i this step (-1: d >= rc): the row's slab base
@@ -327,12 +361,13 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
                                                    const int32_t *__restrict__ nact,
                                                    const int32_t *__restrict__ act_n, const float *__restrict__ c,
                                                    const ModelDev *__restrict__ md, float inv_scale,
+                                                   const int32_t *__restrict__ row_perm,
                                                    float *__restrict__ O, float *__restrict__ feat) {
     constexpr int M = n_mono(L), KMT = pad16(K * M) / 16, DT = pad16(n_feat(K, L)) / 16;
     __shared__ float4 lds[5 * kBlock];
     const int64_t i0 = xcd_block() * kBlock;
     if (i0 >= n) return;                       // whole block past the end (grid rounded to 8 XCDs)
-    const int64_t i = i0 + threadIdx.x;
+    const int64_t i = block_row(i0, n, row_perm);
     float acc[K][M];
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -355,8 +390,9 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         }
     }
     // rows n..np-1 of the last block are padding: written, never read
-    store_o_rows<K, L>(acc, lds, O + i0 * 16, np, std::make_integer_sequence<int, KMT>{});
-    store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, std::make_integer_sequence<int, DT>{});
+    store_o_rows<K, L>(acc, lds, O + i0 * 16, np, (int)(i - i0), std::make_integer_sequence<int, KMT>{});
+    store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, (int)(i - i0),
+                             std::make_integer_sequence<int, DT>{});
 }
 
 // Orbital sums in fp64 (the accurate mode): channels k in [P KB, (P+1) KB) of O^t_i, with the
@@ -368,14 +404,15 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
                                                      const int64_t *__restrict__ slab_off,
                                                      const int32_t *__restrict__ nact,
                                                      const int32_t *__restrict__ act_n, const float *__restrict__ c,
-                                                     const ModelDev *__restrict__ md, float *__restrict__ O) {
+                                                     const ModelDev *__restrict__ md,
+                                                     const int32_t *__restrict__ row_perm, float *__restrict__ O) {
     constexpr int M = n_mono(L), Q0 = P * KB * M;
     constexpr int T0 = Q0 / 16, T1 = (KB == K ? pad16(K * M) : Q0 + KB * M) / 16;
     static_assert(KB == K || (KB * M) % 16 == 0, "a pass must own whole 16-column tiles");
     __shared__ float4 lds[5 * kBlock];
     const int64_t i0 = xcd_block() * kBlock;
     if (i0 >= n) return;
-    const int64_t i = i0 + threadIdx.x;
+    const int64_t i = block_row(i0, n, row_perm);
     double acc[KB][M];
 #pragma unroll
     for (int k = 0; k < KB; ++k)
@@ -405,7 +442,7 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
             const int q = 16 * kt + j - Q0;
             v[j] = (q < KB * M && P * KB + q / M < K) ? (float)acc[q / M][q % M] : 0.0f;
         }
-        store_tile(v, lds, O + (int64_t)kt * np * 16 + i0 * 16);
+        store_tile(v, lds, O + (int64_t)kt * np * 16 + i0 * 16, (int)(i - i0));
     }
 }
 
@@ -423,7 +460,8 @@ __global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const f
     for (int k = 0; k < K; ++k)
 #pragma unroll
         for (int m = 0; m < M; ++m) o[k][m] = O[tiled(np, i, k * M + m)];
-    store_feature_rows<K, L>(o, inv_scale, lds, feat + i0 * 16, np, std::make_integer_sequence<int, DT>{});
+    store_feature_rows<K, L>(o, inv_scale, lds, feat + i0 * 16, np, (int)threadIdx.x,
+                             std::make_integer_sequence<int, DT>{});
 }
 
 // Reverse pass of layer t over one receiver row per thread (Eq. 4 as a VJP), with
@@ -439,11 +477,12 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
                                                         const int32_t *__restrict__ act_n, const float *__restrict__ c,
                                                         const float *__restrict__ Grho, const float *__restrict__ Ot,
                                                         const ModelDev *__restrict__ md,
+                                                        const int32_t *__restrict__ row_perm,
                                                         float *__restrict__ w, float *__restrict__ gedge,
                                                         double *__restrict__ Frecv) {
     constexpr int M = n_mono(L);
     constexpr Mono<L> mono;
-    const int64_t i = xcd_block() * blockDim.x + threadIdx.x;
+    const int64_t i = block_row(xcd_block() * blockDim.x, n, row_perm);
     if (i >= n) return;
     float mu[K];
 #pragma unroll
@@ -664,6 +703,8 @@ __global__ __launch_bounds__(256) void k_assemble_go(int64_t n, int64_t np, cons
         for (int m = 0; m < M; ++m) out[i * (K * M) + k * M + m] = G[k][m];
 }
 
+const int32_t *row_perm(const Context &cx) { return cx.bucket ? cx.row_perm.as<int32_t>() : nullptr; }
+
 #define MPNN_DISPATCH_KL(K_, L_, CALL)                                                 \
     do {                                                                               \
         if ((K_) == 8 && (L_) == 2) { constexpr int KK = 8, LL = 2; CALL; }            \
@@ -690,7 +731,8 @@ Status compact_active(Context &cx) {
     k_compact<<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(),
                                                         cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
                                                         cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(),
-                                                        cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
+                                                        cx.act_n.as<int32_t>(), cx.nact.as<int32_t>(),
+                                                        cx.bucket ? cx.row_perm.as<int32_t>() : nullptr);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
@@ -705,14 +747,14 @@ Status aggregate(Context &cx, int t) {
         MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
                                           cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
                                           cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(),
-                                          cx.inv_scale_host[t], Ot, Ft)));
+                                          cx.inv_scale_host[t], row_perm(cx), Ot, Ft)));
         MPNN_HIP(hipGetLastError());
         return Status::ok();
     }
 #define MPNN_AGG64(KK, LL, KB, P)                                                                               \
     k_aggregate64<KK, LL, KB, P><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                                     \
         cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), \
-        ct, cx.model.as<ModelDev>(), Ot)
+        ct, cx.model.as<ModelDev>(), row_perm(cx), Ot)
     if (cx.K == 12 && cx.L == 3) {
         MPNN_AGG64(12, 3, 4, 0);
         MPNN_AGG64(12, 3, 4, 1);
@@ -754,7 +796,7 @@ Status backward_layer(Context &cx, int t) {
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
-                                      cx.model.as<ModelDev>(), cx.w.as<float>(), cx.gedge.as<float>(),             \
+                                      cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
                                       cx.Frecv.as<double>())))
     if (first && want_w) MPNN_BWD(true, true);
     else if (first) MPNN_BWD(true, false);

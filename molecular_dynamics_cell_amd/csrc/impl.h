@@ -120,6 +120,8 @@ struct Context {
     Buf act_n;    // int32 [E]: sender node of each active slot
     Buf t_act;    // int32 [E]: active slot of each transposed entry this step (-1: d >= rc)
     Buf nact;     // int32 [n] active entries per row
+    Buf row_perm; // int32 [n]: per 256-row block, its rows by descending active count (bucketing)
+    bool bucket = false;   // row kernels take rows in row_perm order (ragged row lengths)
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
     Buf Ei;       // float [n]

@@ -620,9 +620,15 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
             MPNN_HIP(hipMemcpyAsync(widths.data(), cnt, sizeof(int32_t) * nslab, hipMemcpyDeviceToHost, cx.stream));
             MPNN_HIP(hipStreamSynchronize(cx.stream));
         }
-        int64_t longest = 0;
-        for (int32_t w : widths) longest = std::max<int64_t>(longest, w / kSlab);
+        int64_t longest = 0, slots = 0;
+        for (int32_t w : widths) {
+            longest = std::max<int64_t>(longest, w / kSlab);
+            slots += w;
+        }
         cx.mw = (int)std::max<int64_t>(1, (longest + 31) / 32);
+        // ragged rows (slabs less than 90 % full, e.g. a gas with clusters): the row kernels take
+        // each block's rows by descending active count, so a wave's rows have similar lengths
+        cx.bucket = slots > 0 && (double)E < 0.9 * (double)slots;
     }
     MPNN_TRY(exclusive_scan(cx, cnt, nslab, cx.slab_off.as<int64_t>()));
     int64_t Es = 0;
@@ -706,6 +712,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
+    MPNN_TRY(cx.grow(cx.row_perm, sizeof(int32_t) * n1));
     if (cx.T > 1) MPNN_TRY(cx.grow(cx.w, sizeof(float) * (size_t)E1 * cx.K));
     MPNN_TRY(cx.grow(cx.Frecv, sizeof(double) * 3 * n1));
     MPNN_TRY(cx.grow(cx.F, sizeof(double) * 3 * n1));
