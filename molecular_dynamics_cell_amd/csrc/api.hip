@@ -199,6 +199,8 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     if (p->precision == 2 && (p->hidden != 64 || mpnn::n_feat(p->K, p->L) > 128)) return MPNN_E_INVALID_ARG;
     for (int t = 0; t < p->T; ++t)
         if (!(p->layer_scale[t] > 0) || !std::isfinite(p->layer_scale[t])) return MPNN_E_INVALID_ARG;
+    for (int k = 0; k < p->K; ++k)
+        if (!std::isfinite(p->mu[k])) return MPNN_E_INVALID_ARG;
     mpnn_ctx *ctx = new (std::nothrow) mpnn_ctx;
     if (!ctx) return MPNN_E_OOM;
     mpnn::Context &cx = ctx->cx;
@@ -237,11 +239,22 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
         md.g_a0 = -1.0 / (2.0 * s2);
         const double delta = cx.K > 1 ? p->mu[1] - p->mu[0] : 0.0;
         md.g_e = delta / s2;
+        // the chain R_{k+1} = R_k E g_c[k] (1 + g_eps[k] d) replaces exp(g_eps[k] d) by its first
+        // two terms, so it needs |g_eps[k]| rc below 2e-5 (the dropped terms stay under 2e-10
+        // relative; evenly spaced centres stored in fp32 give about 4e-6), and
+        // E = exp(delta rc / sigma^2), R_0 = exp(-(rc - mu_0)^2 / (2 sigma^2)) must stay inside the
+        // fp64 range; otherwise every channel is evaluated directly
+        bool chain = true;
         for (int k = 0; k + 1 < cx.K; ++k) {
             const double dk = p->mu[k + 1] - p->mu[k];
             md.g_c[k] = std::exp(-dk * (p->mu[k] + p->mu[k + 1]) / (2.0 * s2));
             md.g_eps[k] = (dk - delta) / s2;
+            chain = chain && std::fabs(md.g_eps[k]) * p->rc < 2e-5 && std::isfinite(md.g_c[k]) && md.g_c[k] > 0.0;
         }
+        double span = 0.0;
+        for (int k = 0; k < cx.K; ++k) span = std::max(span, std::fabs(p->rc - p->mu[k]) + std::fabs(p->mu[k]));
+        chain = chain && std::fabs(md.g_e) * p->rc < 600.0 && span * span / (2.0 * s2) < 600.0;
+        cx.chain = chain;
         md.inv_rc64 = 1.0 / p->rc;
         md.half_pi_over_rc = 0.5 * mpnn::kPi / p->rc;
     }

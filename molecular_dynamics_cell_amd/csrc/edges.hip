@@ -86,11 +86,12 @@ struct Basis {
 // neighbouring centres, R_{k+1} / R_k = exp(delta_k d / s^2) exp(-delta_k (mu_k + mu_{k+1}) / (2 s^2))
 // with delta_k = mu_{k+1} - mu_k; writing delta_k = delta + (delta_k - delta), the first factor is
 // one exponential E = exp(delta d / s^2) times 1 + (delta_k - delta) d / s^2 (the next term is below
-// 1e-11), so an edge needs two fp64 exponentials.  The cutoff is cos^2(pi d / (2 rc)) from the
+// 2e-10 where the chain is used), so an edge needs two fp64 exponentials.  Centres too uneven or
+// widths too narrow for it (see the model set-up) take one exponential per channel (CHAIN false).  The cutoff is cos^2(pi d / (2 rc)) from the
 // Taylor series of cos to the t^18 term (truncation below 1e-14 on [0, pi/2]).
 // K0, KB: only the radial channels K0 .. K0 + KB - 1 (the chain starts from a direct
 // exponential at mu_K0).
-template <int K, int L, typename S = float, int K0 = 0, int KB = K>
+template <int K, int L, typename S = float, int K0 = 0, int KB = K, bool CHAIN = true>
 struct BasisHP {
     static constexpr int M = n_mono(L);
     S P[KB];  // c_k R_k f_c, k = K0 + index
@@ -112,14 +113,24 @@ struct BasisHP {
         cs = fma(cs, t2, -0.5);
         cs = fma(cs, t2, 1.0);
         const double fc = cs * cs;
-        const double x0 = d - md->mu64[K0];
-        double R = exp(md->g_a0 * x0 * x0);
-        const double E = exp(md->g_e * d);
+        if constexpr (CHAIN) {
+            const double x0 = d - md->mu64[K0];
+            double R = exp(md->g_a0 * x0 * x0);
+            const double E = exp(md->g_e * d);
 #pragma unroll
-        for (int j = 0; j < KB; ++j) {
-            const int k = K0 + j;
-            P[j] = (S)((double)cv[k] * R * fc);
-            if (j + 1 < KB) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
+            for (int j = 0; j < KB; ++j) {
+                const int k = K0 + j;
+                P[j] = (S)((double)cv[k] * R * fc);
+                if (j + 1 < KB) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
+            }
+        } else {
+            // centres too uneven or widths too narrow for the chain: one exponential per channel
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int k = K0 + j;
+                const double x = d - md->mu64[k];
+                P[j] = (S)((double)cv[k] * exp(md->g_a0 * x * x) * fc);
+            }
         }
         const double ux = dx * md->inv_rc64, uy = dy * md->inv_rc64, uz = dz * md->inv_rc64;
         double px[L + 1], py[L + 1], pz[L + 1];
@@ -355,7 +366,7 @@ __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64
 
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
 // atom's density features from it; both leave through LDS-staged, column-tiled stores.
-template <int K, int L>
+template <int K, int L, bool CHAIN>
 __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
@@ -379,7 +390,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L> b;
+            BasisHP<K, L, float, 0, K, CHAIN> b;
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
             const double *pv = reinterpret_cast<const double *>(rv);
             b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
@@ -399,7 +410,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
 // basis factors and their products kept in fp64 and one rounding when O is stored.  The K = 12,
 // L = 3 orbital block is too large for fp64 registers in one pass, so it takes several passes over
 // the edges (KB M a multiple of 16, so each pass owns whole 16-column tiles of the O rows).
-template <int K, int L, int KB, int P>
+template <int K, int L, int KB, int P, bool CHAIN>
 __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, const double *__restrict__ pos,
                                                      const int64_t *__restrict__ slab_off,
                                                      const int32_t *__restrict__ nact,
@@ -424,7 +435,7 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L, double, P * KB, KB> b;   // this pass's radial channels only
+            BasisHP<K, L, double, P * KB, KB, CHAIN> b;   // this pass's radial channels only
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
             const double *pv = reinterpret_cast<const double *>(rv);
             b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
@@ -744,17 +755,26 @@ Status aggregate(Context &cx, int t) {
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
-        MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
-                                          cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),
-                                          cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(),
-                                          cx.inv_scale_host[t], row_perm(cx), Ot, Ft)));
+#define MPNN_AGG32(CH)                                                                                          \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(             \
+                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
+                                      cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
+                                      cx.inv_scale_host[t], row_perm(cx), Ot, Ft)))
+        if (cx.chain) MPNN_AGG32(true);
+        else MPNN_AGG32(false);
+#undef MPNN_AGG32
         MPNN_HIP(hipGetLastError());
         return Status::ok();
     }
 #define MPNN_AGG64(KK, LL, KB, P)                                                                               \
-    k_aggregate64<KK, LL, KB, P><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                                     \
-        cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), \
-        ct, cx.model.as<ModelDev>(), row_perm(cx), Ot)
+    if (cx.chain)                                                                                               \
+        k_aggregate64<KK, LL, KB, P, true><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                           \
+            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),                 \
+            cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), row_perm(cx), Ot);                             \
+    else                                                                                                        \
+        k_aggregate64<KK, LL, KB, P, false><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                          \
+            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),                 \
+            cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), row_perm(cx), Ot)
     if (cx.K == 12 && cx.L == 3) {
         MPNN_AGG64(12, 3, 4, 0);
         MPNN_AGG64(12, 3, 4, 1);

@@ -102,3 +102,20 @@ def test_permutation_of_input_order():
     E1, F1, _ = gpu_model(p, s).energy_forces()
     E2, F2, _ = gpu_model(p, s2).energy_forces()
     check_ef(E2, F2.cpu().numpy(), E1, F1.cpu().numpy()[perm], label="permuted input")
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_uneven_centres(precision):
+    """Radial centres that are not evenly spaced: the aggregation evaluates every channel as its
+    own exponential instead of the ratio chain; energies and forces still match the oracle."""
+    s = systems.ag(6, seed=9)
+    p = I.make_params(4)
+    p.spec.precision = precision
+    k = np.arange(p.spec.K)
+    p.mu = np.asarray(p.mu, np.float64) + 0.08 * np.sin(1.7 * k + 0.3)   # uneven, inside [0, rc]
+    p.mu[0] = max(p.mu[0], 0.0)
+    say(f"[uneven] centres {np.round(p.mu, 3).tolist()} precision {precision}")
+    m = gpu_model(p, s)
+    E, F, _ = m.energy_forces()
+    Eo, Fo, _ = oracle_ef(p, s)
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"uneven centres, precision {precision}")
