@@ -249,6 +249,7 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
             const double dk = p->mu[k + 1] - p->mu[k];
             md.g_c[k] = std::exp(-dk * (p->mu[k] + p->mu[k + 1]) / (2.0 * s2));
             md.g_eps[k] = (dk - delta) / s2;
+            md.g_ce[k] = md.g_c[k] * md.g_eps[k];
             chain = chain && std::fabs(md.g_eps[k]) * p->rc < 2e-5 && std::isfinite(md.g_c[k]) && md.g_c[k] > 0.0;
         }
         double span = 0.0;

@@ -165,6 +165,7 @@ struct ModelDev {
     double g_e;             // delta / sigma^2, delta = mu_1 - mu_0
     double g_c[16];         // exp(-delta_k (mu_k + mu_{k+1}) / (2 sigma^2)), delta_k = mu_{k+1} - mu_k
     double g_eps[16];       // (delta_k - delta) / sigma^2
+    double g_ce[16];        // g_c[k] g_eps[k]
     double inv_rc64;        // 1 / rc
     double half_pi_over_rc; // pi / (2 rc)
 };

@@ -80,6 +80,29 @@ struct Basis {
     }
 };
 
+// e^x in fp64 for x <= 709: x = n ln 2 + r with ln 2 in two parts (Cody and Waite), so r is exact
+// to rounding and |r| <= ln 2 / 2; e^r from its Taylor series to r^11 (truncation below 7e-15
+// relative), scaled by 2^n.  Arguments below -745 give 0 (the fp64 result underflows there).
+__device__ __forceinline__ double exp_fp64(double x) {
+    x = fmax(x, -745.0);
+    const double n = rint(x * 1.4426950408889634);
+    double r = fma(n, -6.93147180369123816490e-01, x);
+    r = fma(n, -1.90821492927058770002e-10, r);
+    double p = 1.0 / 39916800.0;          // 1/11!
+    p = fma(p, r, 1.0 / 3628800.0);       // 1/10!
+    p = fma(p, r, 1.0 / 362880.0);
+    p = fma(p, r, 1.0 / 40320.0);
+    p = fma(p, r, 1.0 / 5040.0);
+    p = fma(p, r, 1.0 / 720.0);
+    p = fma(p, r, 1.0 / 120.0);
+    p = fma(p, r, 1.0 / 24.0);
+    p = fma(p, r, 1.0 / 6.0);
+    p = fma(p, r, 0.5);
+    p = fma(p, r, 1.0);
+    p = fma(p, r, 1.0);
+    return ldexp(p, (int)n);
+}
+
 // Aggregation factors accurate to about half an fp32 ulp each, so that every product
 // c_k R_k f_c A_m entering an orbital sum carries a single rounding: the Gaussians, the cutoff and
 // the monomials are evaluated in fp64 and rounded once.  The Gaussians follow from the ratio of
@@ -114,14 +137,15 @@ struct BasisHP {
         cs = fma(cs, t2, 1.0);
         const double fc = cs * cs;
         if constexpr (CHAIN) {
+            // the chain runs on R_k f_c: P_k = c_k (R_k f_c), next = this E (g_c + g_c g_eps d)
             const double x0 = d - md->mu64[K0];
-            double R = exp(md->g_a0 * x0 * x0);
-            const double E = exp(md->g_e * d);
+            double Rf = exp_fp64(md->g_a0 * x0 * x0) * fc;
+            const double E = exp_fp64(md->g_e * d);
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
                 const int k = K0 + j;
-                P[j] = (S)((double)cv[k] * R * fc);
-                if (j + 1 < KB) R *= E * md->g_c[k] * fma(md->g_eps[k], d, 1.0);
+                P[j] = (S)((double)cv[k] * Rf);
+                if (j + 1 < KB) Rf *= E * fma(md->g_ce[k], d, md->g_c[k]);
             }
         } else {
             // centres too uneven or widths too narrow for the chain: one exponential per channel
