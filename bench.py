@@ -372,6 +372,14 @@ def main():
     if modeled:
         dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
         roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg, p.spec.precision)
+        if roof["bound"] == "hbm" and not args.no_profile:
+            # context: the measured HBM rate of this kernel next to a plain device copy's on this GPU
+            copy = bandwidth(gib=2, reps=5)["copy_read_plus_write"]
+            roof["copy_rate_GBs"] = copy
+            if roof.get("traffic"):
+                rate = roof["traffic"] / (roof["avg_ms"] * 1e-3) / 1e9
+                roof["traffic_GBs"] = round(rate, 1)
+                roof["traffic_frac_of_copy"] = round(rate / copy, 4)
     for k in modeled:
         kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg, p.spec.precision)
 
