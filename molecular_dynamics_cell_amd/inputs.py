@@ -21,6 +21,7 @@ atomic networks per element).  Unit system: A, eV, fs, amu.
 """
 from __future__ import annotations
 
+import dataclasses
 import json
 import os
 from dataclasses import dataclass, field
@@ -78,6 +79,7 @@ class Params:
     layer_scale: np.ndarray    # [T]
     e_scale: float
     masses: np.ndarray         # [S]
+    contraction: np.ndarray = None   # [K][K] contraction of the radial primitives, or None
 
     @property
     def D(self) -> int:
@@ -343,6 +345,20 @@ def random_params(spec: ModelSpec, seed: int, masses, layer_scale=None, e_scale:
         layer_scale = np.ones(T)
     return Params(spec, mu, c0, mlp, np.asarray(layer_scale, np.float64), float(e_scale),
                   np.asarray(masses, np.float64))
+
+
+def contraction_matrix(K: int, seed: int) -> np.ndarray:
+    """Random contraction of the K radial primitives into K orbitals: C[n][k] ~ N(0, 1/K),
+    rounded to float32 like every other drawn parameter."""
+    return _f32(_rng(seed).standard_normal((K, K)) / np.sqrt(K))
+
+
+def with_contraction(params: Params, C) -> Params:
+    """The same model with orbital n built from the radial function sum_k C[n][k] R_k."""
+    C = np.asarray(C, np.float64)
+    if C.shape != (params.spec.K, params.spec.K):
+        raise ValueError("contraction must be K x K")
+    return dataclasses.replace(params, contraction=C.copy())
 
 
 def load_scales() -> dict:

@@ -41,7 +41,7 @@ class _Model(C.Structure):
                 ("rc", C.c_double), ("sigma", C.c_double),
                 ("mu", C.POINTER(C.c_double)), ("c0", C.POINTER(C.c_double)),
                 ("mlp", C.POINTER(C.c_double)), ("layer_scale", C.POINTER(C.c_double)),
-                ("e_scale", C.c_double)]
+                ("e_scale", C.c_double), ("contraction", C.POINTER(C.c_double))]
 
 
 class _Dump(C.Structure):
@@ -95,10 +95,13 @@ class Model:
         self.M = (s.L + 1) * (s.L + 2) * (s.L + 3) // 6
         self.D = s.K * (s.K + 1) * (s.L + 1) // 2
         dp = C.POINTER(C.c_double)
+        self.contraction = (None if params.contraction is None else
+                            np.ascontiguousarray(params.contraction, np.float64).reshape(s.K, s.K))
         self.struct = _Model(s.n_species, s.K, s.L, s.T, s.H, s.rc, s.sigma,
                              self.mu.ctypes.data_as(dp), self.c0.ctypes.data_as(dp),
                              self.mlp.ctypes.data_as(dp), self.scale.ctypes.data_as(dp),
-                             float(params.e_scale))
+                             float(params.e_scale),
+                             None if self.contraction is None else self.contraction.ctypes.data_as(dp))
 
 
 def wrap(pos, box):

@@ -17,6 +17,11 @@
  *   over primitive pairs a <= b (dimension K(K+1)(L+1)/2 as the paper states);
  *   rho-tilde = rho / s_t; atomic networks D->H->H->out with SiLU, one per species and layer;
  *   E_i = e_scale * network output.
+ * Contraction variant (section "REANN Architecture": each neighbour orbital G_j is a
+ * contraction of the N_phi primitive Gaussian-type orbitals, its coefficients left to the
+ * supporting information): with a matrix C[K][K] shared by all species and layers, orbital n
+ * uses the radial function sum_k C[n][k] R_k(d); the element-wise coefficient c_j[n] then
+ * multiplies that contracted orbital.  C = identity is the base model.
  */
 #include "orc.h"
 
@@ -281,6 +286,22 @@ static void edge_basis(const ctx_t *c, const double r[3], double d, double *R, d
         double x = d - m->mu[k];
         R[k] = exp(-x * x / (2.0 * s2));
         if (dR) dR[k] = -x / s2 * R[k];
+    }
+    if (m->contraction) {   /* contracted radial functions and their derivatives */
+        double Rc[32], dRc[32];
+        for (int q = 0; q < c->K; ++q) {
+            double a = 0.0, b = 0.0;
+            for (int k = 0; k < c->K; ++k) {
+                a += m->contraction[q * c->K + k] * R[k];
+                if (dR) b += m->contraction[q * c->K + k] * dR[k];
+            }
+            Rc[q] = a;
+            dRc[q] = b;
+        }
+        for (int q = 0; q < c->K; ++q) {
+            R[q] = Rc[q];
+            if (dR) dR[q] = dRc[q];
+        }
     }
     *fc = 0.5 * (1.0 + cos(ORC_PI * d / m->rc));
     if (dfc) *dfc = -0.5 * ORC_PI / m->rc * sin(ORC_PI * d / m->rc);

@@ -30,6 +30,9 @@ typedef struct {
     const double *mlp;          /* for t, for s: W1[H][D] b1[H] W2[H][H] b2[H] W3[out][H] b3[out]; out = K (t<T-1) or 1 */
     const double *layer_scale;  /* [T] */
     double e_scale;
+    const double *contraction;  /* [K][K] or NULL.  Variant: every neighbour's orbital n uses the
+                                   contracted radial function sum_k C[n][k] R_k(d) in place of
+                                   R_n(d); NULL is the base model (C = identity). */
 } orc_model;
 
 /* Optional per-atom intermediates, each NULL or [T][n][...] (row-major). */

@@ -50,15 +50,19 @@ def test_feature_dimension_matches_paper(orc):
         assert dump["rho"].shape[-1] == D
 
 
-@pytest.mark.parametrize("cfg,make,t", [
-    (1, lambda: systems.ag(3), 0),
-    (1, lambda: systems.ag(3), 1),
-    (5, lambda: systems.water_molecules(12, 16.0), 2),   # K=12, L=3 model, 2 species used
+@pytest.mark.parametrize("cfg,make,t,contracted", [
+    (1, lambda: systems.ag(3), 0, False),
+    (1, lambda: systems.ag(3), 1, False),
+    (5, lambda: systems.water_molecules(12, 16.0), 2, False),   # K=12, L=3 model, 2 species used
+    (1, lambda: systems.ag(3), 1, True),
+    (5, lambda: systems.water_molecules(12, 16.0), 2, True),
 ])
-def test_multinomial_identity(orc, cfg, make, t):
+def test_multinomial_identity(orc, cfg, make, t, contracted):
     """rho[(a,b),l] = sum_{e,e'} P_a(e) P_b(e') ((r_e . r_e') / rc^2)^l."""
     s = make()
     p = systems.params_for(cfg)
+    if contracted:
+        p = I.with_contraction(p, I.contraction_matrix(p.spec.K, 500 + cfg))
     m = orc.Model(p)
     pos = orc.wrap(s.pos, s.box)
     pl = orc.pairs(pos, s.box, p.spec.rc + p.spec.skin)
@@ -72,6 +76,8 @@ def test_multinomial_identity(orc, cfg, make, t):
         sel = (pi == i) & act
         re, de = r[sel], d[sel]
         R = np.exp(-(de[:, None] - p.mu[None, :]) ** 2 / (2 * sig ** 2))
+        if contracted:
+            R = R @ p.contraction.T                             # [E][n] = sum_k C[n][k] R_k
         fc = 0.5 * (1 + np.cos(np.pi * de / rc))
         P = dump["c"][t][pj[sel]] * R * fc[:, None]          # [E][K]
         dots = (re @ re.T) / rc ** 2                          # [E][E]
@@ -91,6 +97,8 @@ def _dimer_energy(p, d, types, rc):
     """Closed form of the model for two atoms on the x axis at distance d (complex-safe)."""
     K, L, T = p.spec.K, p.spec.L, p.spec.T
     R = np.exp(-(d - p.mu) ** 2 / (2 * p.spec.sigma ** 2))
+    if p.contraction is not None:                     # orbital n: sum_k C[n][k] R_k
+        R = p.contraction @ R
     fc = 0.5 * (1 + np.cos(np.pi * d / rc))
     silu = lambda x: x / (1 + np.exp(-x))
     c = [p.c0[types[0]].astype(complex), p.c0[types[1]].astype(complex)]
@@ -134,6 +142,58 @@ def test_dimer_closed_form(orc, K, L, T, S):
         assert np.abs(F[:, 1:]).max() <= 1e-14
 
 
+@pytest.mark.parametrize("K,L,T,S", [(2, 1, 1, 2), (3, 2, 3, 2)])
+def test_dimer_closed_form_contracted(orc, K, L, T, S):
+    """The contraction variant: a non-symmetric C, so a transposed matrix fails."""
+    spec = I.ModelSpec(n_species=S, K=K, L=L, T=T, H=6, rc=4.0, skin=0.5)
+    p = I.random_params(spec, 91 + K + 10 * T, [1.0] * S, np.linspace(0.5, 1.5, T), 1.3)
+    C = I.contraction_matrix(K, 300 + K)
+    assert np.abs(C - C.T).max() > 0.1
+    p = I.with_contraction(p, C)
+    types = np.array([0, S - 1], np.int32)
+    box = np.array([40.0, 40.0, 40.0])
+    m = orc.Model(p)
+    for d in [1.1, 2.5, 3.9]:
+        pos = np.array([[10.0, 20.0, 20.0], [10.0 + d, 20.0, 20.0]])
+        E, F, _ = orc.energy_forces(m, pos, types, box)
+        Ecf = _dimer_energy(p, d, types, spec.rc).real
+        h = 1e-30
+        dEdd = _dimer_energy(p, d + 1j * h, types, spec.rc).imag / h
+        assert abs(E - Ecf) <= 1e-13 * max(1.0, abs(Ecf))
+        assert abs(F[1, 0] + dEdd) <= 1e-12 * max(1.0, abs(dEdd))
+        assert abs(F[0, 0] - dEdd) <= 1e-12 * max(1.0, abs(dEdd))
+
+
+def test_contraction_identity_is_base_model(orc):
+    s = systems.ag(3)
+    p = systems.params_for(1)
+    base = _eval(orc, orc.Model(p), s)
+    ident = _eval(orc, orc.Model(I.with_contraction(p, np.eye(p.spec.K))), s)
+    assert base[0] == ident[0]
+    assert np.array_equal(base[1], ident[1])
+
+
+def test_contraction_diagonal_equals_rescaled_coefficients(orc):
+    """C = diag(alpha) scales orbital n of every neighbour by alpha_n, which the base model
+    reproduces with c0[s][n] and the rows n of every message network's output layer scaled by
+    alpha_n (the density features, hence everything downstream, are then identical)."""
+    s = systems.water_molecules(4, 14.0)
+    p = systems.params_for(2)
+    K = p.spec.K
+    alpha = np.array([1.3, -0.7, 0.5, 1.1, -1.6, 0.9, 0.25, 2.0])[:K]
+    ref = I.random_params(p.spec, 1202, p.masses, p.layer_scale, p.e_scale)
+    ref.c0 = p.c0 * alpha[None, :]
+    for t in range(p.spec.T - 1):
+        for sp in range(p.spec.n_species):
+            ref.mlp[t][sp]["W3"] = p.mlp[t][sp]["W3"] * alpha[:, None]
+            ref.mlp[t][sp]["b3"] = p.mlp[t][sp]["b3"] * alpha
+    E1, F1, _ = _eval(orc, orc.Model(I.with_contraction(p, np.diag(alpha))), s)
+    E0, F0, _ = _eval(orc, orc.Model(ref), s)
+    frms = np.sqrt(np.mean(np.sum(F0 * F0, 1)))
+    assert abs(E1 - E0) <= 1e-12 * abs(E0)
+    assert np.abs(F1 - F0).max() <= 1e-11 * frms
+
+
 def test_beyond_cutoff_is_zero(orc):
     spec = I.ModelSpec(n_species=1, K=2, L=1, T=2, H=4, rc=4.0, skin=0.5)
     p = I.random_params(spec, 5, [1.0])
@@ -159,9 +219,13 @@ def test_beyond_cutoff_is_zero(orc):
     (3, lambda: I.System("HEA20", systems.hea(3).pos[:20], systems.hea(3).types[:20], np.array([9.6] * 3), systems.hea(3).vel[:20], [], np.ones(5)),
      [(0, 0), (3, 1), (7, 2), (11, 0), (15, 1), (19, 2)]),
 ])
-def test_finite_difference_forces(orc, cfg, make, dofs):
+@pytest.mark.parametrize("contracted", [False, True])
+def test_finite_difference_forces(orc, cfg, make, dofs, contracted):
     s = make()
-    m = _model(orc, cfg)
+    p = systems.params_for(cfg)
+    if contracted:
+        p = I.with_contraction(p, I.contraction_matrix(p.spec.K, 400 + cfg))
+    m = orc.Model(p)
     pos = orc.wrap(s.pos, s.box)
     pl = orc.pairs(pos, s.box, m.params.spec.rc + m.params.spec.skin)
     E, F, _ = orc.energy_forces(m, pos, s.types, s.box, pair_list=pl)
