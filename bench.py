@@ -100,11 +100,11 @@ def csrc_digest():
     return h.hexdigest()
 
 
-def measured_traffic(fam, cfg, precision=0):
+def measured_traffic(fam, cfg, precision=0, contracted=False):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE readings (scaled
-    by the copy-kernel calibration; taken on the 2.05M-atom Ag workload in fp32 mode), or None if
-    absent, taken on different kernel sources or for another workload or mode."""
-    if cfg != 4 or precision != 0 or not os.path.exists(TRAFFIC_FILE):
+    by the copy-kernel calibration; taken on the 2.05M-atom Ag workload in fp32 mode, base model),
+    or None if absent, taken on different kernel sources or for another workload, mode or model."""
+    if cfg != 4 or precision != 0 or contracted or not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
@@ -114,9 +114,9 @@ def measured_traffic(fam, cfg, precision=0):
     return int((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024)
 
 
-def roofline_for(fam, ms_avg, g, cfg=4, precision=0):
+def roofline_for(fam, ms_avg, g, cfg=4, precision=0, contracted=False):
     bytes_, flops, kind = kernel_model(fam, g)
-    traffic = measured_traffic(fam, cfg, precision)
+    traffic = measured_traffic(fam, cfg, precision, contracted)
     t = ms_avg * 1e-3
     gbs = bytes_ / t / 1e9
     tfs = flops / t / 1e12
@@ -267,6 +267,10 @@ def main():
                     help="px,py,pz virtual subdomains (per-layer ghost refresh between them)")
     ap.add_argument("--bandwidth", action="store_true",
                     help="instead of the benchmark line: device copy / fill / read rates (practical HBM ceiling)")
+    ap.add_argument("--contraction", type=int, default=None, metavar="SEED",
+                    help="time the contraction variant of the model (a seeded random K x K contraction "
+                         "of the radial primitives, with layer scales frozen for it: seed 7 on the Ag "
+                         "subdomain)")
     ap.add_argument("--t-sweep", action="store_true",
                     help="instead of the benchmark line: E+F cost vs layers T and ghost volume vs size")
     args = ap.parse_args()
@@ -298,9 +302,10 @@ def main():
         args.warmup = max(1, args.steps // 10)
     t_setup = time.perf_counter()
     s = I.make_system(cfg)
-    p = I.make_params(cfg)
+    p = I.make_params(cfg, contraction_seed=args.contraction)
     if args.precision is not None:
         p.spec.precision = args.precision
+    contracted = p.contraction is not None
     m = binding.MPNN(p, dev)
     sub = tuple(int(x) for x in args.subdomains.split(","))
     m.set_subdomains(*sub)
@@ -371,7 +376,7 @@ def main():
     modeled = [k for k in kernels if kernel_model(k, g) is not None]
     if modeled:
         dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
-        roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg, p.spec.precision)
+        roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg, p.spec.precision, contracted)
         if roof["bound"] == "hbm" and not args.no_profile:
             # context: the measured HBM rate of this kernel next to a plain device copy's on this GPU
             copy = bandwidth(gib=2, reps=5)["copy_read_plus_write"]
@@ -381,7 +386,7 @@ def main():
                 roof["traffic_GBs"] = round(rate, 1)
                 roof["traffic_frac_of_copy"] = round(rate / copy, 4)
     for k in modeled:
-        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg, p.spec.precision)
+        kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg, p.spec.precision, contracted)
 
     out = {
         "metric": METRIC,
@@ -400,7 +405,7 @@ def main():
                                f"K={p.spec.K}, L={p.spec.L}, MLP 2x{p.spec.H}, rc={p.spec.rc}, "
                                f"skin={p.spec.skin}, dt={c['dt']} fs, rebuild every {c['rebuild_every']}",
                    "atoms": s.n, "ghosts": info["n_ghost"], "verlet_entries": info["n_edges"],
-                   "active_edges": EA, "parallelism": "single GPU" if sub == (1, 1, 1) else
+                   "active_edges": EA, "contraction": contracted, "parallelism": "single GPU" if sub == (1, 1, 1) else
                    "single GPU, {}x{}x{} virtual subdomains".format(*sub), "graph_replay_steps": replay},
         "roofline": roof,
         "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,

@@ -32,7 +32,8 @@ class _Params(C.Structure):
                 ("hidden", C.c_int32), ("precision", C.c_int32), ("rc", C.c_double),
                 ("sigma", C.c_double), ("mu", C.POINTER(C.c_double)), ("c0", C.POINTER(C.c_double)),
                 ("mlp", C.POINTER(C.c_double)), ("layer_scale", C.POINTER(C.c_double)),
-                ("e_scale", C.c_double), ("mass", C.POINTER(C.c_double))]
+                ("e_scale", C.c_double), ("mass", C.POINTER(C.c_double)),
+                ("contraction", C.POINTER(C.c_double))]
 
 
 # device allocator hooks of mpnn_set_allocator
@@ -118,8 +119,12 @@ class MPNN:
                       (params.mu, params.c0, params.packed_mlp(), params.layer_scale, params.masses)]
         dp = C.POINTER(C.c_double)
         mu, c0, mlp, sc, ms = (a.ctypes.data_as(dp) for a in self._keep)
+        ct = None
+        if params.contraction is not None:
+            self._keep.append(np.ascontiguousarray(params.contraction, np.float64).reshape(s.K, s.K))
+            ct = self._keep[-1].ctypes.data_as(dp)
         self._p = _Params(s.n_species, s.K, s.L, s.T, s.H, int(s.precision), s.rc, s.sigma, mu, c0, mlp, sc,
-                          float(params.e_scale), ms)
+                          float(params.e_scale), ms, ct)
         h = C.c_void_p()
         self._check(lib().mpnn_create(C.byref(self._p), C.byref(h)), None)
         self.h = h

@@ -201,6 +201,9 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
         if (!(p->layer_scale[t] > 0) || !std::isfinite(p->layer_scale[t])) return MPNN_E_INVALID_ARG;
     for (int k = 0; k < p->K; ++k)
         if (!std::isfinite(p->mu[k])) return MPNN_E_INVALID_ARG;
+    if (p->contraction)
+        for (int q = 0; q < p->K * p->K; ++q)
+            if (!std::isfinite(p->contraction[q])) return MPNN_E_INVALID_ARG;
     mpnn_ctx *ctx = new (std::nothrow) mpnn_ctx;
     if (!ctx) return MPNN_E_OOM;
     mpnn::Context &cx = ctx->cx;
@@ -259,6 +262,12 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
         md.inv_rc64 = 1.0 / p->rc;
         md.half_pi_over_rc = 0.5 * mpnn::kPi / p->rc;
     }
+    cx.contracted = p->contraction != nullptr;
+    if (cx.contracted)
+        for (int q = 0; q < cx.K * cx.K; ++q) {
+            md.C64[q] = p->contraction[q];
+            md.C32[q] = (float)p->contraction[q];
+        }
     Status s = cx.grow(cx.model, sizeof md);
     if (!s.bad()) {
         if (hipMemcpy(cx.model.p, &md, sizeof md, hipMemcpyHostToDevice) != hipSuccess)
@@ -337,6 +346,8 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
     }
     return mpnn::finish(ctx, s);
 }
+
+}  // extern "C"
 
 namespace mpnn {
 
@@ -430,6 +441,8 @@ Status replay_chunk(Context &cx, double dt, int k, bool *done, double *max_disp)
 }
 
 }  // namespace mpnn
+
+extern "C" {
 
 mpnn_status mpnn_set_graph_replay(mpnn_ctx *ctx, int32_t steps_per_replay) {
     if (!ctx || steps_per_replay < 0) return MPNN_E_INVALID_ARG;

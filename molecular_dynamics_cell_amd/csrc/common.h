@@ -168,6 +168,9 @@ struct ModelDev {
     double g_ce[16];        // g_c[k] g_eps[k]
     double inv_rc64;        // 1 / rc
     double half_pi_over_rc; // pi / (2 rc)
+    // contraction variant: orbital n uses the radial function sum_k C[n][k] R_k (row stride K)
+    double C64[16 * 16];
+    float C32[16 * 16];
 };
 
 // Sliced-ELLPACK neighbour storage: rows are grouped in slabs of 64 consecutive (cell-ordered)

@@ -35,7 +35,8 @@ __device__ __forceinline__ void sincos_half_pi(float v, float &s, float &c) {
 // f_c = (1 + cos(pi v))/2 = cos^2(pi v/2), f_c' = -(pi/rc) sin(pi v/2) cos(pi v/2), which has no
 // cancellation near rc.  (The hardware sqrt and cos/sin shifted the total energy by several
 // 1e-6 relative.)
-template <int K, int L>
+// CT: the contraction variant, orbital n from sum_k C[n][k] R_k (and its derivative), in fp32.
+template <int K, int L, bool CT = false>
 struct Basis {
     static constexpr int M = n_mono(L);
     float Rf[K], Rd[K], A[M];   // R_k f_c, its derivative along d, monomials of r / rc
@@ -65,6 +66,26 @@ struct Basis {
             const float R = __builtin_amdgcn_exp2f(c2 * x * x);
             Rf[k] = R * fc;
             Rd[k] = R * fmaf(-x, is2fc, dfc);
+        }
+        if constexpr (CT) {
+            float cf[K], cd[K];
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+                float x = 0.0f, y = 0.0f;
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const float w = md->C32[q * K + k];
+                    x = fmaf(w, Rf[k], x);
+                    y = fmaf(w, Rd[k], y);
+                }
+                cf[q] = x;
+                cd[q] = y;
+            }
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+                Rf[q] = cf[q];
+                Rd[q] = cd[q];
+            }
         }
         const float qx = div_rc(rx), qy = div_rc(ry), qz = div_rc(rz);
         float ux[L + 1], uy[L + 1], uz[L + 1];
@@ -113,8 +134,9 @@ __device__ __forceinline__ double exp_fp64(double x) {
 // widths too narrow for it (see the model set-up) take one exponential per channel (CHAIN false).  The cutoff is cos^2(pi d / (2 rc)) from the
 // Taylor series of cos to the t^18 term (truncation below 1e-14 on [0, pi/2]).
 // K0, KB: only the radial channels K0 .. K0 + KB - 1 (the chain starts from a direct
-// exponential at mu_K0).
-template <int K, int L, typename S = float, int K0 = 0, int KB = K, bool CHAIN = true>
+// exponential at mu_K0).  CT: the contraction variant, orbital n = K0 + j from
+// sum_k C[n][k] R_k f_c over all K primitives, summed in fp64 before the one rounding.
+template <int K, int L, typename S = float, int K0 = 0, int KB = K, bool CHAIN = true, bool CT = false>
 struct BasisHP {
     static constexpr int M = n_mono(L);
     S P[KB];  // c_k R_k f_c, k = K0 + index
@@ -136,7 +158,33 @@ struct BasisHP {
         cs = fma(cs, t2, -0.5);
         cs = fma(cs, t2, 1.0);
         const double fc = cs * cs;
-        if constexpr (CHAIN) {
+        if constexpr (CT) {
+            double Rf[K];
+            if constexpr (CHAIN) {
+                const double x0 = d - md->mu64[0];
+                double r = exp_fp64(md->g_a0 * x0 * x0) * fc;
+                const double E = exp_fp64(md->g_e * d);
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    Rf[k] = r;
+                    if (k + 1 < K) r *= E * fma(md->g_ce[k], d, md->g_c[k]);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k) {
+                    const double x = d - md->mu64[k];
+                    Rf[k] = exp(md->g_a0 * x * x) * fc;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                const int q = K0 + j;
+                double a = 0.0;
+#pragma unroll
+                for (int k = 0; k < K; ++k) a = fma(md->C64[q * K + k], Rf[k], a);
+                P[j] = (S)((double)cv[q] * a);
+            }
+        } else if constexpr (CHAIN) {
             // the chain runs on R_k f_c: P_k = c_k (R_k f_c), next = this E (g_c + g_c g_eps d)
             const double x0 = d - md->mu64[K0];
             double Rf = exp_fp64(md->g_a0 * x0 * x0) * fc;
@@ -311,8 +359,9 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
     const int nl = len[i];
     int o = 0;
     uint32_t bits = 0;
-    // four entries per step: their index and position loads are all in flight together
-    constexpr int U = 4;
+    // eight entries per step: their index and position loads are all in flight together (four:
+    // 16 % slower; sixteen: 2.2x slower)
+    constexpr int U = 8;
     for (int j0 = 0; j0 < nl; j0 += U) {
         int32_t v[U];
         float4 pv[U];
@@ -390,7 +439,7 @@ __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64
 
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
 // atom's density features from it; both leave through LDS-staged, column-tiled stores.
-template <int K, int L, bool CHAIN>
+template <int K, int L, bool CHAIN, bool CT>
 __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
@@ -414,7 +463,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L, float, 0, K, CHAIN> b;
+            BasisHP<K, L, float, 0, K, CHAIN, CT> b;
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
             const double *pv = reinterpret_cast<const double *>(rv);
             b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
@@ -434,7 +483,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
 // basis factors and their products kept in fp64 and one rounding when O is stored.  The K = 12,
 // L = 3 orbital block is too large for fp64 registers in one pass, so it takes several passes over
 // the edges (KB M a multiple of 16, so each pass owns whole 16-column tiles of the O rows).
-template <int K, int L, int KB, int P, bool CHAIN>
+template <int K, int L, int KB, int P, bool CHAIN, bool CT>
 __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, const double *__restrict__ pos,
                                                      const int64_t *__restrict__ slab_off,
                                                      const int32_t *__restrict__ nact,
@@ -459,7 +508,7 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
         const int na = nact[i];
         for (int a = 0; a < na; ++a) {
             const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L, double, P * KB, KB, CHAIN> b;   // this pass's radial channels only
+            BasisHP<K, L, double, P * KB, KB, CHAIN, CT> b;   // this pass's radial channels only
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
             const double *pv = reinterpret_cast<const double *>(rv);
             b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
@@ -505,7 +554,7 @@ __global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const f
 //   s = sum_k c_v[k] u_k (R'_k f_c + R_k f'_c),  Q_m = sum_k c_v[k] R_k f_c G[k,m]
 //   dE/dr_e += s r/d + sum_m Q_m dA_m/dr              (accumulated over layers)
 // The receiver-side force sum is accumulated in fp64 per row.
-template <int K, int L, bool FIRST, bool WANT_W>
+template <int K, int L, bool FIRST, bool WANT_W, bool CT>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
@@ -534,7 +583,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
         const int64_t v = act_n[e];
         const float *rv = c + v * rec_stride(K);   // node record: position, then messages
         const double *pv = reinterpret_cast<const double *>(rv);
-        Basis<K, L> b;
+        Basis<K, L, CT> b;
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
         const float *cv = rv + kRecC;
         float s = 0.0f, Q[M];
@@ -740,6 +789,13 @@ __global__ __launch_bounds__(256) void k_assemble_go(int64_t n, int64_t np, cons
 
 const int32_t *row_perm(const Context &cx) { return cx.bucket ? cx.row_perm.as<int32_t>() : nullptr; }
 
+template <int K, int L, int KB, int P, bool CH, bool CT>
+void launch_agg64(Context &cx, const float *ct, float *Ot) {
+    k_aggregate64<K, L, KB, P, CH, CT><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
+        cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(),
+        ct, cx.model.as<ModelDev>(), row_perm(cx), Ot);
+}
+
 #define MPNN_DISPATCH_KL(K_, L_, CALL)                                                 \
     do {                                                                               \
         if ((K_) == 8 && (L_) == 2) { constexpr int KK = 8, LL = 2; CALL; }            \
@@ -779,26 +835,30 @@ Status aggregate(Context &cx, int t) {
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
-#define MPNN_AGG32(CH)                                                                                          \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(             \
+#define MPNN_AGG32(CH, CT)                                                                                      \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(         \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], row_perm(cx), Ot, Ft)))
-        if (cx.chain) MPNN_AGG32(true);
-        else MPNN_AGG32(false);
+        if (cx.contracted) {
+            if (cx.chain) MPNN_AGG32(true, true);
+            else MPNN_AGG32(false, true);
+        } else {
+            if (cx.chain) MPNN_AGG32(true, false);
+            else MPNN_AGG32(false, false);
+        }
 #undef MPNN_AGG32
         MPNN_HIP(hipGetLastError());
         return Status::ok();
     }
 #define MPNN_AGG64(KK, LL, KB, P)                                                                               \
-    if (cx.chain)                                                                                               \
-        k_aggregate64<KK, LL, KB, P, true><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                           \
-            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),                 \
-            cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), row_perm(cx), Ot);                             \
-    else                                                                                                        \
-        k_aggregate64<KK, LL, KB, P, false><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(                          \
-            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(),                 \
-            cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), row_perm(cx), Ot)
+    if (cx.contracted) {                                                                                        \
+        if (cx.chain) launch_agg64<KK, LL, KB, P, true, true>(cx, ct, Ot);                                      \
+        else launch_agg64<KK, LL, KB, P, false, true>(cx, ct, Ot);                                              \
+    } else {                                                                                                    \
+        if (cx.chain) launch_agg64<KK, LL, KB, P, true, false>(cx, ct, Ot);                                     \
+        else launch_agg64<KK, LL, KB, P, false, false>(cx, ct, Ot);                                             \
+    }
     if (cx.K == 12 && cx.L == 3) {
         MPNN_AGG64(12, 3, 4, 0);
         MPNN_AGG64(12, 3, 4, 1);
@@ -837,7 +897,12 @@ Status backward_layer(Context &cx, int t) {
     const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     const bool first = (t == cx.T - 1), want_w = (t >= 1);
 #define MPNN_BWD(FIRST_, W_)                                                                               \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+    do {                                                                                                   \
+        if (cx.contracted) MPNN_BWD_CT(FIRST_, W_, true);                                                  \
+        else MPNN_BWD_CT(FIRST_, W_, false);                                                               \
+    } while (0)
+#define MPNN_BWD_CT(FIRST_, W_, CT_)                                                                       \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
@@ -847,6 +912,7 @@ Status backward_layer(Context &cx, int t) {
     else if (want_w) MPNN_BWD(false, true);
     else MPNN_BWD(false, false);
 #undef MPNN_BWD
+#undef MPNN_BWD_CT
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

@@ -65,6 +65,7 @@ struct Context {
     // ---- model ----
     int S = 0, K = 0, L = 0, T = 0, H = 0, M = 0, D = 0, DP = 0;
     bool chain = true;  // aggregation Gaussians by the ratio chain (else one exponential each)
+    bool contracted = false;  // orbitals from contracted radial functions (mpnn_params.contraction)
     int precision = 0;  // 0: fp32 orbital sums / fp32 networks; 1: fp64 orbital sums and networks;
                         // 2: fp32 orbital sums, bf16-operand networks with fp32 accumulation
     double rc = 0, sigma = 0, e_scale = 0;

@@ -257,13 +257,26 @@ __global__ void k_ghost_pos(int64_t G, int64_t n, const int32_t *__restrict__ ow
     if (types) types[n + k] = types[o];
 }
 
-// fp32 copy of every node's position for the active-edge pre-test, and the fp64 position into the
-// node record of every layer
-__global__ void k_pos32(int64_t NN, int T, int rs, const double *__restrict__ pos, float4 *__restrict__ pos32,
-                        float *__restrict__ rec) {
+// Every node's position for this step: a ghost takes its owner's plus S L (as k_ghost_pos; owners
+// are local atoms, which this kernel does not write), then the fp32 copy for the active-edge
+// pre-test and the fp64 position in the node record of every layer.
+__global__ void k_node_pos(int64_t NN, int64_t n, int T, int rs, const int32_t *__restrict__ owner,
+                           const int32_t *__restrict__ code, Grid g, double *__restrict__ pos,
+                           float4 *__restrict__ pos32, float *__restrict__ rec) {
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (v >= NN) return;
-    const double x = pos[3 * v], y = pos[3 * v + 1], z = pos[3 * v + 2];
+    double x, y, z;
+    if (v < n) {
+        x = pos[3 * v]; y = pos[3 * v + 1]; z = pos[3 * v + 2];
+    } else {
+        const int64_t o = owner[v - n];
+        int s[3];
+        shift_of(code[v - n], s[0], s[1], s[2]);
+        x = __dadd_rn(pos[3 * o], (double)s[0] * g.L[0]);
+        y = __dadd_rn(pos[3 * o + 1], (double)s[1] * g.L[1]);
+        z = __dadd_rn(pos[3 * o + 2], (double)s[2] * g.L[2]);
+        pos[3 * v] = x; pos[3 * v + 1] = y; pos[3 * v + 2] = z;
+    }
     pos32[v] = float4{(float)x, (float)y, (float)z, 0.0f};
     for (int t = 0; t < T; ++t) {
         double *r = reinterpret_cast<double *>(rec + ((int64_t)t * NN + v) * rs);
@@ -729,16 +742,12 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
 
 Status refresh_ghost_positions(Context &cx) {
     ProfScope ps_(cx, kProfGhostPos);
-    if (cx.G > 0) {
-        const Grid g = make_grid(cx);
-        k_ghost_pos<<<grid_for(cx.G), kBlock, 0, cx.stream>>>(cx.G, cx.n, cx.ghost_owner.as<int32_t>(),
-                                                               cx.ghost_code.as<int32_t>(), g, cx.pos.as<double>(),
-                                                               nullptr);
-        MPNN_HIP(hipGetLastError());
-    }
     if (cx.NN > 0) {
-        k_pos32<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.T, rec_stride(cx.K), cx.pos.as<double>(),
-                                                            cx.pos32.as<float4>(), cx.c.as<float>());
+        const Grid g = make_grid(cx);
+        k_node_pos<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.n, cx.T, rec_stride(cx.K),
+                                                               cx.ghost_owner.as<int32_t>(), cx.ghost_code.as<int32_t>(),
+                                                               g, cx.pos.as<double>(), cx.pos32.as<float4>(),
+                                                               cx.c.as<float>());
         MPNN_HIP(hipGetLastError());
     }
     return Status::ok();

@@ -368,18 +368,29 @@ def load_scales() -> dict:
         return json.load(f)
 
 
-def make_params(cfg: int, require_scales: bool = True) -> Params:
-    """Random-init parameters of benchmark model `cfg` with its frozen layer/energy scales."""
+def scales_key(cfg: int, contraction_seed: int = None) -> str:
+    return str(cfg) if contraction_seed is None else f"{cfg}+contraction{contraction_seed}"
+
+
+def make_params(cfg: int, require_scales: bool = True, contraction_seed: int = None) -> Params:
+    """Random-init parameters of benchmark model `cfg` with its frozen layer/energy scales;
+    with contraction_seed, the contraction variant of the same model (C from that seed) with the
+    scales frozen for it."""
     spec = model_spec(cfg)
     sysm = {1: ["Ag"], 2: ["O", "H"], 3: ["V", "Nb", "Mo", "Ta", "W"], 4: ["Ag"],
             5: ["H", "C", "N", "O"]}[cfg]
     masses = [MASS[s] for s in sysm]
-    scales = load_scales().get(str(cfg))
+    key = scales_key(cfg, contraction_seed)
+    scales = load_scales().get(key)
     if scales is None:
         if require_scales:
-            raise RuntimeError(f"no frozen scales for config {cfg} in {SCALES_FILE}")
-        return random_params(spec, 1200 + cfg, masses)
-    return random_params(spec, 1200 + cfg, masses, scales["layer_scale"], scales["e_scale"])
+            raise RuntimeError(f"no frozen scales for model {key} in {SCALES_FILE}")
+        p = random_params(spec, 1200 + cfg, masses)
+    else:
+        p = random_params(spec, 1200 + cfg, masses, scales["layer_scale"], scales["e_scale"])
+    if contraction_seed is not None:
+        p = with_contraction(p, contraction_matrix(spec.K, contraction_seed))
+    return p
 
 
 def small_spec(K=2, L=1, T=2, H=8, S=1, rc=4.0, skin=0.5, sigma=0.5) -> ModelSpec:

@@ -35,19 +35,28 @@ def pow2(x: float) -> float:
     return float(2.0 ** np.round(np.log2(x)))
 
 
-def calibrate(cfg: int) -> dict:
+# contraction variants with scales of their own: (config, seed of the contraction matrix)
+CONTRACTED = [(4, 7)]
+
+
+def calibrate(cfg: int, contraction_seed: int = None) -> dict:
     spec = I.model_spec(cfg)
     sysr = I.make_system(cfg, reduced=True)
     pos = O.wrap(sysr.pos, sysr.box)
     pl = O.pairs(pos, sysr.box, spec.rc + spec.skin)
     scales = np.ones(spec.T)
-    for t in range(spec.T):
+
+    def model(scales):
         p = I.random_params(spec, 1200 + cfg, sysr.masses, scales, 1.0)
-        _, _, _, dump = O.energy_forces(O.Model(p), pos, sysr.types, sysr.box, pair_list=pl,
+        if contraction_seed is not None:
+            p = I.with_contraction(p, I.contraction_matrix(spec.K, contraction_seed))
+        return O.Model(p)
+
+    for t in range(spec.T):
+        _, _, _, dump = O.energy_forces(model(scales), pos, sysr.types, sysr.box, pair_list=pl,
                                         dump=True)
         scales[t] = pow2(float(np.sqrt(np.mean(dump["rho"][t] ** 2))))
-    p = I.random_params(spec, 1200 + cfg, sysr.masses, scales, 1.0)
-    _, F, _ = O.energy_forces(O.Model(p), pos, sysr.types, sysr.box, pair_list=pl)
+    _, F, _ = O.energy_forces(model(scales), pos, sysr.types, sysr.box, pair_list=pl)
     frms = float(np.sqrt(np.mean(np.sum(F * F, axis=1))))
     return {"layer_scale": [float(x) for x in scales], "e_scale": pow2(TARGET_FRMS / frms),
             "calibration_atoms": int(sysr.n), "calibration_system": sysr.name}
@@ -58,6 +67,10 @@ def main():
     for cfg in sorted(I.CONFIGS):
         out[str(cfg)] = calibrate(cfg)
         print(cfg, out[str(cfg)], flush=True)
+    for cfg, seed in CONTRACTED:
+        key = I.scales_key(cfg, seed)
+        out[key] = calibrate(cfg, seed)
+        print(key, out[key], flush=True)
     with open(I.SCALES_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")

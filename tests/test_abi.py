@@ -60,3 +60,30 @@ def test_no_oracle_in_product_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "orc.h" not in text and "liborc" not in text, f
+
+
+def test_create_rejects_bad_params(mpnn_lib):
+    """mpnn_create validates its arguments before touching the device (runs without a GPU)."""
+    import numpy as np
+    from molecular_dynamics_cell_amd import binding
+    from molecular_dynamics_cell_amd import inputs as I
+    p = I.random_params(I.small_spec(K=2, L=1, T=2, H=64), 3, [1.0])
+    dp = C.POINTER(C.c_double)
+    keep = [np.ascontiguousarray(a, np.float64) for a in
+            (p.mu, p.c0, p.packed_mlp(), p.layer_scale, p.masses, np.eye(2))]
+    ptr = [a.ctypes.data_as(dp) for a in keep]
+
+    def create(precision=0, K=2, contraction=ptr[5]):
+        s = p.spec
+        prm = binding._Params(s.n_species, K, s.L, s.T, s.H, precision, s.rc, s.sigma, *ptr[:4],
+                              float(p.e_scale), ptr[4], contraction)
+        h = C.c_void_p()
+        fn = mpnn_lib.mpnn_create
+        fn.argtypes = [C.POINTER(binding._Params), C.POINTER(C.c_void_p)]
+        fn.restype = C.c_int
+        return fn(C.byref(prm), C.byref(h))
+
+    assert create(precision=3) == -1              # unknown arithmetic mode
+    assert create(K=5) == -1                      # unsupported (K, L)
+    keep[5][0, 1] = np.nan
+    assert create(contraction=ptr[5]) == -1       # non-finite contraction entry
