@@ -713,7 +713,7 @@ __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, 
 __global__ void k_fold_ghost_grad(int64_t n, int K, const int64_t *__restrict__ ghost_off,
                                   float *__restrict__ Gc) {
     const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (o >= n) return;
+    if (o >= n || ghost_off[o] == ghost_off[o + 1]) return;   // most atoms have no ghost image
     for (int k = 0; k < K; ++k) {
         float s = Gc[o * K + k];
         for (int64_t g = ghost_off[o]; g < ghost_off[o + 1]; ++g) s += Gc[(n + g) * K + k];

@@ -358,24 +358,28 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
     if (!FILL) cnt[i] = c;
 }
 
+// Entries sent by every node: the count, and each entry's arrival rank at its sender (in an
+// arbitrary order; the segments are sorted by edge afterwards, so the final order is fixed).
 __global__ void k_tcount(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                         const int32_t *__restrict__ nbr, int32_t *__restrict__ cnt) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t b = sell_base(slab_off, i);
-    for (int j = 0; j < len[i]; ++j) atomicAdd(&cnt[nbr[b + kSlab * j]], 1);
-}
-
-__global__ void k_tfill(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                        const int32_t *__restrict__ nbr, const int64_t *__restrict__ t_off,
-                        int32_t *__restrict__ cursor, int32_t *__restrict__ t_eid) {
+                         const int32_t *__restrict__ nbr, int32_t *__restrict__ cnt, int32_t *__restrict__ rank) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const int64_t b = sell_base(slab_off, i);
     for (int j = 0; j < len[i]; ++j) {
         const int64_t e = b + kSlab * j;
-        const int32_t v = nbr[e];
-        t_eid[t_off[v] + atomicAdd(&cursor[v], 1)] = (int32_t)e;
+        rank[e] = atomicAdd(&cnt[nbr[e]], 1);
+    }
+}
+
+__global__ void k_tfill(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
+                        const int32_t *__restrict__ nbr, const int64_t *__restrict__ t_off,
+                        const int32_t *__restrict__ rank, int32_t *__restrict__ t_eid) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t b = sell_base(slab_off, i);
+    for (int j = 0; j < len[i]; ++j) {
+        const int64_t e = b + kSlab * j;
+        t_eid[t_off[nbr[e]] + rank[e]] = (int32_t)e;
     }
 }
 
@@ -661,24 +665,26 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)NN1 + 64));
+    // per-entry scratch in the edge-gradient buffer (3 words per slot; it is written per step
+    // later): the arrival ranks in its first E1 words, the receivers in the next E1
+    MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
+    int32_t *trank = reinterpret_cast<int32_t *>(cx.gedge.p);
     cnt = cx.tmp_c.as<int32_t>();
     MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
     k_tcount<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-                                                    cx.nbr.as<int32_t>(), cnt);
+                                                    cx.nbr.as<int32_t>(), cnt, trank);
     MPNN_HIP(hipGetLastError());
     MPNN_TRY(exclusive_scan(cx, cnt, cx.NN, cx.t_off.as<int64_t>()));
-    MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
     k_tfill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-                                                   cx.nbr.as<int32_t>(), cx.t_off.as<int64_t>(), cnt,
+                                                   cx.nbr.as<int32_t>(), cx.t_off.as<int64_t>(), trank,
                                                    cx.t_eid.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     if (cx.NN > 0)
         k_rank_sort_segments<<<(unsigned)cx.NN, 64, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     {
-        // receiver of each edge, then of each transposed entry (reuses the gradient buffer)
-        MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
-        int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p);
+        // receiver of each edge, then of each transposed entry
+        int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p) + E1;
         k_edge_receiver<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(),
                                                                cx.row_len.as<int32_t>(), recv);
         MPNN_HIP(hipGetLastError());
