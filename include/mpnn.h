@@ -112,9 +112,11 @@ typedef struct {
     int64_t n_edges;            /* Verlet-list entries (d < rc + skin), receivers local */
     int64_t cells[3];           /* interior cells per axis of one subdomain (side >= rc + skin) */
     int64_t bytes_device;       /* device memory held by the context */
-    int64_t row_bucketing;      /* 1: the neighbour slabs are less than 90 % full (ragged rows), so
+    int64_t row_bucketing;      /* 1: the neighbour slabs are less than 85 % full (ragged rows), so
                                    every step the row kernels take each 256-row block's rows in
                                    descending active count; 0: in order */
+    int64_t n_slots;            /* neighbour storage slots: 64-row slabs, each as wide as its longest
+                                   row (n_edges / n_slots is the slabs' fill) */
 } mpnn_info;
 
 /* Validates and copies the parameters, uploads the weights in the matrix-core layout.

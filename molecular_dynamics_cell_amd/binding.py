@@ -51,7 +51,8 @@ class MDStats(C.Structure):
 
 class Info(C.Structure):
     _fields_ = [("n_local", C.c_int64), ("n_ghost", C.c_int64), ("n_edges", C.c_int64),
-                ("cells", C.c_int64 * 3), ("bytes_device", C.c_int64), ("row_bucketing", C.c_int64)]
+                ("cells", C.c_int64 * 3), ("bytes_device", C.c_int64), ("row_bucketing", C.c_int64),
+                ("n_slots", C.c_int64)]
 
 
 _lib = None
@@ -252,4 +253,5 @@ class MPNN:
         inf = Info()
         self._check(lib().mpnn_get_info(self.h, C.byref(inf)))
         return dict(n_local=inf.n_local, n_ghost=inf.n_ghost, n_edges=inf.n_edges,
-                    cells=list(inf.cells), bytes_device=inf.bytes_device, row_bucketing=inf.row_bucketing)
+                    cells=list(inf.cells), bytes_device=inf.bytes_device, row_bucketing=inf.row_bucketing,
+                    n_slots=inf.n_slots)

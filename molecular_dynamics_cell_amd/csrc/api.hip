@@ -651,6 +651,7 @@ mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info) {
     for (int a = 0; a < 3; ++a) info->cells[a] = cx.nc[a];
     info->bytes_device = (int64_t)cx.device_bytes;
     info->row_bucketing = cx.bucket ? 1 : 0;
+    info->n_slots = cx.E_sell;
     return mpnn::finish(ctx, Status::ok());
 }
 

@@ -643,9 +643,16 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
             slots += w;
         }
         cx.mw = (int)std::max<int64_t>(1, (longest + 31) / 32);
-        // ragged rows (slabs less than 90 % full, e.g. a gas with clusters): the row kernels take
-        // each block's rows by descending active count, so a wave's rows have similar lengths
-        cx.bucket = slots > 0 && (double)E < 0.9 * (double)slots;
+        // ragged rows (slabs less than 85 % full, e.g. a gas with clusters): the row kernels take
+        // each block's rows by descending active count, so a wave's rows have similar lengths.  The
+        // reordering scatters the rows' per-edge stores and spreads a wave over four slabs, so it
+        // pays only for strongly ragged rows (the CHON gas, 83 % full: reverse pass 6 % faster; a
+        // heated metal, 90 % full: 50 % slower)
+        cx.bucket = slots > 0 && (double)E < 0.85 * (double)slots;
+        // per-edge streams (index, w_e, dE/dr_e) several times the 256 MB last-level cache, rows in
+        // order (measured: the 2M-atom Ag subdomain, 7 GB, gains 6 %; a 128,000-atom alloy, 0.45 GB,
+        // loses 3 %; a 4,608-atom water box, which fits in the caches, loses 13 %)
+        cx.nt = !cx.bucket && (double)E * 4.0 * (cx.K + 3) > 1024.0 * (1 << 20);
     }
     MPNN_TRY(exclusive_scan(cx, cnt, nslab, cx.slab_off.as<int64_t>()));
     int64_t Es = 0;

@@ -185,3 +185,20 @@ def test_torch_allocator():
     assert results[0][2] == results[1][2] >= 2
     assert results[0][0] == results[1][0]
     assert np.array_equal(results[0][1], results[1][1])
+
+
+def test_row_bucketing_decision():
+    """Rows are taken by descending active count only where the slabs are less than 85 % full: the
+    CHON gas (ragged rows) is bucketed and matches the oracle, a lattice is not."""
+    from tests import systems
+    s = I.make_system(5, reduced=True)
+    p = I.make_params(5)
+    m = gpu_model(p, s)
+    inf = m.info()
+    fill = inf["n_edges"] / inf["n_slots"]
+    assert inf["row_bucketing"] == 1 and fill < 0.85, inf
+    E, F, _ = m.energy_forces()
+    Eo, Fo, _ = oracle_ef(p, s)
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"CHON4002 bucketed (slab fill {fill:.3f})")
+    inf = gpu_model(I.make_params(4), systems.ag(10, seed=4)).info()
+    assert inf["row_bucketing"] == 0 and inf["n_edges"] / inf["n_slots"] >= 0.85, inf
