@@ -277,8 +277,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the multi-GPU halo exchange is designed, "
-              "not built); run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the library decomposes a box into subdomains on one "
+              "device; there is no multi-GPU halo exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.t_sweep:
