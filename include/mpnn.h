@@ -89,9 +89,9 @@ typedef struct {
     const double *mass;         /* [n_species] amu */
     const double *contraction;  /* [K][K] row-major or NULL.  NULL: orbital k of a neighbour uses
                                    the primitive radial Gaussian R_k (the base model).  Otherwise
-                                   the contraction variant ([JACS] "REANN Architecture": each
-                                   neighbour orbital is a contraction of the N_phi primitive
-                                   Gaussian-type orbitals): orbital n uses sum_k C[n][k] R_k(d),
+                                   the contraction variant ([JACS] "REANN Architecture", where a
+                                   neighbour's orbitals are built as linear combinations of the
+                                   primitive Gaussians): orbital n uses sum_k C[n][k] R_k(d),
                                    one matrix for every species and layer, multiplied by the
                                    element-wise coefficient c_j[n] as before.  Non-finite entries:
                                    MPNN_E_INVALID_ARG. */

@@ -17,9 +17,9 @@
  *   over primitive pairs a <= b (dimension K(K+1)(L+1)/2 as the paper states);
  *   rho-tilde = rho / s_t; atomic networks D->H->H->out with SiLU, one per species and layer;
  *   E_i = e_scale * network output.
- * Contraction variant (section "REANN Architecture": each neighbour orbital G_j is a
- * contraction of the N_phi primitive Gaussian-type orbitals, its coefficients left to the
- * supporting information): with a matrix C[K][K] shared by all species and layers, orbital n
+ * Contraction variant (section "REANN Architecture" builds a neighbour's orbitals G_j as linear
+ * combinations of the primitive Gaussians and leaves the coefficients to its supporting
+ * information): with a matrix C[K][K] shared by all species and layers, orbital n
  * uses the radial function sum_k C[n][k] R_k(d); the element-wise coefficient c_j[n] then
  * multiplies that contracted orbital.  C = identity is the base model.
  */
