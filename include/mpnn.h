@@ -20,15 +20,19 @@
  *   E_i = e_scale * MLP^{T-1}_{s_i}(rho^{T-1}_i / s_{T-1}); E = sum_i E_i (fp64)
  *   MLP(x) = W3 silu(W2 silu(W1 x + b1) + b2) + b3, silu(x) = x / (1 + exp(-x))
  *   F_i = -dE/dr_i.
+ *   (Contraction variant, mpnn_params.contraction: R_k replaced by sum_k' C[k][k'] R_k'.)
  *
- * Units: A, eV, fs, amu.  Arithmetic: positions, velocities and forces fp64; edge basis,
- * aggregation and networks fp32 (matrix cores); energy accumulated in fp64.
+ * Units: A, eV, fs, amu.  Arithmetic: positions, velocities and forces fp64, energy and force
+ * sums fp64; the rest per mpnn_params.precision (0: fp32 orbital sums of fp64-evaluated basis
+ * factors and fp32 networks on the matrix cores, 1: fp64 orbital sums and networks, 2: as 0
+ * with bf16-pair network operands).
  *
  * Conventions for every call:
  *   - Array arguments are DEVICE pointers (e.g. torch tensors on the same GPU), read or
  *     written on the context's stream; scalars and `box` are host values.
  *   - The caller owns every array it passes; the library never frees caller memory.  The
- *     context owns its device scratch (hipMalloc) and releases it in mpnn_destroy.
+ *     context owns its device scratch (hipMalloc, or the hooks of mpnn_set_allocator) and
+ *     releases it in mpnn_destroy.
  *   - Atom arrays are in the caller's order; the library keeps its own locality (cell) order
  *     internally and converts on the way in and out.
  *   - Every call returns mpnn_status; on error mpnn_last_error() describes it and the
