@@ -244,6 +244,47 @@ __device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], flo
     ((v[J] = (float)(feature_q<K, L, 16 * KT + J>(O) * s)), ...);
 }
 
+// Lane groups: the sender-major gathers, and the row kernels on small systems, give one node 16
+// lanes; lane q takes entries q, q+16, ... of the node's list, and the 16 partial sums are
+// combined by a fixed butterfly, after which every lane of the group holds the same bits (each
+// step adds two operands in either order), so the result is reproducible.
+constexpr int kGatherLanes = 16;
+
+template <class T>
+__device__ __forceinline__ T group_sum16(T x) {
+#pragma unroll
+    for (int o = kGatherLanes / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kGatherLanes);
+    return x;
+}
+
+// Column C of a row's orbital sums / density features, written by the lane q = C % 16 of the
+// row's group (lane-group rows; register indices stay compile-time constants).
+template <int K, int L, int C>
+__device__ __forceinline__ void store_o_col(const float (&O)[K][n_mono(L)], float *__restrict__ dst, int64_t np,
+                                            int64_t i, int q) {
+    constexpr int M = n_mono(L);
+    if (q != C % 16) return;
+    float v = 0.0f;
+    if constexpr (C < K * M) v = O[C / M][C % M];
+    dst[tiled(np, i, C)] = v;
+}
+template <int K, int L, int Q>
+__device__ __forceinline__ void store_feature_col(const float (&O)[K][n_mono(L)], float s, float *__restrict__ dst,
+                                                  int64_t np, int64_t i, int q) {
+    if (q != Q % 16) return;
+    dst[tiled(np, i, Q)] = (float)(feature_q<K, L, Q>(O) * s);
+}
+template <int K, int L, int... C>
+__device__ __forceinline__ void store_o_cols(const float (&O)[K][n_mono(L)], float *dst, int64_t np, int64_t i, int q,
+                                             std::integer_sequence<int, C...>) {
+    (store_o_col<K, L, C>(O, dst, np, i, q), ...);
+}
+template <int K, int L, int... Q>
+__device__ __forceinline__ void store_feature_cols(const float (&O)[K][n_mono(L)], float s, float *dst, int64_t np,
+                                                   int64_t i, int q, std::integer_sequence<int, Q...>) {
+    (store_feature_col<K, L, Q>(O, s, dst, np, i, q), ...);
+}
+
 // One 16-column tile of the block's 256 rows: thread t holds the 16 values of row i0 + t; the
 // tile is staged through LDS (rows padded to 80 bytes) and written as one contiguous 16 KB run,
 // 1 KB per store instruction.  All threads of the block call it.
@@ -441,6 +482,55 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
     }
 }
 
+// The same compaction with one 16-lane group per row (small systems): each step tests 16 entries,
+// one per lane, and the group's activity bits (a ballot) give every active entry its rank, so the
+// active list keeps the row's entry order as above.
+__global__ __launch_bounds__(256) void k_compact_groups(int64_t n, const double *__restrict__ pos,
+                                                        const float4 *__restrict__ pos32,
+                                                        const int64_t *__restrict__ slab_off,
+                                                        const int32_t *__restrict__ len,
+                                                        const int32_t *__restrict__ nbr, double rc2, float lo,
+                                                        float hi, uint32_t *__restrict__ amask,
+                                                        int32_t *__restrict__ act_n, int32_t *__restrict__ nact) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kGatherLanes;
+    const int q = (int)(threadIdx.x % kGatherLanes);
+    const int shift = (int)(threadIdx.x % 64) & ~(kGatherLanes - 1);   // the group's lanes in the wave
+    if (i >= n) return;   // a group shares its row, so its 16 lanes leave together
+    const float4 pi = pos32[i];
+    const int64_t b = sell_base(slab_off, i);
+    const int nl = len[i];
+    int o = 0;
+    uint32_t lo_bits = 0;
+    for (int j0 = 0; j0 < nl; j0 += kGatherLanes) {
+        const int j = j0 + q;
+        bool act = false;
+        int32_t v = 0;
+        if (j < nl) {
+            v = nbr[b + kSlab * j];
+            const float4 pv = pos32[v];
+            const float dx = pv.x - pi.x, dy = pv.y - pi.y, dz = pv.z - pi.z;
+            const float d2f = dx * dx + dy * dy + dz * dz;
+            act = d2f < lo;
+            if (!act && d2f < hi) {
+                const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+                act = d2_exact(__dsub_rn(pos[3 * (int64_t)v], xi), __dsub_rn(pos[3 * (int64_t)v + 1], yi),
+                               __dsub_rn(pos[3 * (int64_t)v + 2], zi)) < rc2;
+            }
+        }
+        const uint32_t bits = (uint32_t)(__ballot(act) >> shift) & 0xFFFFu;
+        if (act) act_n[b + kSlab * (o + __popc(bits & ((1u << q) - 1u)))] = v;
+        o += __popc(bits);
+        // 32-entry activity words: entries j0 .. j0 + 15 are the low or the high half
+        if ((j0 & 31) == 0) {
+            lo_bits = bits;
+            if (q == 0 && j0 + kGatherLanes >= nl) amask[(int64_t)(j0 >> 5) * n + i] = lo_bits;
+        } else if (q == 0) {
+            amask[(int64_t)(j0 >> 5) * n + i] = lo_bits | (bits << 16);
+        }
+    }
+    if (q == 0) nact[i] = o;
+}
+
 // Active slot of Verlet slot e of receiver row i this step (-1: d >= rc): the row's slab base
 // plus 64 times the number of active entries before entry j = (e - base) / 64.
 __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64_t *__restrict__ slab_off,
@@ -457,7 +547,10 @@ __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64
 
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
 // atom's density features from it; both leave through LDS-staged, column-tiled stores.
-template <int K, int L, bool CHAIN, bool CT, bool NT>
+// LANES = 1: one row per lane, 256-row blocks (row bucketing applies) with LDS-staged tile stores;
+// LANES = 16 (small systems): one row per lane group, the group's partial sums combined by
+// group_sum16 and the row's columns written by its lanes.
+template <int K, int L, bool CHAIN, bool CT, bool NT, int LANES>
 __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
@@ -465,11 +558,18 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
                                                    const ModelDev *__restrict__ md, float inv_scale,
                                                    const int32_t *__restrict__ row_perm,
                                                    float *__restrict__ O, float *__restrict__ feat) {
+    static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
     constexpr int M = n_mono(L), KMT = pad16(K * M) / 16, DT = pad16(n_feat(K, L)) / 16;
-    __shared__ float4 lds[5 * kBlock];
-    const int64_t i0 = xcd_block() * kBlock;
-    if (i0 >= n) return;                       // whole block past the end (grid rounded to 8 XCDs)
-    const int64_t i = block_row(i0, n, row_perm);
+    int64_t i, i0 = 0;
+    int q = 0;
+    if constexpr (LANES == 1) {
+        i0 = xcd_block() * kBlock;
+        if (i0 >= n) return;                       // whole block past the end (grid rounded to 8 XCDs)
+        i = block_row(i0, n, row_perm);
+    } else {
+        i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
+        q = (int)(threadIdx.x % LANES);
+    }
     float acc[K][M];
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -479,7 +579,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
         const int64_t b0 = sell_base(slab_off, i);
         const int na = nact[i];
-        for (int a = 0; a < na; ++a) {
+        for (int a = q; a < na; a += LANES) {
             const int64_t v = ld_s<NT>(&act_n[b0 + kSlab * a]);
             BasisHP<K, L, float, 0, K, CHAIN, CT> b;
             const float *rv = c + v * rec_stride(K);   // node record: position, then messages
@@ -491,10 +591,22 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
                 for (int m = 0; m < M; ++m) acc[k][m] = fmaf(b.P[k], b.A[m], acc[k][m]);
         }
     }
-    // rows n..np-1 of the last block are padding: written, never read
-    store_o_rows<K, L>(acc, lds, O + i0 * 16, np, (int)(i - i0), std::make_integer_sequence<int, KMT>{});
-    store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, (int)(i - i0),
-                             std::make_integer_sequence<int, DT>{});
+    if constexpr (LANES == 1) {
+        __shared__ float4 lds[5 * kBlock];
+        // rows n..np-1 of the last block are padding: written, never read
+        store_o_rows<K, L>(acc, lds, O + i0 * 16, np, (int)(i - i0), std::make_integer_sequence<int, KMT>{});
+        store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, (int)(i - i0),
+                                 std::make_integer_sequence<int, DT>{});
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[k][m] = group_sum16(acc[k][m]);
+        if (i < n) {
+            store_o_cols<K, L>(acc, O, np, i, q, std::make_integer_sequence<int, 16 * KMT>{});
+            store_feature_cols<K, L>(acc, inv_scale, feat, np, i, q, std::make_integer_sequence<int, 16 * DT>{});
+        }
+    }
 }
 
 // Orbital sums in fp64 (the accurate mode): channels k in [P KB, (P+1) KB) of O^t_i, with the
@@ -577,7 +689,7 @@ __global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const f
 // the node records this pass gathers (4.7 % faster than ordinary stores, measured there); the
 // streamed active indices and the dE/dr_e read back for accumulation are loaded the same way
 // (another 1.2 %).
-template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT>
+template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
@@ -587,21 +699,31 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
                                                         const int32_t *__restrict__ row_perm,
                                                         float *__restrict__ w, float *__restrict__ gedge,
                                                         double *__restrict__ Frecv) {
+    static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
     constexpr int M = n_mono(L);
     constexpr Mono<L> mono;
-    const int64_t i = block_row(xcd_block() * blockDim.x, n, row_perm);
-    if (i >= n) return;
+    int64_t i;
+    int q = 0;
+    if constexpr (LANES == 1) {
+        i = block_row(xcd_block() * blockDim.x, n, row_perm);
+        if (i >= n) return;
+    } else {   // lane group per row (small systems); the group's force partials meet below
+        i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
+        q = (int)(threadIdx.x % LANES);
+    }
+    const bool row = i < n;
+    const int64_t ir_ = row ? i : 0;   // idle groups past the end read row 0 and write nothing
     float mu[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
     const float ir = md->inv_rc;
-    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const double xi = pos[3 * ir_], yi = pos[3 * ir_ + 1], zi = pos[3 * ir_ + 2];
     float G[K][M];
-    assemble_go_row<K, L>(Grho, Ot, np, i, G);
+    assemble_go_row<K, L>(Grho, Ot, np, ir_, G);
     double F[3] = {0.0, 0.0, 0.0};
-    const int64_t b0 = sell_base(slab_off, i);
-    const int na = nact[i];
-    for (int a = 0; a < na; ++a) {
+    const int64_t b0 = sell_base(slab_off, ir_);
+    const int na = row ? nact[ir_] : 0;
+    for (int a = q; a < na; a += LANES) {
         const int64_t e = b0 + kSlab * a;   // active slot: per-edge outputs are stored here
         const int64_t v = ld_s<NT>(&act_n[e]);
         const float *rv = c + v * rec_stride(K);   // node record: position, then messages
@@ -649,6 +771,11 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
         F[1] += (double)g[1];
         F[2] += (double)g[2];
     }
+    if constexpr (LANES > 1) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) F[c] = group_sum16(F[c]);
+        if (!row || q != 0) return;
+    }
     if (FIRST) {
         Frecv[3 * i] = F[0]; Frecv[3 * i + 1] = F[1]; Frecv[3 * i + 2] = F[2];
     } else {
@@ -656,17 +783,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
     }
 }
 
-// Sender-major gathers use 16 lanes per node: lane q takes entries q, q+16, ... of the node's
-// list (skipping entries outside rc, tested exactly as the receiver row did), and the 16
-// partial sums are combined by a fixed butterfly, so the result is reproducible.
-constexpr int kGatherLanes = 16;
-
-template <class T>
-__device__ __forceinline__ T group_sum16(T x) {
-#pragma unroll
-    for (int o = kGatherLanes / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, kGatherLanes);
-    return x;
-}
+// Sender-major gathers use kGatherLanes lanes per node (see group_sum16 above).
 
 // dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
 // term, gathered without atomics).  The first gather of an evaluation (BUILD) looks up the active
@@ -852,7 +969,11 @@ Status compact_active(Context &cx) {
             cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(), cx.nact.as<int32_t>(),
             cx.bucket ? cx.row_perm.as<int32_t>() : nullptr);
     };
-    if (cx.nt) launch(std::true_type{});
+    if (cx.lane_groups)
+        k_compact_groups<<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(
+            cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(), cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
+            cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
+    else if (cx.nt) launch(std::true_type{});
     else launch(std::false_type{});
     MPNN_HIP(hipGetLastError());
     return Status::ok();
@@ -866,13 +987,20 @@ Status aggregate(Context &cx, int t) {
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
 #define MPNN_AGG32_NT(CH, CT, NT)                                                                               \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(     \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT, 1><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(  \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], row_perm(cx), Ot, Ft)))
+#define MPNN_AGG32_LG(CH, CT)                                                                                   \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, false, kGatherLanes><<<grid_for(cx.n * kGatherLanes), \
+                                                                                   kBlock, 0, cx.stream>>>(      \
+                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
+                                      cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
+                                      cx.inv_scale_host[t], nullptr, Ot, Ft)))
 #define MPNN_AGG32(CH, CT)                                                                                      \
     do {                                                                                                        \
-        if (cx.nt) MPNN_AGG32_NT(CH, CT, true);                                                                 \
+        if (cx.lane_groups) MPNN_AGG32_LG(CH, CT);                                                              \
+        else if (cx.nt) MPNN_AGG32_NT(CH, CT, true);                                                            \
         else MPNN_AGG32_NT(CH, CT, false);                                                                      \
     } while (0)
         if (cx.contracted) {
@@ -884,6 +1012,7 @@ Status aggregate(Context &cx, int t) {
         }
 #undef MPNN_AGG32
 #undef MPNN_AGG32_NT
+#undef MPNN_AGG32_LG
         MPNN_HIP(hipGetLastError());
         return Status::ok();
     }
@@ -939,11 +1068,19 @@ Status backward_layer(Context &cx, int t) {
     } while (0)
 #define MPNN_BWD_CT(FIRST_, W_, CT_)                                                                       \
     do {                                                                                                   \
-        if (cx.nt) MPNN_BWD_NT(FIRST_, W_, CT_, true);                                                     \
+        if (cx.lane_groups) MPNN_BWD_LG(FIRST_, W_, CT_);                                                  \
+        else if (cx.nt) MPNN_BWD_NT(FIRST_, W_, CT_, true);                                                \
         else MPNN_BWD_NT(FIRST_, W_, CT_, false);                                                          \
     } while (0)
+#define MPNN_BWD_LG(FIRST_, W_, CT_)                                                                       \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, false, kGatherLanes>           \
+                                  <<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(                 \
+                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
+                                      cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
+                                      cx.model.as<ModelDev>(), nullptr, cx.w.as<float>(), cx.gedge.as<float>(), \
+                                      cx.Frecv.as<double>())))
 #define MPNN_BWD_NT(FIRST_, W_, CT_, NT_)                                                                  \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
@@ -955,6 +1092,7 @@ Status backward_layer(Context &cx, int t) {
 #undef MPNN_BWD
 #undef MPNN_BWD_CT
 #undef MPNN_BWD_NT
+#undef MPNN_BWD_LG
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

@@ -125,6 +125,7 @@ struct Context {
     Buf row_perm; // int32 [n]: per 256-row block, its rows by descending active count (bucketing)
     bool bucket = false;   // row kernels take rows in row_perm order (ragged row lengths)
     bool nt = false;       // per-edge streams far larger than the caches, rows in order: nontemporal
+    bool lane_groups = false;   // small systems: the row kernels give each row a 16-lane group
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
     Buf Ei;       // float [n]

@@ -648,11 +648,15 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         // reordering scatters the rows' per-edge stores and spreads a wave over four slabs, so it
         // pays only for strongly ragged rows (the CHON gas, 83 % full: reverse pass 6 % faster; a
         // heated metal, 90 % full: 50 % slower)
-        cx.bucket = slots > 0 && (double)E < 0.85 * (double)slots;
+        // up to 32,768 rows, one row per lane would leave most of the chip idle (at most 512
+        // waves on 1,024 SIMDs) and each wave's rows run one edge after another: the row kernels
+        // give every row 16 lanes instead (and need no bucketing)
+        cx.lane_groups = n <= 32768;
+        cx.bucket = !cx.lane_groups && slots > 0 && (double)E < 0.85 * (double)slots;
         // per-edge streams (index, w_e, dE/dr_e) several times the 256 MB last-level cache, rows in
         // order (measured: the 2M-atom Ag subdomain, 7 GB, gains 6 %; a 128,000-atom alloy, 0.45 GB,
         // loses 3 %; a 4,608-atom water box, which fits in the caches, loses 13 %)
-        cx.nt = !cx.bucket && (double)E * 4.0 * (cx.K + 3) > 1024.0 * (1 << 20);
+        cx.nt = !cx.bucket && !cx.lane_groups && (double)E * 4.0 * (cx.K + 3) > 1024.0 * (1 << 20);
     }
     MPNN_TRY(exclusive_scan(cx, cnt, nslab, cx.slab_off.as<int64_t>()));
     int64_t Es = 0;

@@ -188,17 +188,20 @@ def test_torch_allocator():
 
 
 def test_row_bucketing_decision():
-    """Rows are taken by descending active count only where the slabs are less than 85 % full: the
-    CHON gas (ragged rows) is bucketed and matches the oracle, a lattice is not."""
+    """Above 32,768 atoms, rows are taken by descending active count only where the slabs are less
+    than 85 % full: a 40,000-atom random gas (ragged rows) is bucketed and matches the oracle, a
+    37,044-atom lattice is not; smaller systems use lane groups and never bucket."""
     from tests import systems
-    s = I.make_system(5, reduced=True)
-    p = I.make_params(5)
+    s = _gas(40000, 126.0, 21)
+    p = I.make_params(1)
     m = gpu_model(p, s)
     inf = m.info()
     fill = inf["n_edges"] / inf["n_slots"]
     assert inf["row_bucketing"] == 1 and fill < 0.85, inf
     E, F, _ = m.energy_forces()
     Eo, Fo, _ = oracle_ef(p, s)
-    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"CHON4002 bucketed (slab fill {fill:.3f})")
-    inf = gpu_model(I.make_params(4), systems.ag(10, seed=4)).info()
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"gas40000 bucketed (slab fill {fill:.3f})")
+    inf = gpu_model(I.make_params(4), systems.ag(21, seed=4)).info()
     assert inf["row_bucketing"] == 0 and inf["n_edges"] / inf["n_slots"] >= 0.85, inf
+    inf = gpu_model(I.make_params(5), I.make_system(5, reduced=True)).info()
+    assert inf["row_bucketing"] == 0, inf
