@@ -99,3 +99,16 @@ def test_contracted_md_one_step_and_snapshot():
     s2 = I.System(s.name, pos.cpu().numpy(), s.types, s.box, s.vel, s.species, s.masses)
     Eo, Fo, _ = oracle_ef(p, s2)
     check_ef(E, F.cpu().numpy(), Eo, Fo, label="contracted snapshot after 21 steps")
+
+
+@pytest.mark.parametrize("precision", [0, 1])
+def test_contracted_one_row_per_lane(precision):
+    """Above 32,768 atoms the row kernels take one row per lane (below, a 16-lane group): the
+    contracted model with uneven centres on a 37,044-atom lattice, both arithmetic modes."""
+    s = systems.ag(21, seed=4)
+    p = _params(4, precision, mu_shift=True)
+    m = gpu_model(p, s)
+    assert s.n > 32768
+    E, F, _ = m.energy_forces()
+    Eo, Fo, _ = oracle_ef(p, s)
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"contracted, uneven centres, 37,044 atoms, precision {precision}")
