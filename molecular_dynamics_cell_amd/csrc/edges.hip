@@ -102,6 +102,51 @@ struct Basis {
     }
 };
 
+// The fp32 edge basis for half of the radial channels (the channel-split reverse pass): mu holds
+// the lane's K/2 centres; monomials, 1/d and the displacement as in Basis.
+template <int K, int L>
+struct BasisHalf {
+    static constexpr int KH = K / 2, M = n_mono(L);
+    float Rf[KH], Rd[KH], A[M];
+    float inv_d, rx, ry, rz;
+
+    __device__ __forceinline__ void eval(double dx, double dy, double dz, const ModelDev *__restrict__ md,
+                                         const float (&mu)[KH]) {
+        constexpr Mono<L> mono;
+        rx = (float)dx; ry = (float)dy; rz = (float)dz;
+        const float d = sqrtf(rx * rx + ry * ry + rz * rz);
+        inv_d = 1.0f / d;
+        const float rc = md->rc, ir = md->inv_rc;
+        auto div_rc = [rc, ir](float x) {
+            const float q = x * ir;
+            return fmaf(fmaf(-q, rc, x), ir, q);
+        };
+        float sh, ch;
+        sincos_half_pi(div_rc(d), sh, ch);
+        const float fc = ch * ch;
+        const float dfc = 2.0f * md->dfc_scale * sh * ch;
+        const float c2 = md->exp2_coef, is2fc = md->inv_s2 * fc;
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+            const float x = d - mu[k];
+            const float R = __builtin_amdgcn_exp2f(c2 * x * x);
+            Rf[k] = R * fc;
+            Rd[k] = R * fmaf(-x, is2fc, dfc);
+        }
+        const float qx = div_rc(rx), qy = div_rc(ry), qz = div_rc(rz);
+        float ux[L + 1], uy[L + 1], uz[L + 1];
+        ux[0] = uy[0] = uz[0] = 1.0f;
+#pragma unroll
+        for (int p = 1; p <= L; ++p) {
+            ux[p] = ux[p - 1] * qx;
+            uy[p] = uy[p - 1] * qy;
+            uz[p] = uz[p - 1] * qz;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) A[m] = ux[mono.lx[m]] * uy[mono.ly[m]] * uz[mono.lz[m]];
+    }
+};
+
 // e^x in fp64 for x <= 709: x = n ln 2 + r with ln 2 in two parts (Cody and Waite), so r is exact
 // to rounding and |r| <= ln 2 / 2; e^r from its Taylor series to r^11 (truncation below 7e-15
 // relative), scaled by 2^n.  Arguments below -745 give 0 (the fp64 result underflows there).
@@ -371,6 +416,38 @@ __device__ __forceinline__ void assemble_go_row(const float *__restrict__ grho, 
 #pragma unroll
         for (int m = 0; m < n_mono(L); ++m) G[k][m] = 0.0f;
     go_terms<K, L>(grho, O, np, i, G, std::make_integer_sequence<int, n_feat(K, L)>{});
+}
+
+// The same for the channels H K/2 .. (H+1) K/2 - 1 only (the channel-split reverse pass): the
+// terms that touch those channels, in the same order, so the entries equal the full assembly's.
+template <int K, int L, int H, int Q>
+__device__ __forceinline__ void go_term_half(const float *__restrict__ grho, const float *__restrict__ O, int64_t np,
+                                             int64_t i, float (&G)[K / 2][n_mono(L)]) {
+    constexpr int M = n_mono(L), KH = K / 2;
+    constexpr FeatIdx f = feat_idx(K, Q);
+    constexpr bool in_a = f.a / KH == H, in_b = f.b / KH == H;
+    if constexpr (in_a || in_b) {
+        constexpr Mono<L> mono;
+        constexpr int m0 = f.l * (f.l + 1) * (f.l + 2) / 6, m1 = m0 + (f.l + 1) * (f.l + 2) / 2;
+        const float g = grho[tiled(np, i, Q)];
+#pragma unroll
+        for (int m = m0; m < m1; ++m) {
+            const float wg = mono.w[m] * g;
+            if constexpr (in_a) G[f.a - KH * H][m] += wg * O[tiled(np, i, f.b * M + m)];
+            if constexpr (in_b) G[f.b - KH * H][m] += wg * O[tiled(np, i, f.a * M + m)];
+        }
+    }
+}
+
+template <int K, int L, int H, int... Q>
+__device__ __forceinline__ void assemble_go_half(const float *__restrict__ grho, const float *__restrict__ O,
+                                                 int64_t np, int64_t i, float (&G)[K / 2][n_mono(L)],
+                                                 std::integer_sequence<int, Q...>) {
+#pragma unroll
+    for (int k = 0; k < K / 2; ++k)
+#pragma unroll
+        for (int m = 0; m < n_mono(L); ++m) G[k][m] = 0.0f;
+    (go_term_half<K, L, H, Q>(grho, O, np, i, G), ...);
 }
 
 // Ordinary or nontemporal (streamed past the caches) accesses.  Nontemporal accesses pay where the
@@ -783,6 +860,97 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
     }
 }
 
+// The reverse pass with each row's radial channels split over two adjacent lanes (the 12-channel
+// models: the full dE/dO block, 12 x 20 values, with the basis and the running sums exceeds the
+// registers of one lane, which then runs one wave per SIMD and spills).  Lane h holds channels
+// h K/2 .. (h+1) K/2 - 1 of dE/dO, evaluates the radial factors of those channels, writes their
+// w_e, and the two halves' dE/dr_e terms meet by one exchange (the sum of two operands, so both
+// lanes hold the same bits).  Same outputs and layout as k_backward_layer.
+template <int K, int L, bool FIRST, bool WANT_W, bool NT>
+__global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np, const double *__restrict__ pos,
+                                                        const int64_t *__restrict__ slab_off,
+                                                        const int32_t *__restrict__ nact,
+                                                        const int32_t *__restrict__ act_n, const float *__restrict__ c,
+                                                        const float *__restrict__ Grho, const float *__restrict__ Ot,
+                                                        const ModelDev *__restrict__ md,
+                                                        const int32_t *__restrict__ row_perm,
+                                                        float *__restrict__ w, float *__restrict__ gedge,
+                                                        double *__restrict__ Frecv) {
+    static_assert(K % 2 == 0, "two channel halves");
+    constexpr int M = n_mono(L), KH = K / 2;
+    constexpr Mono<L> mono;
+    const int64_t p = xcd_block() * (kBlock / 2) + threadIdx.x / 2;   // row position
+    const int h = (int)(threadIdx.x & 1);                               // channel half
+    if (p >= n) return;   // both lanes of a row leave together
+    const int64_t i = row_perm ? (int64_t)row_perm[p] : p;
+    float mu[KH];
+#pragma unroll
+    for (int k = 0; k < KH; ++k) mu[k] = md->mu[KH * h + k];
+    const float ir = md->inv_rc;
+    const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    float G[KH][M];
+    if (h == 0) assemble_go_half<K, L, 0>(Grho, Ot, np, i, G, std::make_integer_sequence<int, n_feat(K, L)>{});
+    else assemble_go_half<K, L, 1>(Grho, Ot, np, i, G, std::make_integer_sequence<int, n_feat(K, L)>{});
+    double F[3] = {0.0, 0.0, 0.0};
+    const int64_t b0 = sell_base(slab_off, i);
+    const int na = nact[i];
+    for (int a = 0; a < na; ++a) {
+        const int64_t e = b0 + kSlab * a;
+        const int64_t v = ld_s<NT>(&act_n[e]);
+        const float *rv = c + v * rec_stride(K);
+        const double *pv = reinterpret_cast<const double *>(rv);
+        BasisHalf<K, L> b;
+        b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
+        const float *cv = rv + kRecC + KH * h;
+        float s = 0.0f, Q[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) Q[m] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+            float u = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
+            if (WANT_W) st_s<NT>(u * b.Rf[k], &w[e * K + KH * h + k]);
+            s = fmaf(cv[k] * u, b.Rd[k], s);
+            const float P = cv[k] * b.Rf[k];
+#pragma unroll
+            for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
+        }
+        float ga[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
+            if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
+            if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
+        }
+        const float sd = s * b.inv_d;
+        float g[3] = {fmaf(sd, b.rx, ga[0] * ir), fmaf(sd, b.ry, ga[1] * ir), fmaf(sd, b.rz, ga[2] * ir)};
+#pragma unroll
+        for (int q = 0; q < 3; ++q) g[q] += __shfl_xor(g[q], 1);   // the other channel half
+        if (h == 0) {
+            float *ge = gedge + 3 * e;
+            if (FIRST) {
+                st_s<NT>(g[0], &ge[0]);
+                st_s<NT>(g[1], &ge[1]);
+                st_s<NT>(g[2], &ge[2]);
+            } else {
+                st_s<NT>(ld_s<NT>(&ge[0]) + g[0], &ge[0]);
+                st_s<NT>(ld_s<NT>(&ge[1]) + g[1], &ge[1]);
+                st_s<NT>(ld_s<NT>(&ge[2]) + g[2], &ge[2]);
+            }
+        }
+        F[0] += (double)g[0];
+        F[1] += (double)g[1];
+        F[2] += (double)g[2];
+    }
+    if (h != 0) return;
+    if (FIRST) {
+        Frecv[3 * i] = F[0]; Frecv[3 * i + 1] = F[1]; Frecv[3 * i + 2] = F[2];
+    } else {
+        Frecv[3 * i] += F[0]; Frecv[3 * i + 1] += F[1]; Frecv[3 * i + 2] += F[2];
+    }
+}
+
 // Sender-major gathers use kGatherLanes lanes per node (see group_sum16 above).
 
 // dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
@@ -1068,10 +1236,18 @@ Status backward_layer(Context &cx, int t) {
     } while (0)
 #define MPNN_BWD_CT(FIRST_, W_, CT_)                                                                       \
     do {                                                                                                   \
-        if (cx.lane_groups) MPNN_BWD_LG(FIRST_, W_, CT_);                                                  \
+        if (!CT_ && cx.K == 12) {                                                                          \
+            if (cx.nt) MPNN_BWD_SPLIT(FIRST_, W_, true);                                                   \
+            else MPNN_BWD_SPLIT(FIRST_, W_, false);                                                        \
+        } else if (cx.lane_groups) MPNN_BWD_LG(FIRST_, W_, CT_);                                           \
         else if (cx.nt) MPNN_BWD_NT(FIRST_, W_, CT_, true);                                                \
         else MPNN_BWD_NT(FIRST_, W_, CT_, false);                                                          \
     } while (0)
+#define MPNN_BWD_SPLIT(FIRST_, W_, NT_)                                                                    \
+    k_backward_split<12, 3, FIRST_, W_, NT_><<<grid_xcd(2 * cx.n), kBlock, 0, cx.stream>>>(                \
+        cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), \
+        ct, Gt, Ot, cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(),          \
+        cx.Frecv.as<double>())
 #define MPNN_BWD_LG(FIRST_, W_, CT_)                                                                       \
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, false, kGatherLanes>           \
                                   <<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(                 \
@@ -1093,6 +1269,7 @@ Status backward_layer(Context &cx, int t) {
 #undef MPNN_BWD_CT
 #undef MPNN_BWD_NT
 #undef MPNN_BWD_LG
+#undef MPNN_BWD_SPLIT
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
