@@ -465,6 +465,21 @@ __device__ __forceinline__ void st_s(T v, T *p) {
     else *p = v;
 }
 
+// Sender indices of active entries a0 .. a0 + kIdxStage - 1 of this thread's row (one row per
+// thread, na >= 1 active entries), staged in the thread's own LDS column: the batch's loads are in
+// flight together, so the row loop's chain (index, then the sender's record) waits on memory once
+// per edge instead of twice.  Entries past na repeat the row's last one and are never read.
+constexpr int kIdxStage = 16;
+template <bool NT>
+__device__ __forceinline__ void stage_indices(int32_t (*stage)[kBlock], const int32_t *__restrict__ act_n,
+                                              int64_t b0, int a0, int na) {
+    int32_t t[kIdxStage];
+#pragma unroll
+    for (int u = 0; u < kIdxStage; ++u) t[u] = ld_s<NT>(&act_n[b0 + kSlab * min(a0 + u, na - 1)]);
+#pragma unroll
+    for (int u = 0; u < kIdxStage; ++u) stage[u][threadIdx.x] = t[u];
+}
+
 // Per-step active list: the Verlet entries of each row with d^2 < rc^2 (fp64, the same
 // expression as the build), compacted in row order into the row's leading slots (sender node of
 // active entry a at slot base + 64 a), plus one activity bit per Verlet entry (word j/32, bit j%32
@@ -652,20 +667,32 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
     for (int k = 0; k < K; ++k)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[k][m] = 0.0f;
+    // one row per thread: indices staged kIdxStage at a time; lane groups: one span, direct loads
+    constexpr int SPAN = LANES == 1 ? kIdxStage : (1 << 24);
+    __shared__ int32_t stage[LANES == 1 ? kIdxStage : 1][kBlock];
     if (i < n) {
         const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
         const int64_t b0 = sell_base(slab_off, i);
         const int na = nact[i];
-        for (int a = q; a < na; a += LANES) {
-            const int64_t v = ld_s<NT>(&act_n[b0 + kSlab * a]);
-            BasisHP<K, L, float, 0, K, CHAIN, CT> b;
-            const float *rv = c + v * rec_stride(K);   // node record: position, then messages
-            const double *pv = reinterpret_cast<const double *>(rv);
-            b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
+        for (int a0 = q; a0 < na; a0 += SPAN) {
+            if constexpr (LANES == 1) stage_indices<NT>(stage, act_n, b0, a0, na);
+            const int a1 = min(a0 + SPAN, na);
+            for (int a = a0; a < a1; a += LANES) {
+                const int64_t v = LANES == 1 ? stage[a - a0][threadIdx.x] : ld_s<NT>(&act_n[b0 + kSlab * a]);
+                BasisHP<K, L, float, 0, K, CHAIN, CT> b;
+                const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+                const double *pv = reinterpret_cast<const double *>(rv);
+                const double px = pv[0], py = pv[1], pz = pv[2];
+                float cr[K];
 #pragma unroll
-            for (int k = 0; k < K; ++k)
+                for (int k = 0; k < K; ++k) cr[k] = rv[kRecC + k];
+                __builtin_amdgcn_sched_barrier(0);   // the whole record is requested before the basis starts
+                b.eval(px - xi, py - yi, pz - zi, cr, md);
 #pragma unroll
-                for (int m = 0; m < M; ++m) acc[k][m] = fmaf(b.P[k], b.A[m], acc[k][m]);
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int m = 0; m < M; ++m) acc[k][m] = fmaf(b.P[k], b.A[m], acc[k][m]);
+            }
         }
     }
     if constexpr (LANES == 1) {
@@ -709,20 +736,25 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
     for (int k = 0; k < KB; ++k)
 #pragma unroll
         for (int m = 0; m < M; ++m) acc[k][m] = 0.0;
+    __shared__ int32_t stage[kIdxStage][kBlock];
     if (i < n) {
         const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
         const int64_t b0 = sell_base(slab_off, i);
         const int na = nact[i];
-        for (int a = 0; a < na; ++a) {
-            const int64_t v = act_n[b0 + kSlab * a];
-            BasisHP<K, L, double, P * KB, KB, CHAIN, CT> b;   // this pass's radial channels only
-            const float *rv = c + v * rec_stride(K);   // node record: position, then messages
-            const double *pv = reinterpret_cast<const double *>(rv);
-            b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
+        for (int a0 = 0; a0 < na; a0 += kIdxStage) {
+            stage_indices<false>(stage, act_n, b0, a0, na);
+            const int a1 = min(a0 + kIdxStage, na);
+            for (int a = a0; a < a1; ++a) {
+                const int64_t v = stage[a - a0][threadIdx.x];
+                BasisHP<K, L, double, P * KB, KB, CHAIN, CT> b;   // this pass's radial channels only
+                const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+                const double *pv = reinterpret_cast<const double *>(rv);
+                b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
 #pragma unroll
-            for (int k = 0; k < KB; ++k)
+                for (int k = 0; k < KB; ++k)
 #pragma unroll
-                for (int m = 0; m < M; ++m) acc[k][m] = fma(b.P[k], b.A[m], acc[k][m]);
+                    for (int m = 0; m < M; ++m) acc[k][m] = fma(b.P[k], b.A[m], acc[k][m]);
+            }
         }
     }
 #pragma unroll
