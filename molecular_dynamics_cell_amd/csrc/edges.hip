@@ -465,10 +465,11 @@ __device__ __forceinline__ void st_s(T v, T *p) {
     else *p = v;
 }
 
-// Sender indices of active entries a0 .. a0 + kIdxStage - 1 of this thread's row (one row per
-// thread, na >= 1 active entries), staged in the thread's own LDS column: the batch's loads are in
-// flight together, so the row loop's chain (index, then the sender's record) waits on memory once
-// per edge instead of twice.  Entries past na repeat the row's last one and are never read.
+// Entries a0 .. a0 + kIdxStage - 1 of this thread's row of a slab-layout index list (one row per
+// thread, na >= 1 entries: the active senders, or the Verlet entries for the compaction), staged in
+// the thread's own LDS column: the batch's loads are in flight together, so the row loop's chain
+// (index, then the sender's record or position) waits on memory once per edge instead of twice.
+// Entries past na repeat the row's last one and are never read.
 constexpr int kIdxStage = 16;
 template <bool NT>
 __device__ __forceinline__ void stage_indices(int32_t (*stage)[kBlock], const int32_t *__restrict__ act_n,
@@ -503,7 +504,7 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
                                            const float4 *__restrict__ pos32, const int64_t *__restrict__ slab_off,
                                            const int32_t *__restrict__ len, const int32_t *__restrict__ nbr,
                                            double rc2, float lo, float hi, uint32_t *__restrict__ amask,
-                                           int32_t *__restrict__ act_n) {
+                                           int32_t *__restrict__ act_n, int32_t (*stage)[kBlock]) {
     const float4 pi = pos32[i];
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
@@ -512,11 +513,14 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
     // eight entries per step: their index and position loads are all in flight together (four:
     // 16 % slower; sixteen: 2.2x slower)
     constexpr int U = 8;
+    static_assert(kIdxStage % U == 0, "whole steps per staged batch");
     for (int j0 = 0; j0 < nl; j0 += U) {
+        // the Verlet indices arrive through the thread's LDS column, kIdxStage at a time
+        if (j0 % kIdxStage == 0) stage_indices<NT>(stage, nbr, b, j0, nl);
         int32_t v[U];
         float4 pv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = j0 + u < nl ? ld_s<NT>(&nbr[b + kSlab * (j0 + u)]) : (int32_t)i;
+        for (int u = 0; u < U; ++u) v[u] = j0 + u < nl ? stage[j0 % kIdxStage + u][threadIdx.x] : (int32_t)i;
 #pragma unroll
         for (int u = 0; u < U; ++u) pv[u] = pos32[v[u]];
 #pragma unroll
@@ -555,7 +559,8 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
                                                  uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
                                                  int32_t *__restrict__ nact, int32_t *__restrict__ row_perm) {
     const int64_t i0 = xcd_block() * blockDim.x, i = i0 + threadIdx.x;
-    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n) : -1;
+    __shared__ int32_t stage[kIdxStage][kBlock];
+    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n, stage) : -1;
     if (i < n) nact[i] = na;
     if (row_perm) {
         // the block's rows by descending active count (ties by row), so the waves of the row
