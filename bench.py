@@ -69,8 +69,9 @@ def kernel_model(fam, g):
     if fam == "force_gather":
         b = 8 * NN + 4 * EL + 12 * EA + 8 * N + 24 * N + 48 * N
         return b, 3 * EA, "hbm"
+    SA = g.get("SA", False)   # fp32 64-wide message networks: silu' saved forward, read back in reverse
     if fam == "net_forward":
-        b = 4 * DP * N + 4 * K * N
+        b = 4 * DP * N + 4 * K * N + (8 * H * N if SA else 0)
         f = N * 2 * (H * D + H * H + K * H)
         return b, f, "mfma"
     if fam == "net_energy":
@@ -78,6 +79,8 @@ def kernel_model(fam, g):
         f = N * 2 * (2 * H * D + 2 * H * H + 2 * H)
         return b, f, "mfma"
     if fam == "net_backward":
+        if SA:   # the vector-Jacobian product alone
+            return 4 * K * N + 8 * H * N + 4 * DP * N, N * 2 * (H * D + H * H + K * H), "mfma"
         b = 4 * DP * N + 4 * K * N + 4 * DP * N
         f = N * 2 * (2 * H * D + 2 * H * H + K * H + K * H)
         return b, f, "mfma"
@@ -369,7 +372,8 @@ def main():
     ef_rate = s.n / float(np.median(ef)) if ef else None
 
     g = dict(N=s.n, NN=info["n_local"] + info["n_ghost"], EL=info["n_edges"], EA=EA, K=p.spec.K,
-             M=(p.spec.L + 1) * (p.spec.L + 2) * (p.spec.L + 3) // 6, D=p.D, H=p.spec.H, T=p.spec.T)
+             M=(p.spec.L + 1) * (p.spec.L + 2) * (p.spec.L + 3) // 6, D=p.D, H=p.spec.H, T=p.spec.T,
+             SA=p.spec.precision == 0 and p.spec.H == 64 and p.spec.T > 1)
     kernels = {k: {"ms_total": round(v[0], 3), "launches": v[1],
                    "ms_avg": round(v[0] / v[1], 4) if v[1] else 0.0}
                for k, v in prof.items() if v[1]}

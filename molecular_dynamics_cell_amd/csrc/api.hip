@@ -116,7 +116,7 @@ Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
-                  &gedge, &w, &amask, &act_n, &t_act, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
+                  &gedge, &w, &amask, &act_n, &t_act, &dact, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel, &bak_pos, &bak_vel, &bak_F};
     for (const Chunk &c : graphs) (void)hipGraphExecDestroy(c.exec);

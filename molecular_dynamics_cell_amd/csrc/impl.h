@@ -121,6 +121,7 @@ struct Context {
     Buf amask;    // uint32 [mw][n]: bit j%32 of word j/32 = entry j of the row is active (d < rc)
     Buf act_n;    // int32 [E]: sender node of each active slot
     Buf t_act;    // int32 [E]: active slot of each transposed entry this step (-1: d >= rc)
+    Buf dact;     // float [T-1][n][2H]: silu' of both hidden layers of each message network (fp32 mode)
     Buf nact;     // int32 [n] active entries per row
     Buf row_perm; // int32 [n]: per 256-row block, its rows by descending active count (bucketing)
     bool bucket = false;   // row kernels take rows in row_perm order (ragged row lengths)

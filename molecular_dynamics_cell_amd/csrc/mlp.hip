@@ -109,12 +109,14 @@ struct NetArgs {
     const float *Gc;       // backward: dE/dc^{t+1} [*][K]
     float *Grho;           // energy/backward: dE/drho^t, column-tiled [np][DP]
     int64_t np;
+    float *dact;           // fp32 message networks: silu' of both hidden layers, [species-list position][2H]
 };
 
 enum { kForward = 0, kEnergy = 1, kBackward = 2 };
 
-template <int K, int L, int H, int MODE, int CT>
+template <int K, int L, int H, int MODE, int CT, bool SAVE = false>
 __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
+    static_assert(!SAVE || MODE == kForward, "only the forward network saves silu'");
     constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
     constexpr int DT = DP / 16, HT = H / 16;
     const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
@@ -129,6 +131,12 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
     for (int c = 0; c < CT; ++c) me[c] = (base + 16 * c + col < cnt) ? (int64_t)list[base + 16 * c + col] : -1;
     const float *W = a.W + (int64_t)s * a.stride;
     const float *b1 = W + a.ob1, *b2 = W + a.ob2, *b3 = W + a.ob3;
+    // SAVE: this lane's silu' values go to the atom's row of dact (rows 16 rt + 4 grp .. + 3 of
+    // each layer as one float4), for the reverse network of the same layer
+    float *dsave[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+        dsave[c] = (SAVE && me[c] >= 0) ? a.dact + (a.sp_off[s] + base + 16 * c + col) * (2 * H) : nullptr;
 
     // layer 1: Z1 = W1 rho~ + b1
     double z1[HT][CT][4];
@@ -151,7 +159,7 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
     // silu'(Z1) is parked in LDS (one word per lane per value, conflict-free) until the reverse pass
     // needs it, which keeps the 128-wide reverse networks within their register budget
     __shared__ float sd1[MODE == kForward ? 1 : HT * CT * 4][64];
-    float h1[HT][CT][4];
+    float h1[HT][CT][4], ds[4];
 #pragma unroll
     for (int rt = 0; rt < HT; ++rt)
 #pragma unroll
@@ -162,6 +170,9 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
                 const float sg = sigmoid(z);
                 h1[rt][c][i] = z * sg;
                 if constexpr (MODE != kForward) sd1[(rt * CT + c) * 4 + i][lane] = sg * (1.0f + z * (1.0f - sg));
+                if constexpr (SAVE) ds[i] = sg * (1.0f + z * (1.0f - sg));
+                if (SAVE && i == 3 && dsave[c])
+                    *reinterpret_cast<float4 *>(dsave[c] + 16 * rt + 4 * grp) = float4{ds[0], ds[1], ds[2], ds[3]};
             }
     // layer 2
     double z2[HT][CT][4];
@@ -183,6 +194,9 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
                 const float sg = sigmoid(z);
                 h2[rt][c][i] = z * sg;
                 if constexpr (MODE != kForward) d2[rt][c][i] = sg * (1.0f + z * (1.0f - sg));
+                if constexpr (SAVE) ds[i] = sg * (1.0f + z * (1.0f - sg));
+                if (SAVE && i == 3 && dsave[c])
+                    *reinterpret_cast<float4 *>(dsave[c] + H + 16 * rt + 4 * grp) = float4{ds[0], ds[1], ds[2], ds[3]};
             }
 
     if constexpr (MODE != kBackward) {
@@ -271,6 +285,77 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
                         float4{(float)(gr[0][c][0] * a.inv_scale), (float)(gr[0][c][1] * a.inv_scale),
                                (float)(gr[0][c][2] * a.inv_scale), (float)(gr[0][c][3] * a.inv_scale)};
         }
+    }
+}
+
+// The reverse message network from the silu' values its forward pass saved (fp32 mode): the same
+// vector-Jacobian product as k_net's reverse mode, without recomputing the two hidden layers, so
+// half the matrix work.  The saved values are bitwise those the recomputation would give (same
+// products in the same order), so the results are too.
+template <int K, int L, int H>
+__global__ __launch_bounds__(64, 2) void k_net_vjp(const NetArgs a) {
+    constexpr int D = n_feat(K, L), DP = (D + 15) / 16 * 16;
+    constexpr int DT = DP / 16, HT = H / 16;
+    const int lane = threadIdx.x, col = lane & 15, grp = lane >> 4;
+    const int tile = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.S && tile >= a.tile_start[s + 1]) ++s;
+    const int64_t base = (int64_t)(tile - a.tile_start[s]) * 16;
+    const int64_t cnt = a.sp_off[s + 1] - a.sp_off[s];
+    const bool valid = base + col < cnt;
+    const int64_t me = valid ? (int64_t)a.sp_list[a.sp_off[s] + base + col] : -1;
+    const float *dl = a.dact + (valid ? (a.sp_off[s] + base + col) * (2 * H) : 0);
+    const float *W = a.W + (int64_t)s * a.stride;
+    float gy[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int k = 4 * grp + i;
+        gy[i] = (k < K && me >= 0) ? a.Gc[me * K + k] : 0.0f;
+    }
+    // dE/dZ2 = (W3^T dE/dy) silu'(Z2): a single 16-input chunk, fp32 from the matrix cores
+    float gz2[HT][1][4];
+    {
+        const float4 *W3t = reinterpret_cast<const float4 *>(W + a.oW3t);
+#pragma unroll
+        for (int rt = 0; rt < HT; ++rt) {
+            const float4 w = W3t[rt * 64 + lane];
+            const float4 d = valid ? *reinterpret_cast<const float4 *>(dl + H + 16 * rt + 4 * grp)
+                                   : float4{0.f, 0.f, 0.f, 0.f};
+            floatx4 t = mfma4(w.x, gy[0], floatx4{0.f, 0.f, 0.f, 0.f});
+            t = mfma4(w.y, gy[1], t);
+            t = mfma4(w.z, gy[2], t);
+            t = mfma4(w.w, gy[3], t);
+            gz2[rt][0][0] = t[0] * d.x; gz2[rt][0][1] = t[1] * d.y;
+            gz2[rt][0][2] = t[2] * d.z; gz2[rt][0][3] = t[3] * d.w;
+        }
+    }
+    // dE/dZ1 = (W2^T dE/dZ2) silu'(Z1)
+    double g1[HT][1][4];
+    zero(g1);
+    {
+        const float4 *W2t = reinterpret_cast<const float4 *>(W + a.oW2t);
+#pragma unroll
+        for (int kt = 0; kt < HT; ++kt) gemm_step<HT, 1>(W2t, HT, kt, gz2[kt], g1, lane);
+    }
+    float gz1[HT][1][4];
+#pragma unroll
+    for (int rt = 0; rt < HT; ++rt) {
+        const float4 d = valid ? *reinterpret_cast<const float4 *>(dl + 16 * rt + 4 * grp) : float4{0.f, 0.f, 0.f, 0.f};
+        gz1[rt][0][0] = (float)g1[rt][0][0] * d.x; gz1[rt][0][1] = (float)g1[rt][0][1] * d.y;
+        gz1[rt][0][2] = (float)g1[rt][0][2] * d.z; gz1[rt][0][3] = (float)g1[rt][0][3] * d.w;
+    }
+    // dE/drho = (W1^T dE/dZ1) / s_t, one 16-row tile at a time, stored as float4 row pieces
+    const float4 *W1t = reinterpret_cast<const float4 *>(W + a.oW1t);
+#pragma unroll 1
+    for (int rt = 0; rt < DT; ++rt) {
+        double gr[1][1][4];
+        zero(gr);
+#pragma unroll
+        for (int kt = 0; kt < HT; ++kt) gemm_step<1, 1>(W1t + (size_t)rt * HT * 64, HT, kt, gz1[kt], gr, lane);
+        if (me >= 0)
+            *reinterpret_cast<float4 *>(a.Grho + tiled(a.np, me, 16 * rt + 4 * grp)) =
+                float4{(float)(gr[0][0][0] * a.inv_scale), (float)(gr[0][0][1] * a.inv_scale),
+                       (float)(gr[0][0][2] * a.inv_scale), (float)(gr[0][0][3] * a.inv_scale)};
     }
 }
 
@@ -703,6 +788,9 @@ NetArgs make_args(Context &cx, int t, int mode) {
     do {                                                                                         \
         if (cx.precision == 1) k_net64<K_, L_, H_, MODE_><<<tiles, 64, 0, cx.stream>>>(A_);     \
         else if (cx.precision == 2) k_net16<K_, L_, H_, MODE_, kBf16Tiles><<<tiles, 64, 0, cx.stream>>>(A_); \
+        else if ((A_).dact && MODE_ == kBackward) k_net_vjp<K_, L_, H_><<<tiles, 64, 0, cx.stream>>>(A_); \
+        else if ((A_).dact)                                                                      \
+            k_net<K_, L_, H_, MODE_, tiles_per_wave(H_, MODE_), MODE_ == kForward><<<tiles, 64, 0, cx.stream>>>(A_); \
         else k_net<K_, L_, H_, MODE_, tiles_per_wave(H_, MODE_)><<<tiles, 64, 0, cx.stream>>>(A_); \
     } while (0)
 
@@ -861,10 +949,18 @@ Status pack_weights(Context &cx, const double *mlp) {
     return Status::ok();
 }
 
+// silu' rows of message layer t saved by its forward network for its reverse network (fp32 mode,
+// 64-wide networks; the 128-wide ones would spill holding them, and the other modes recompute)
+static float *saved_act(Context &cx, int t) {
+    if (cx.precision != 0 || cx.H != 64) return nullptr;
+    return cx.dact.as<float>() + (int64_t)t * cx.n * 2 * cx.H;
+}
+
 Status mlp_forward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetForward);
     NetArgs a = make_args(cx, t, kForward);
     a.c_next = cx.c.as<float>() + (int64_t)(t + 1) * cx.NN * rec_stride(cx.K) + kRecC;
+    a.dact = saved_act(cx, t);
     MPNN_DISPATCH_NET(kForward, a);
     return Status::ok();
 }
@@ -881,6 +977,7 @@ Status mlp_backward(Context &cx, int t) {
     ProfScope ps_(cx, kProfNetBackward);
     NetArgs a = make_args(cx, t, kBackward);
     a.Gc = cx.Gc.as<float>() + (int64_t)(t + 1) * cx.NN * cx.K;
+    a.dact = saved_act(cx, t);
     MPNN_DISPATCH_NET(kBackward, a);
     return Status::ok();
 }
