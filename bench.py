@@ -69,7 +69,7 @@ def kernel_model(fam, g):
     if fam == "force_gather":
         b = 8 * NN + 4 * EL + 12 * EA + 8 * N + 24 * N + 48 * N
         return b, 3 * EA, "hbm"
-    SA = g.get("SA", False)   # fp32 64-wide message networks: silu' saved forward, read back in reverse
+    SA = g.get("SA", False)   # fp32 message networks: silu' saved forward, read back in reverse
     if fam == "net_forward":
         b = 4 * DP * N + 4 * K * N + (8 * H * N if SA else 0)
         f = N * 2 * (H * D + H * H + K * H)
@@ -373,7 +373,7 @@ def main():
 
     g = dict(N=s.n, NN=info["n_local"] + info["n_ghost"], EL=info["n_edges"], EA=EA, K=p.spec.K,
              M=(p.spec.L + 1) * (p.spec.L + 2) * (p.spec.L + 3) // 6, D=p.D, H=p.spec.H, T=p.spec.T,
-             SA=p.spec.precision == 0 and p.spec.H == 64 and p.spec.T > 1)
+             SA=p.spec.precision == 0 and p.spec.T > 1)
     kernels = {k: {"ms_total": round(v[0], 3), "launches": v[1],
                    "ms_avg": round(v[0] / v[1], 4) if v[1] else 0.0}
                for k, v in prof.items() if v[1]}

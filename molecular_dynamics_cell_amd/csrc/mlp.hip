@@ -949,10 +949,10 @@ Status pack_weights(Context &cx, const double *mlp) {
     return Status::ok();
 }
 
-// silu' rows of message layer t saved by its forward network for its reverse network (fp32 mode,
-// 64-wide networks; the 128-wide ones would spill holding them, and the other modes recompute)
+// silu' rows of message layer t saved by its forward network for its reverse network (fp32 mode;
+// the other modes recompute them)
 static float *saved_act(Context &cx, int t) {
-    if (cx.precision != 0 || cx.H != 64) return nullptr;
+    if (cx.precision != 0) return nullptr;
     return cx.dact.as<float>() + (int64_t)t * cx.n * 2 * cx.H;
 }
 

@@ -740,7 +740,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.pos32, sizeof(float4) * NN1));
     MPNN_TRY(cx.grow(cx.amask, sizeof(uint32_t) * (size_t)cx.mw * n1));
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
-    if (cx.precision == 0 && cx.H == 64 && cx.T > 1)
+    if (cx.precision == 0 && cx.T > 1)
         MPNN_TRY(cx.grow(cx.dact, sizeof(float) * (size_t)(cx.T - 1) * n1 * 2 * cx.H));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
