@@ -8,8 +8,9 @@ One "step" = one MD step of the whole path (half-kick + drift, skin test, rebuil
 ghost refresh, T forward layers, energy network, reverse pass, force gather, half-kick).
 
 Prints ONE JSON line.  Timing: warmup steps untimed, then `--steps` steps bracketed by
-torch.cuda.synchronize(); inputs are resident in HBM before the timed region.  Per-kernel
-durations come from the library's hipEvent profiler on the stream the kernels run on.
+torch.cuda.synchronize(); inputs are resident in HBM before the timed region, and nothing else
+(no profiler) runs inside it.  Per-kernel durations come from a separate pass of profiled steps
+afterwards: the library's hipEvent profiler on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -32,8 +33,41 @@ DTYPE = {0: "f32", 1: "f64", 2: "f32 (bf16 MLP operands)"}
 METRIC = "atom-steps/s (E+F, T=3) on 2.05M-atom Ag subdomain, 1 MI355X; % HBM roof"
 
 
+# Algorithmic HBM bytes per atom-step of each part of the path on the 2.05M-atom Ag subdomain
+# (K = 8, L = 2, H = 64, T = 3; 54 active and 78.9 Verlet neighbours per atom), the budget of the
+# minimal design: forward edges = the Verlet index (79 x 4 B) and the O row written (320 B) per
+# layer; the networks read their feature rows and write their outputs once; the reverse edge pass
+# reads a transposed index and the dE/dO rows and writes 12 B of dE/dr per active edge; the force
+# gather reads those back; integrator, ghost refresh and the amortised rebuild take the rest.
+AG2M_BYTES_PER_ATOM_STEP = {
+    "forward_edges": 2100, "networks_forward": 1300, "networks_vjp": 1300,
+    "reverse_edges": 4000, "force_gather": 1500, "integrate_ghosts_rebuild": 300,
+}
+AG2M_TOTAL = sum(AG2M_BYTES_PER_ATOM_STEP.values())   # 10.5 KB per atom-step
+
+
+def ag2m_alg_bytes(fam, g):
+    """Bytes per launch of kernel family `fam` from the per-atom-step budget above (the 2.05M-atom
+    Ag workload only): each family gets the parts of the path it performs, spread over its
+    launches per step; None for families that the budget counts inside another part."""
+    N, T = g["N"], g["T"]
+    B = AG2M_BYTES_PER_ATOM_STEP
+    per_launch = {
+        "aggregate": B["forward_edges"] / T,
+        "net_forward": B["networks_forward"] / T,
+        "net_energy": B["networks_forward"] / T + B["networks_vjp"] / T,
+        "net_backward": B["networks_vjp"] / T,
+        # the two-direction reverse pass forms every force itself: reverse edges and force gather
+        "reverse_edges": (B["reverse_edges"] + B["force_gather"]) / T,
+        # receiver pass + sender-major gathers (the 12-channel models' reverse pass)
+        "backward_layer": B["reverse_edges"] / T,
+        "force_gather": B["force_gather"],
+    }.get(fam)
+    return None if per_launch is None else per_launch * N
+
+
 def kernel_model(fam, g):
-    """Algorithmic (bytes, flops, kind) per launch of kernel family `fam`.
+    """Itemised (bytes, flops, kind) per launch of kernel family `fam`, for any workload.
 
     Bytes count each array the kernel must touch once (index streams, per-atom state read or
     written, per-edge outputs); gathered neighbour data (positions, messages) is counted once
@@ -53,6 +87,17 @@ def kernel_model(fam, g):
         # counts, active list, positions and messages (per node); O and feature rows out
         b = 4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * KMP * N + 4 * DP * N
         f = EA * (2 * KM + 2 * K)
+        return b, f, "alu"
+    if fam == "node_grad":
+        # dE/drho and O rows in, one dE/dO row out per node (locals and ghosts)
+        b = 4 * DP * N + 4 * KMP * N + 4 * KM * NN
+        f = N * 2 * (2 * D * M)
+        return b, f, "hbm"
+    if fam == "reverse_edges":
+        # per node: position, messages and dE/dO row (gathered per edge, counted once); per atom:
+        # dE/dc and the force out (fp64); active index per edge
+        b = 4 * N + 4 * EA + (24 + 4 * K + 4 * KM) * NN + 4 * K * N + 24 * N
+        f = EA * (8 * KM + 8 * K + 6 * M)
         return b, f, "alu"
     if fam == "backward_layer":
         w_frac = (T - 1) / T                       # layers that emit dE/dc edge terms
@@ -117,57 +162,127 @@ def measured_traffic(fam, cfg, precision=0, contracted=False):
     return int((k["fetch_kib"] * t["fetch_scale"] + k["write_kib"] * t["write_scale"]) * 1024)
 
 
+VALU_FILE = os.path.join(ROOT, "profiles", "valu_ag2m.json")
+
+
+def measured_valu(fam, cfg, precision=0, contracted=False):
+    """VALU utilisation of kernel family `fam` from the committed rocprofv3 SQ counter pass on the
+    2.05M-atom Ag workload (fp32 mode, base model), or None if absent or taken on other sources."""
+    if cfg != 4 or precision != 0 or contracted or not os.path.exists(VALU_FILE):
+        return None
+    with open(VALU_FILE) as f:
+        t = json.load(f)
+    k = t.get("kernels", {}).get(fam)
+    if k is None or t.get("source_sha256") != csrc_digest():
+        return None
+    return k
+
+
 def roofline_for(fam, ms_avg, g, cfg=4, precision=0, contracted=False):
-    bytes_, flops, kind = kernel_model(fam, g)
+    """The kernel's HBM roofline: achieved = algorithmic bytes per launch (the 2.05M-atom budget
+    where it applies, else the itemised model) / its average duration, against the 8 TB/s peak.
+    Matrix-core kernels (the networks) report their MFMA rate against the mode's matrix peak
+    instead.  `traffic` = measured HBM bytes per launch (rocprofv3 counters) when current."""
+    layout_b, flops, kind = kernel_model(fam, g)
+    alg = ag2m_alg_bytes(fam, g) if cfg == 4 and g["K"] == 8 and g["T"] == 3 else None
+    bytes_ = alg if alg is not None else layout_b
     traffic = measured_traffic(fam, cfg, precision, contracted)
     t = ms_avg * 1e-3
     gbs = bytes_ / t / 1e9
-    tfs = flops / t / 1e12
-    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
-    mfma_peak = MFMA_PEAK_TFLOPS[precision]
-    t_cmp = flops / ((mfma_peak if kind == "mfma" else FP32_VALU_TFLOPS) * 1e12)
-    if kind == "hbm" or t_hbm >= t_cmp:
-        return {"kernel": fam, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": int(bytes_), "avg_ms": round(ms_avg, 4)}
-    peak = mfma_peak if kind == "mfma" else FP32_VALU_TFLOPS
-    return {"kernel": fam, "bound": "mfma" if kind == "mfma" else "alu", "achieved": round(tfs, 2),
-            "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": traffic,
-            "algorithmic_flops": int(flops), "algorithmic_bytes": int(bytes_),
-            "hbm_GBs_at_algorithmic_bytes": round(gbs, 1), "avg_ms": round(ms_avg, 4)}
+    out = {"kernel": fam, "avg_ms": round(ms_avg, 4), "traffic": traffic,
+           "algorithmic_bytes": int(bytes_),
+           "bytes_basis": "per-atom-step budget" if alg is not None else "itemised model",
+           "itemised_bytes": int(layout_b), "algorithmic_flops": int(flops)}
+    if kind == "mfma":
+        peak = MFMA_PEAK_TFLOPS[precision]
+        tfs = flops / t / 1e12
+        out.update({"bound": "mfma", "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tfs / peak, 4), "hbm_GBs_at_algorithmic_bytes": round(gbs, 1)})
+    else:
+        out.update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        if kind == "alu":
+            out["valu_tflops_at_algorithmic_flops"] = round(flops / t / 1e12, 2)
+    v = measured_valu(fam, cfg, precision, contracted)
+    if v is not None:
+        out["valu_busy"] = v.get("valu_busy")
+        out["valu_insts_per_unit"] = v.get("valu_insts_per_unit")
+    return out
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """fp64 oracle (as it stands) on a bounded periodic sample of the same workload."""
+def _oracle_sample(cfg):
+    """A bounded periodic sample of workload `cfg` with the same model (seconds of oracle work)."""
+    from molecular_dynamics_cell_amd import inputs as I
+    if cfg in (1, 4):
+        return I.ag(10, 1004, 1104, name="Ag4000"), "fcc Ag 10^3 cells (4,000 atoms, periodic), same model and lattice"
+    if cfg == 3:
+        return I.hea(13), "bcc HEA 13^3 cells (4,394 atoms, periodic), same model"
+    if cfg == 5:
+        return I.make_system(5, reduced=True), "CHON gas, 4,002 atoms at 0.5 g/cm3, same model"
+    return I.make_system(2), "the full 4,608-atom water box"
+
+
+def _oracle_md_rate(cfg, budget_s):
+    """atom-steps/s of the oracle's velocity-Verlet loop on the bounded sample, sized to about
+    budget_s seconds; returns (rate, steps, seconds, threads, sample text)."""
     import oracle
     from molecular_dynamics_cell_amd import inputs as I
     p = I.make_params(cfg)
-    if cfg in (1, 4):
-        s = I.ag(10, 1004, 1104, name="Ag4000")
-        sample = "fcc Ag 10^3 cells (4,000 atoms, periodic), same model and lattice"
-    elif cfg == 3:
-        s = I.hea(13)
-        sample = "bcc HEA 13^3 cells (4,394 atoms, periodic), same model"
-    elif cfg == 5:
-        s = I.make_system(5, reduced=True)
-        sample = "CHON gas, 4,002 atoms at 0.5 g/cm3, same model"
-    else:
-        s = I.make_system(2)
-        sample = "the full 4,608-atom water box"
+    s, sample = _oracle_sample(cfg)
     m = oracle.Model(p)
     rb = I.CONFIGS[cfg]["rebuild_every"]
     dt = I.CONFIGS[cfg]["dt"]
-    # a short run sizes the timed one to about budget_s seconds (the first step also builds the list)
     t0 = time.perf_counter()
-    oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, dt, 5, rebuild_every=rb)
-    t1 = (time.perf_counter() - t0) / 5
+    oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, dt, 2, rebuild_every=rb)
+    t1 = (time.perf_counter() - t0) / 3          # 2 steps plus the initial evaluation
     steps = int(max(1, min(1000, budget_s / max(t1, 1e-3))))
     t0 = time.perf_counter()
     oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, dt, steps, rebuild_every=rb)
     el = time.perf_counter() - t0
-    return {"value": round(s.n * steps / el, 1), "unit": "atom-steps/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{sample}; {steps} velocity-Verlet steps (E+F each step) in {el:.1f} s"}
+    return s.n * steps / el, steps, el, oracle.num_threads(), sample
+
+
+def cpu_baseline(cfg, system=None, full=True, sample_budget_s=10.0):
+    """The fp64 oracle as it stands, on this host's cores: on the full workload (one E+F, then one
+    velocity-Verlet step; rate = N / time of that step) where it fits a minute, and on a bounded
+    sample of the same workload with all threads and with one thread (a child process started
+    with OMP_NUM_THREADS=1, which touches no GPU)."""
+    import subprocess
+    import oracle
+    from molecular_dynamics_cell_amd import inputs as I
+    out = {"unit": "atom-steps/s", "kind": "oracle"}
+    rate, steps, el, thr, sample = _oracle_md_rate(cfg, sample_budget_s)
+    out["sample_all_threads"] = {"value": round(rate, 1), "threads": thr,
+                                 "sample": f"{sample}; {steps} velocity-Verlet steps in {el:.1f} s"}
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = ("import json, sys; sys.path.insert(0, %r); import bench; "
+            "print(json.dumps(bench._oracle_md_rate(%d, %f)))" % (ROOT, cfg, sample_budget_s))
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=600)
+    if r.returncode == 0:
+        r1 = json.loads(r.stdout.strip().splitlines()[-1])
+        out["sample_one_thread"] = {"value": round(r1[0], 1), "threads": r1[3],
+                                    "sample": f"{r1[4]}; {r1[1]} velocity-Verlet steps in {r1[2]:.1f} s"}
+    if full and system is not None:
+        p = I.make_params(cfg)
+        m = oracle.Model(p)
+        s = system
+        t0 = time.perf_counter()
+        oracle.energy_forces(m, oracle.wrap(s.pos, s.box), s.types, s.box)
+        t_ef = time.perf_counter() - t0
+        print(f"cpu_baseline: oracle E+F on {s.n} atoms in {t_ef:.1f} s", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        oracle.md(m, s.pos, s.vel, s.types, s.masses, s.box, I.CONFIGS[cfg]["dt"], 1,
+                  rebuild_every=I.CONFIGS[cfg]["rebuild_every"])
+        t_md = time.perf_counter() - t0
+        t_step = max(t_md - t_ef, 1e-9)
+        out.update({"value": round(s.n / t_step, 1), "cores": oracle.num_threads(),
+                    "sample": f"the full workload ({s.n} atoms): one E+F in {t_ef:.1f} s, then "
+                              f"E+F + one velocity-Verlet step in {t_md:.1f} s; value = N / "
+                              f"({t_md:.1f} - {t_ef:.1f}) s"})
+    else:
+        out.update({"value": out["sample_all_threads"]["value"], "cores": thr,
+                    "sample": out["sample_all_threads"]["sample"]})
+    return out
 
 
 def bandwidth(gib=4, reps=10):
@@ -258,6 +373,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="untimed MD steps first (default: steps / 10)")
     ap.add_argument("--config", type=int, default=4, help="benchmark system 1..5 (default 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample-baseline", action="store_true",
+                    help="time the oracle on the bounded sample only (not on the full workload)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event timing")
     ap.add_argument("--ef-evals", type=int, default=10)
     ap.add_argument("--precision", type=int, choices=(0, 1, 2), default=None,
@@ -341,22 +458,20 @@ def main():
     # warm-up covers at least one full replayed chunk, so its recording is not timed
     m.md_step(c["dt"], max(args.warmup, replay), c["rebuild_every"], stats=False)
     torch.cuda.synchronize()
-    # the event profiler times each kernel family inside the timed steps; replayed chunks cannot
-    # carry it, so with replay the per-kernel times come from extra profiled steps afterwards
-    profile_inline = not args.no_profile and replay == 0
-    if profile_inline:
-        m.set_profiling(True)
+    # timed region: the MD steps alone (the fp64 energy sum runs inside every step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     st = m.md_step(c["dt"], args.steps, c["rebuild_every"], stats=False)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    if not args.no_profile and not profile_inline:
+    # per-kernel durations: a separate pass of profiled steps (event pairs on the library's stream)
+    prof = {}
+    if not args.no_profile:
         m.set_profiling(True)
         m.md_step(c["dt"], max(1, min(args.steps, 20)), c["rebuild_every"], stats=False)
         torch.cuda.synchronize()
-    prof = m.profile() if not args.no_profile else {}
-    m.set_profiling(False)
+        prof = m.profile()
+        m.set_profiling(False)
     st = m.md_step(c["dt"], 0, c["rebuild_every"])      # energies at the end of the run
     elapsed = t1 - t0
     value = s.n * args.steps / elapsed
@@ -382,16 +497,24 @@ def main():
     if modeled:
         dom = max(modeled, key=lambda k: kernels[k]["ms_total"])
         roof = roofline_for(dom, kernels[dom]["ms_avg"], g, cfg, p.spec.precision, contracted)
-        if roof["bound"] == "hbm" and not args.no_profile:
-            # context: the measured HBM rate of this kernel next to a plain device copy's on this GPU
-            copy = bandwidth(gib=2, reps=5)["copy_read_plus_write"]
-            roof["copy_rate_GBs"] = copy
-            if roof.get("traffic"):
-                rate = roof["traffic"] / (roof["avg_ms"] * 1e-3) / 1e9
-                roof["traffic_GBs"] = round(rate, 1)
-                roof["traffic_frac_of_copy"] = round(rate / copy, 4)
     for k in modeled:
         kernels[k]["roofline"] = roofline_for(k, kernels[k]["ms_avg"], g, cfg, p.spec.precision, contracted)
+    # whole step against the HBM roof: atom-steps/s x algorithmic bytes per atom-step / 8 TB/s
+    # (the per-atom-step budget on the 2.05M-atom workload; elsewhere the sum of the itemised
+    # per-launch bytes of one profiled step)
+    if cfg == 4 and g["K"] == 8 and g["T"] == 3:
+        bpas, basis = float(AG2M_TOTAL), "per-atom-step budget"
+    elif kernels:
+        nsteps = max(1, min(args.steps, 20))
+        tot = sum(kernel_model(k, g)[0] * v["launches"] for k, v in kernels.items() if kernel_model(k, g))
+        bpas, basis = tot / nsteps / s.n, "itemised model of the profiled steps"
+    else:
+        bpas, basis = None, None
+    whole = None
+    if bpas:
+        gbs = value * bpas / 1e9
+        whole = {"bytes_per_atom_step": round(bpas, 1), "bytes_basis": basis, "achieved_GBs": round(gbs, 1),
+                 "peak": HBM_PEAK_GBS, "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
     out = {
         "metric": METRIC,
@@ -413,6 +536,7 @@ def main():
                    "active_edges": EA, "contraction": contracted, "parallelism": "single GPU" if sub == (1, 1, 1) else
                    "single GPU, {}x{}x{} virtual subdomains".format(*sub), "graph_replay_steps": replay},
         "roofline": roof,
+        "hbm_roof_whole_step": whole,
         "ef_only_atom_steps_per_s": round(ef_rate, 1) if ef_rate else None,
         "md": {"epot_start": E0, "epot_end": st["epot"], "ekin_end": st["ekin"],
                "temp_end": st["temp"], "steps_total": st["steps"],
@@ -421,7 +545,10 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg)
+        m.close()
+        del m, pos
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, system=s, full=not args.sample_baseline)
     print(json.dumps(out))
 
 

@@ -2,7 +2,7 @@
  *
  * The library evaluates the energy and forces of the model described in "Efficient
  * Parallelization of Message Passing Neural Network Potentials for Large-Scale Molecular
- * Dynamics" (Xia & Jiang), section "REANN Architecture", Eq. 1 (embedded-atom density from
+ * Dynamics" (Xia & Jiang; [JACS] below), section "REANN Architecture", Eq. 1 (embedded-atom density from
  * Gaussian-type orbital sums), Eq. 2 (messages c^t from atomic networks) and Fig. 1, with
  * forces from the reverse pass of section "Parallelization Algorithm", Eq. 3-5, on one GPU's
  * subdomain: the local atoms plus a ghost shell of periodic images, refreshed per layer
@@ -73,14 +73,24 @@ typedef struct {
     int32_t L;                  /* maximum angular momentum */
     int32_t T;                  /* message-passing layers */
     int32_t hidden;             /* width H of both hidden layers */
-    int32_t precision;          /* 0: fp32 orbital sums and fp32 networks (fp64 accumulation of
-                                   16-product chunks); 1: fp64 orbital sums and fp64 networks,
-                                   for force distributions with heavy tails (slower); 2: fp32
-                                   orbital sums, networks on the bf16 matrix cores with fp32
-                                   accumulation, every operand (features, weights, hidden
-                                   activations) carried as a pair of bf16 values; only for
-                                   hidden = 64 and D <= 128 (MPNN_E_INVALID_ARG otherwise); forces
-                                   within 2e-3 of the RMS force of the fp64 model */
+    int32_t precision;          /* arithmetic mode, which also fixes how the parameters are held:
+                                   0: fp32 orbital sums and fp32 networks (fp64 accumulation of
+                                      16-product chunks).  Parameters are held as fp32: mpnn_create
+                                      rounds mu, c0, every network weight and bias, 1/s_t, e_scale
+                                      and the contraction matrix to the nearest fp32 value, and the
+                                      model evaluated is the one with those rounded parameters.
+                                   1: fp64 orbital sums and fp64 networks, for force distributions
+                                      with heavy tails (slower).  Every parameter is held in fp64
+                                      exactly as passed (the per-layer messages and features are
+                                      stored in fp32 between kernels; the reverse pass runs in fp32
+                                      with fp64 force sums).
+                                   2: as 0 (parameters rounded to fp32), with the networks on the
+                                      bf16 matrix cores: every operand (features, weights, hidden
+                                      activations) is carried as a pair of bf16 values (the bf16
+                                      rounding and the bf16 rounding of the remainder), fp32
+                                      accumulation; only for hidden = 64 and D <= 128
+                                      (MPNN_E_INVALID_ARG otherwise); forces within 2e-3 of the RMS
+                                      force of the fp64 model */
     double rc;                  /* cutoff radius, A */
     double sigma;               /* Gaussian standard deviation, A */
     const double *mu;           /* [K] radial centres, A */
@@ -153,7 +163,10 @@ mpnn_status mpnn_set_allocator(mpnn_ctx *ctx, void *(*alloc)(size_t bytes, void 
 mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t *types,
                                  int64_t n, const double box[3], double rc, double skin);
 
-/* Energy and forces.  pos: NULL uses the context's current positions; otherwise new positions
+/* Energy and forces ([JACS] "Parallelization Algorithm", Eq. 3: E is the sum of the local atoms'
+ * energies E_i and F_k = -dE/dr_k; Eq. 4-5: the derivative runs back through every layer's density
+ * features, orbital coefficients and messages; "REANN Architecture", Eq. 1-2, for the forward
+ * model).  pos: NULL uses the context's current positions; otherwise new positions
  * ([n][3] fp64, device, caller order) replace them (if any atom moved more than skin/2 from
  * the last build the list is rebuilt first).  energy: host out (eV) or NULL; forces: device
  * out [n][3] fp64 (eV/A, caller order) or NULL; atom_energy: device out [n] fp64 or NULL.
@@ -161,21 +174,29 @@ mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t
 mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
                                double *atom_energy);
 
-/* n_steps velocity-Verlet steps of dt_fs (NVE).  The list is rebuilt every rebuild_every steps
+/* n_steps velocity-Verlet steps of dt_fs (NVE; [JACS] "Strong Scaling" checks the parallel code by the
+ * energy conservation of NVE runs; the integrator itself is not on the pages: half-kick, drift,
+ * new forces, half-kick, a = F / m in A/fs^2 with 1 eV/(A amu) = 9.648533212e-3 A/fs^2).  After the
+ * steps the total potential energy of the final state is summed in fixed order (fp64) on the
+ * device; it is copied to the host only when stats is given.  The list is rebuilt every rebuild_every steps
  * (0: never by count) and whenever an atom has moved more than skin/2 since the last build.
  * stats: host out or NULL. */
 mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t rebuild_every,
                          mpnn_md_stats *stats);
 
-/* Replace positions and/or velocities ([n][3] fp64, device, caller order; either may be NULL).
- * New positions trigger a rebuild. */
+/* MD state of the velocity-Verlet loop (positions and velocities, the system's phase-space point;
+ * see mpnn_md_step).  Replace positions and/or velocities ([n][3] fp64, device, caller order;
+ * either may be NULL).  New positions trigger a rebuild. */
 mpnn_status mpnn_set_state(mpnn_ctx *ctx, const double *pos, const double *vel);
 
-/* Current positions/velocities ([n][3] fp64 device out, caller order; either may be NULL) and
- * the step counter (host out or NULL). */
+/* Current positions/velocities of the MD state ([n][3] fp64 device out, caller order; either may be
+ * NULL; positions are wrapped into the box at the last rebuild) and the step counter (host out or
+ * NULL). */
 mpnn_status mpnn_get_state(mpnn_ctx *ctx, double *pos, double *vel, int64_t *step);
 
-/* The Verlet list as canonical tuples in caller ids: receiver i, sender j and image shift S
+/* The Verlet list (the cutoff-sphere neighbours N_c(i) of "REANN Architecture", Eq. 1, widened by
+ * the skin; with the periodic images that stand in for the ghost atoms of "Parallelization
+ * Algorithm", Fig. 3a) as canonical tuples in caller ids: receiver i, sender j and image shift S
  * (r_ij = r_j + S*box - r_i for the wrapped positions of the last build).  Device outputs
  * i[cap], j[cap], shift[cap][3] (int32); *n_pairs (host) receives the total count; at most cap
  * entries are written. */

@@ -1,6 +1,7 @@
 // C ABI entry points (include/mpnn.h): validation, buffer management and the call sequence
 // of one energy/force evaluation and of the velocity-Verlet loop.
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -57,7 +58,8 @@ Status Context::grow_keep(Buf &b, size_t bytes, size_t keep) {
 const char *const kProfNames[kProfCount] = {
     "build_sort", "build_ghosts", "build_rows", "build_transpose", "build_species", "ghost_positions",
     "compact", "aggregate", "net_forward", "net_energy", "net_backward", "ghost_messages",
-    "backward_layer", "message_grad", "ghost_grad_fold", "force_gather", "kick_drift", "kick", "reduce"};
+    "backward_layer", "message_grad", "ghost_grad_fold", "force_gather", "kick_drift", "kick", "reduce",
+    "node_grad", "reverse_edges"};
 
 void Context::prof_begin(int id) {
     if (!prof_on) return;
@@ -114,7 +116,7 @@ void Context::release(Buf &b) {
 
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
-    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
+    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &Rn, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &dact, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
@@ -150,15 +152,24 @@ Status evaluate(Context &cx, double *F_caller) {
             MPNN_TRY(mlp_energy(cx));
         }
     }
-    for (int t = cx.T - 1; t >= 0; --t) {
-        MPNN_TRY(backward_layer(cx, t));
-        if (t >= 1) {
-            MPNN_TRY(backward_messages(cx, t));
-            MPNN_TRY(mlp_backward(cx, t - 1));
+    if (cx.two_dir) {
+        for (int t = cx.T - 1; t >= 0; --t) {
+            MPNN_TRY(node_grad(cx, t));
+            MPNN_TRY(reverse_edges(cx, t, F_caller));
+            if (t >= 1) MPNN_TRY(mlp_backward(cx, t - 1));
         }
+    } else {
+        for (int t = cx.T - 1; t >= 0; --t) {
+            MPNN_TRY(backward_layer(cx, t));
+            if (t >= 1) {
+                MPNN_TRY(backward_messages(cx, t));
+                MPNN_TRY(mlp_backward(cx, t - 1));
+            }
+        }
+        if (cx.T == 1) MPNN_TRY(transpose_active(cx));
+        MPNN_TRY(force_gather(cx, F_caller));
     }
-    if (cx.T == 1) MPNN_TRY(transpose_active(cx));
-    MPNN_TRY(force_gather(cx, F_caller));
+    MPNN_TRY(energy_reduce(cx));
     cx.forces_valid = true;
     return Status::ok();
 }
@@ -214,12 +225,28 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     cx.DP = (cx.D + 15) / 16 * 16;
     cx.rc = p->rc; cx.sigma = p->sigma; cx.e_scale = p->e_scale;
     cx.mass.assign(p->mass, p->mass + cx.S);
+    // Parameters as the arithmetic mode holds them: mode 1 keeps every parameter in fp64; modes 0
+    // and 2 hold the radial centres, C0, the contraction matrix, 1/s_t and e_scale rounded to fp32
+    // (the network weights too, see pack_weights), so every part of the path, including the fp64
+    // basis factors of the orbital sums, sees the same fp32 parameter values.
+    const bool p64 = cx.precision == 1;
+    auto held = [p64](double v) { return p64 ? v : (double)(float)v; };
+    std::vector<double> mu(cx.K);
+    for (int k = 0; k < cx.K; ++k) mu[k] = held(p->mu[k]);
     cx.inv_scale_host.resize(cx.T);
-    for (int t = 0; t < cx.T; ++t) cx.inv_scale_host[t] = (float)(1.0 / p->layer_scale[t]);
+    cx.inv_scale64_host.resize(cx.T);
+    for (int t = 0; t < cx.T; ++t) {
+        cx.inv_scale_host[t] = (float)(1.0 / p->layer_scale[t]);
+        cx.inv_scale64_host[t] = 1.0 / p->layer_scale[t];
+    }
     mpnn::ModelDev md{};
     for (int k = 0; k < cx.K; ++k) md.mu[k] = (float)p->mu[k];
+    md.e_scale64 = p->e_scale;
     for (int s = 0; s < cx.S; ++s) {
-        for (int k = 0; k < cx.K; ++k) md.c0[s * cx.K + k] = (float)p->c0[s * cx.K + k];
+        for (int k = 0; k < cx.K; ++k) {
+            md.c0[s * cx.K + k] = (float)p->c0[s * cx.K + k];
+            md.c0_64[s * cx.K + k] = p->c0[s * cx.K + k];
+        }
         md.mass[s] = p->mass[s];
         if (!(p->mass[s] > 0)) {
             delete ctx;
@@ -238,9 +265,9 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
     md.rc2 = p->rc * p->rc;
     {
         const double s2 = p->sigma * p->sigma;
-        for (int k = 0; k < cx.K; ++k) md.mu64[k] = p->mu[k];
+        for (int k = 0; k < cx.K; ++k) md.mu64[k] = mu[k];
         md.g_a0 = -1.0 / (2.0 * s2);
-        const double delta = cx.K > 1 ? p->mu[1] - p->mu[0] : 0.0;
+        const double delta = cx.K > 1 ? mu[1] - mu[0] : 0.0;
         md.g_e = delta / s2;
         // the chain R_{k+1} = R_k E g_c[k] (1 + g_eps[k] d) replaces exp(g_eps[k] d) by its first
         // two terms, so it needs |g_eps[k]| rc below 2e-5 (the dropped terms stay under 2e-10
@@ -249,23 +276,28 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
         // fp64 range; otherwise every channel is evaluated directly
         bool chain = true;
         for (int k = 0; k + 1 < cx.K; ++k) {
-            const double dk = p->mu[k + 1] - p->mu[k];
-            md.g_c[k] = std::exp(-dk * (p->mu[k] + p->mu[k + 1]) / (2.0 * s2));
+            const double dk = mu[k + 1] - mu[k];
+            md.g_c[k] = std::exp(-dk * (mu[k] + mu[k + 1]) / (2.0 * s2));
             md.g_eps[k] = (dk - delta) / s2;
             md.g_ce[k] = md.g_c[k] * md.g_eps[k];
             chain = chain && std::fabs(md.g_eps[k]) * p->rc < 2e-5 && std::isfinite(md.g_c[k]) && md.g_c[k] > 0.0;
         }
         double span = 0.0;
-        for (int k = 0; k < cx.K; ++k) span = std::max(span, std::fabs(p->rc - p->mu[k]) + std::fabs(p->mu[k]));
+        for (int k = 0; k < cx.K; ++k) span = std::max(span, std::fabs(p->rc - mu[k]) + std::fabs(mu[k]));
         chain = chain && std::fabs(md.g_e) * p->rc < 600.0 && span * span / (2.0 * s2) < 600.0;
         cx.chain = chain;
         md.inv_rc64 = 1.0 / p->rc;
         md.half_pi_over_rc = 0.5 * mpnn::kPi / p->rc;
     }
     cx.contracted = p->contraction != nullptr;
+    // reverse pass: the receiver pass with sender-major gathers; the two-direction row kernel
+    // (K <= 8) only on request (MPNN_TWO_DIR=1): measured 5.5 ms per layer on the 2.05M-atom Ag
+    // subdomain against 2.1 ms + gathers, bound by its 24 scattered 16-byte loads per edge
+    cx.two_dir = false;
+    if (const char *e = std::getenv("MPNN_TWO_DIR")) cx.two_dir = cx.K <= 8 && std::atoi(e) != 0;
     if (cx.contracted)
         for (int q = 0; q < cx.K * cx.K; ++q) {
-            md.C64[q] = p->contraction[q];
+            md.C64[q] = held(p->contraction[q]);
             md.C32[q] = (float)p->contraction[q];
         }
     Status s = cx.grow(cx.model, sizeof md);
@@ -335,7 +367,7 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
     Status s;
     if (pos) s = load_positions(cx, pos);
     if (!s.bad()) s = mpnn::evaluate(cx, forces);
-    if (!s.bad() && atom_energy) s = mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, 0, atom_energy);
+    if (!s.bad() && atom_energy) s = mpnn::unpermute_scalar(cx, cx.Ei.as<double>(), atom_energy);
     if (!s.bad() && energy) {
         s = mpnn::energy_sum(cx, energy);
         if (!s.bad() && !std::isfinite(*energy)) s = Status::err(MPNN_E_NONFINITE, "non-finite energy");
@@ -627,7 +659,7 @@ mpnn_status mpnn_get_intermediate(mpnn_ctx *ctx, int32_t which, int32_t t, doubl
                 MPNN_TRY(mpnn::unpermute_float(cx, cx.tmp_a.as<float>(), KM, 0, out));
                 break;
             case 3:
-                MPNN_TRY(mpnn::unpermute_float(cx, cx.Ei.as<float>(), 1, 0, out));
+                MPNN_TRY(mpnn::unpermute_scalar(cx, cx.Ei.as<double>(), out));
                 break;
             case 4:
                 if (t < 1) return Status::err(MPNN_E_INVALID_ARG, "dE/dc^t exists for t >= 1");

@@ -188,7 +188,8 @@ struct BasisHP {
     S P[KB];  // c_k R_k f_c, k = K0 + index
     S A[M];
 
-    __device__ __forceinline__ void eval(double dx, double dy, double dz, const float *__restrict__ cv,
+    template <class CV>
+    __device__ __forceinline__ void eval(double dx, double dy, double dz, const CV *__restrict__ cv,
                                          const ModelDev *__restrict__ md) {
         constexpr Mono<L> mono;
         const double d = sqrt(fma(dx, dx, fma(dy, dy, dz * dz)));
@@ -283,8 +284,8 @@ __device__ __forceinline__ double feature_q(const float (&O)[K][n_mono(L)]) {
     }
 }
 
-template <int K, int L, int KT, int... J>
-__device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], float s, float (&v)[16],
+template <int K, int L, int KT, class SC, int... J>
+__device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], SC s, float (&v)[16],
                                              std::integer_sequence<int, J...>) {
     ((v[J] = (float)(feature_q<K, L, 16 * KT + J>(O) * s)), ...);
 }
@@ -369,16 +370,16 @@ __device__ __forceinline__ void store_o_rows(const float (&O)[K][n_mono(L)], flo
     (store_o_tile<K, L, KT>(O, lds, base + (int64_t)KT * np * 16, slot), ...);
 }
 
-template <int K, int L, int KT>
-__device__ __forceinline__ void store_feature_tile(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *dst,
+template <int K, int L, int KT, class SC>
+__device__ __forceinline__ void store_feature_tile(const float (&O)[K][n_mono(L)], SC s, float4 *lds, float *dst,
                                                    int slot) {
     float v[16];
     feature_tile<K, L, KT>(O, s, v, std::make_integer_sequence<int, 16>{});
     store_tile(v, lds, dst, slot);
 }
 
-template <int K, int L, int... KT>
-__device__ __forceinline__ void store_feature_rows(const float (&O)[K][n_mono(L)], float s, float4 *lds, float *base,
+template <int K, int L, class SC, int... KT>
+__device__ __forceinline__ void store_feature_rows(const float (&O)[K][n_mono(L)], SC s, float4 *lds, float *base,
                                                    int64_t np, int slot, std::integer_sequence<int, KT...>) {
     (store_feature_tile<K, L, KT>(O, s, lds, base + (int64_t)KT * np * 16, slot), ...);
 }
@@ -722,12 +723,15 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
 // basis factors and their products kept in fp64 and one rounding when O is stored.  The K = 12,
 // L = 3 orbital block is too large for fp64 registers in one pass, so it takes several passes over
 // the edges (KB M a multiple of 16, so each pass owns whole 16-column tiles of the O rows).
-template <int K, int L, int KB, int P, bool CHAIN, bool CT>
+// C0 (layer 0): the neighbour's coefficients are the fp64 parameters C0[species] (node types),
+// not the fp32 copies in the node records.
+template <int K, int L, int KB, int P, bool CHAIN, bool CT, bool C0>
 __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, const double *__restrict__ pos,
                                                      const int64_t *__restrict__ slab_off,
                                                      const int32_t *__restrict__ nact,
                                                      const int32_t *__restrict__ act_n, const float *__restrict__ c,
                                                      const ModelDev *__restrict__ md,
+                                                     const int32_t *__restrict__ types,
                                                      const int32_t *__restrict__ row_perm, float *__restrict__ O) {
     constexpr int M = n_mono(L), Q0 = P * KB * M;
     constexpr int T0 = Q0 / 16, T1 = (KB == K ? pad16(K * M) : Q0 + KB * M) / 16;
@@ -754,7 +758,8 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
                 BasisHP<K, L, double, P * KB, KB, CHAIN, CT> b;   // this pass's radial channels only
                 const float *rv = c + v * rec_stride(K);   // node record: position, then messages
                 const double *pv = reinterpret_cast<const double *>(rv);
-                b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
+                if constexpr (C0) b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, md->c0_64 + types[v] * K, md);
+                else b.eval(pv[0] - xi, pv[1] - yi, pv[2] - zi, rv + kRecC, md);
 #pragma unroll
                 for (int k = 0; k < KB; ++k)
 #pragma unroll
@@ -777,7 +782,7 @@ __global__ __launch_bounds__(256) void k_aggregate64(int64_t n, int64_t np, cons
 // Density features from stored (column-tiled) O rows, fp64 sums; used after the fp64 passes.
 template <int K, int L>
 __global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const float *__restrict__ O,
-                                                  float inv_scale, float *__restrict__ feat) {
+                                                  double inv_scale, float *__restrict__ feat) {
     constexpr int M = n_mono(L), DT = pad16(n_feat(K, L)) / 16;
     __shared__ float4 lds[5 * kBlock];
     const int64_t i0 = (int64_t)blockIdx.x * kBlock;
@@ -988,6 +993,181 @@ __global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Two-direction reverse pass (models with K <= 8 channels).  The neighbour relation is symmetric:
+// j (or an image of j) is in row i exactly when i (or an image of i) is in row j, with the opposite
+// displacement r_ji = -r_ij and the same radial factors; the monomials change as
+// A_m(-r) = (-1)^l A_m(r) and their gradients as dA_m(-r) = -(-1)^l dA_m(r).  So row i can form, from
+// one basis evaluation per neighbour, both the terms of its own orbital sums (dE/dO_i, received
+// messages c_j) and those of neighbour j's orbital sums that i's message c_i enters (dE/dO_j).  With
+// G = dE/dO, u_k = sum_m G[k,m] A_m and sg_m = (-1)^l:
+//   dE/dc_i[k] = sum_j R_k f_c  sum_m sg_m G_j[k,m] A_m                         (Eq. 4, dE/dc term)
+//   F_i        = sum_j  s r/d + sum_m Q_m dA_m/dr,                                (Eq. 3-4)
+//      s   = sum_k (R'_k f_c + R_k f'_c) (c_j[k] u^i_k + c_i[k] u^j_k)
+//      Q_m = sum_k R_k f_c (c_j[k] G_i[k,m] + c_i[k] sg_m G_j[k,m])
+// Every output is a fixed-order sum over the row: no per-edge arrays, no sender-major gathers, no
+// ghost folds (a ghost's dE/dO is its owner's, refreshed per layer like the messages).
+// ------------------------------------------------------------------------------------------
+
+// dE/dO^t of every node (a ghost takes its owner's) with the node's position and messages: the
+// reverse records that the two-direction pass gathers.
+template <int K, int L>
+__global__ __launch_bounds__(256) void k_node_grad(int64_t NN, int64_t n, int64_t np, const int32_t *__restrict__ owner,
+                                                    const float *__restrict__ Grho, const float *__restrict__ Ot,
+                                                    const float *__restrict__ rec, float *__restrict__ R) {
+    constexpr int M = n_mono(L), RS = rev_stride(K, L);
+    static_assert(K <= kRevG - kRecC, "messages fit before dE/dO");
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= NN) return;
+    const int64_t o = v < n ? v : (int64_t)owner[v - n];
+    float G[K][M];
+    assemble_go_row<K, L>(Grho, Ot, np, o, G);
+    const float4 *src = reinterpret_cast<const float4 *>(rec + v * rec_stride(K));
+    float4 *dst = reinterpret_cast<float4 *>(R + v * RS);
+    // header: position and messages (the node's own record: a ghost has its own position)
+#pragma unroll
+    for (int q = 0; q < kRevG / 4; ++q) dst[q] = q < rec_stride(K) / 4 ? src[q] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < (RS - kRevG) / 4; ++q) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int f = 4 * q + e;
+            x[e] = f < K * M ? G[f / M][f % M] : 0.0f;
+        }
+        dst[kRevG / 4 + q] = float4{x[0], x[1], x[2], x[3]};
+    }
+}
+
+// The two-direction reverse pass of layer t over one receiver row per lane (LANES = 1) or per
+// 16-lane group (small systems).  WANT_GC: write dE/dc^t_i (t >= 1).  first: the force sum starts
+// (t = T-1), else it accumulates; last (t = 0): the forces are final, written sorted and in the
+// caller's order.
+template <int K, int L, bool WANT_GC, bool CT, bool NT, int LANES>
+__global__ __launch_bounds__(256) void k_reverse_edges(int first, int last, int64_t n, const int64_t *__restrict__ slab_off,
+                                                       const int32_t *__restrict__ nact,
+                                                       const int32_t *__restrict__ act_n, const float *__restrict__ R,
+                                                       const ModelDev *__restrict__ md,
+                                                       const int32_t *__restrict__ row_perm,
+                                                       float *__restrict__ Gc, double *__restrict__ Facc,
+                                                       double *__restrict__ F, const int32_t *__restrict__ perm,
+                                                       double *__restrict__ Fcaller) {
+    static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
+    constexpr int M = n_mono(L), RS = rev_stride(K, L);
+    constexpr Mono<L> mono;
+    int64_t i;
+    int q = 0;
+    if constexpr (LANES == 1) {
+        i = block_row(xcd_block() * blockDim.x, n, row_perm);
+        if (i >= n) return;
+    } else {
+        i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
+        q = (int)(threadIdx.x % LANES);
+    }
+    const bool row = i < n;
+    const int64_t ir_ = row ? i : 0;   // idle groups past the end read row 0 and write nothing
+    float mu[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
+    const float ir = md->inv_rc;
+    const float *Ri = R + ir_ * RS;
+    const double *pi = reinterpret_cast<const double *>(Ri);
+    const double xi = pi[0], yi = pi[1], zi = pi[2];
+    float ci[K], Gi[K][M];
+#pragma unroll
+    for (int k = 0; k < K; ++k) ci[k] = Ri[kRecC + k];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+#pragma unroll
+        for (int m = 0; m < M; ++m) Gi[k][m] = Ri[kRevG + k * M + m];
+    float gc[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) gc[k] = 0.0f;
+    double Fx = 0.0, Fy = 0.0, Fz = 0.0;
+    const int64_t b0 = sell_base(slab_off, ir_);
+    const int na = row ? nact[ir_] : 0;
+    for (int a = q; a < na; a += LANES) {
+        const int64_t j = ld_s<NT>(&act_n[b0 + kSlab * a]);
+        const float *Rj = R + j * RS;
+        const double *pj = reinterpret_cast<const double *>(Rj);
+        Basis<K, L, CT> b;
+        b.eval(__dsub_rn(pj[0], xi), __dsub_rn(pj[1], yi), __dsub_rn(pj[2], zi), md, mu);
+        float cj[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) cj[k] = Rj[kRecC + k];
+        float s = 0.0f, Q[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) Q[m] = 0.0f;
+        // receiving direction (row i's orbital sums)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float u = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) u = fmaf(Gi[k][m], b.A[m], u);
+            s = fmaf(cj[k] * u, b.Rd[k], s);
+            const float P = cj[k] * b.Rf[k];
+#pragma unroll
+            for (int m = 0; m < M; ++m) Q[m] = fmaf(P, Gi[k][m], Q[m]);
+        }
+        // sending direction (neighbour j's orbital sums, displacement -r)
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            float g[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) g[m] = (mono.l[m] & 1) ? -Rj[kRevG + k * M + m] : Rj[kRevG + k * M + m];
+            float u = 0.0f;
+#pragma unroll
+            for (int m = 0; m < M; ++m) u = fmaf(g[m], b.A[m], u);
+            if constexpr (WANT_GC) gc[k] = fmaf(b.Rf[k], u, gc[k]);
+            s = fmaf(ci[k] * u, b.Rd[k], s);
+            const float P = ci[k] * b.Rf[k];
+#pragma unroll
+            for (int m = 0; m < M; ++m) Q[m] = fmaf(P, g[m], Q[m]);
+        }
+        // angular part: dA_m/dx = lx x^(lx-1) y^ly z^lz / rc^lx..., i.e. lx times the monomial
+        // with one power of x fewer, over rc (likewise y, z); then the radial part along r / d
+        float ga[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
+            if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
+            if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
+        }
+        const float sd = s * b.inv_d;
+        Fx += (double)fmaf(sd, b.rx, ga[0] * ir);
+        Fy += (double)fmaf(sd, b.ry, ga[1] * ir);
+        Fz += (double)fmaf(sd, b.rz, ga[2] * ir);
+    }
+    if constexpr (LANES > 1) {
+        Fx = group_sum16(Fx);
+        Fy = group_sum16(Fy);
+        Fz = group_sum16(Fz);
+        if constexpr (WANT_GC) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) gc[k] = group_sum16(gc[k]);
+        }
+        if (!row || q != 0) return;
+    }
+    if constexpr (WANT_GC) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) Gc[i * K + k] = gc[k];
+    }
+    if (!first) {
+        Fx += Facc[3 * i];
+        Fy += Facc[3 * i + 1];
+        Fz += Facc[3 * i + 2];
+    }
+    if (last) {
+        F[3 * i] = Fx; F[3 * i + 1] = Fy; F[3 * i + 2] = Fz;
+        if (Fcaller) {
+            const int64_t c = perm[i];
+            Fcaller[3 * c] = Fx; Fcaller[3 * c + 1] = Fy; Fcaller[3 * c + 2] = Fz;
+        }
+    } else {
+        Facc[3 * i] = Fx; Facc[3 * i + 1] = Fy; Facc[3 * i + 2] = Fz;
+    }
+}
+
 // Sender-major gathers use kGatherLanes lanes per node (see group_sum16 above).
 
 // dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
@@ -1139,10 +1319,15 @@ __global__ __launch_bounds__(256) void k_assemble_go(int64_t n, int64_t np, cons
 const int32_t *row_perm(const Context &cx) { return cx.bucket ? cx.row_perm.as<int32_t>() : nullptr; }
 
 template <int K, int L, int KB, int P, bool CH, bool CT>
-void launch_agg64(Context &cx, const float *ct, float *Ot) {
-    k_aggregate64<K, L, KB, P, CH, CT><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
-        cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(),
-        ct, cx.model.as<ModelDev>(), row_perm(cx), Ot);
+void launch_agg64(Context &cx, const float *ct, float *Ot, bool c0) {
+    if (c0)
+        k_aggregate64<K, L, KB, P, CH, CT, true><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
+            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(),
+            ct, cx.model.as<ModelDev>(), cx.types.as<int32_t>(), row_perm(cx), Ot);
+    else
+        k_aggregate64<K, L, KB, P, CH, CT, false><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
+            cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(),
+            ct, cx.model.as<ModelDev>(), nullptr, row_perm(cx), Ot);
 }
 
 #define MPNN_DISPATCH_KL(K_, L_, CALL)                                                 \
@@ -1223,11 +1408,11 @@ Status aggregate(Context &cx, int t) {
     }
 #define MPNN_AGG64(KK, LL, KB, P)                                                                               \
     if (cx.contracted) {                                                                                        \
-        if (cx.chain) launch_agg64<KK, LL, KB, P, true, true>(cx, ct, Ot);                                      \
-        else launch_agg64<KK, LL, KB, P, false, true>(cx, ct, Ot);                                              \
+        if (cx.chain) launch_agg64<KK, LL, KB, P, true, true>(cx, ct, Ot, t == 0);                                      \
+        else launch_agg64<KK, LL, KB, P, false, true>(cx, ct, Ot, t == 0);                                              \
     } else {                                                                                                    \
-        if (cx.chain) launch_agg64<KK, LL, KB, P, true, false>(cx, ct, Ot);                                     \
-        else launch_agg64<KK, LL, KB, P, false, false>(cx, ct, Ot);                                             \
+        if (cx.chain) launch_agg64<KK, LL, KB, P, true, false>(cx, ct, Ot, t == 0);                                     \
+        else launch_agg64<KK, LL, KB, P, false, false>(cx, ct, Ot, t == 0);                                             \
     }
     if (cx.K == 12 && cx.L == 3) {
         MPNN_AGG64(12, 3, 4, 0);
@@ -1245,7 +1430,7 @@ Status aggregate(Context &cx, int t) {
 #undef MPNN_AGG64
     MPNN_HIP(hipGetLastError());
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_features<KK, LL><<<(unsigned)(cx.np / kBlock), kBlock, 0, cx.stream>>>(
-                                      cx.n, cx.np, Ot, cx.inv_scale_host[t], Ft)));
+                                      cx.n, cx.np, Ot, cx.inv_scale64_host[t], Ft)));
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }
@@ -1307,6 +1492,61 @@ Status backward_layer(Context &cx, int t) {
 #undef MPNN_BWD_NT
 #undef MPNN_BWD_LG
 #undef MPNN_BWD_SPLIT
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status node_grad(Context &cx, int t) {
+    ProfScope ps_(cx, kProfNodeGrad);
+    if (cx.NN == 0) return Status::ok();
+    const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
+    const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
+    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
+#define MPNN_NG(KK, LL)                                                                                        \
+    k_node_grad<KK, LL><<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.n, cx.np, cx.ghost_owner.as<int32_t>(), \
+                                                                    Gt, Ot, ct, cx.Rn.as<float>())
+    if (cx.K == 8 && cx.L == 2) MPNN_NG(8, 2);
+    else if (cx.K == 4 && cx.L == 2) MPNN_NG(4, 2);
+    else if (cx.K == 2 && cx.L == 1) MPNN_NG(2, 1);
+    else return Status::err(MPNN_E_INVALID_ARG, "two-direction reverse pass: unsupported (K, L)");
+#undef MPNN_NG
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status reverse_edges(Context &cx, int t, double *F_caller) {
+    ProfScope ps_(cx, kProfReverseEdges);
+    if (cx.n == 0) return Status::ok();
+    float *Gct = cx.Gc.as<float>() + (int64_t)t * cx.NN * cx.K;
+    const bool gc = t >= 1, first = t == cx.T - 1, last = t == 0;
+    auto launch = [&](auto kl, auto gcf, auto ctf, auto ntf, auto lanes) {
+        constexpr int KK = decltype(kl)::value / 10, LL = decltype(kl)::value % 10;
+        constexpr int LN = decltype(lanes)::value;
+        const unsigned grid = LN == 1 ? grid_xcd(cx.n) : grid_for(cx.n * LN);
+        k_reverse_edges<KK, LL, decltype(gcf)::value, decltype(ctf)::value, decltype(ntf)::value, LN>
+            <<<grid, kBlock, 0, cx.stream>>>(first ? 1 : 0, last ? 1 : 0, cx.n, cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), cx.Rn.as<float>(),
+            cx.model.as<ModelDev>(), LN == 1 ? row_perm(cx) : nullptr, Gct, cx.Frecv.as<double>(), cx.F.as<double>(),
+            cx.perm.as<int32_t>(), F_caller);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    auto by_lanes = [&](auto kl, auto gcf, auto ctf) {
+        if (cx.lane_groups) launch(kl, gcf, ctf, F_{}, std::integral_constant<int, kGatherLanes>{});
+        else if (cx.nt) launch(kl, gcf, ctf, T_{}, std::integral_constant<int, 1>{});
+        else launch(kl, gcf, ctf, F_{}, std::integral_constant<int, 1>{});
+    };
+    auto by_ct = [&](auto kl, auto gcf) {
+        if (cx.contracted) by_lanes(kl, gcf, T_{});
+        else by_lanes(kl, gcf, F_{});
+    };
+    auto by_gc = [&](auto kl) {
+        if (gc) by_ct(kl, T_{});
+        else by_ct(kl, F_{});
+    };
+    if (cx.K == 8 && cx.L == 2) by_gc(std::integral_constant<int, 82>{});
+    else if (cx.K == 4 && cx.L == 2) by_gc(std::integral_constant<int, 42>{});
+    else if (cx.K == 2 && cx.L == 1) by_gc(std::integral_constant<int, 21>{});
+    else return Status::err(MPNN_E_INVALID_ARG, "two-direction reverse pass: unsupported (K, L)");
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

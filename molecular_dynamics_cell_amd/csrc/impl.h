@@ -41,7 +41,7 @@ enum ProfId {
     kProfBuildSort = 0, kProfBuildGhost, kProfBuildRows, kProfBuildTranspose, kProfBuildSpecies,
     kProfGhostPos, kProfCompact, kProfAggregate, kProfNetForward, kProfNetEnergy, kProfNetBackward,
     kProfGhostFeat, kProfBackwardLayer, kProfMessageGrad, kProfGhostFold, kProfForceGather,
-    kProfKickDrift, kProfKick, kProfReduce, kProfCount
+    kProfKickDrift, kProfKick, kProfReduce, kProfNodeGrad, kProfReverseEdges, kProfCount
 };
 extern const char *const kProfNames[kProfCount];
 
@@ -127,10 +127,12 @@ struct Context {
     bool bucket = false;   // row kernels take rows in row_perm order (ragged row lengths)
     bool nt = false;       // per-edge streams far larger than the caches, rows in order: nontemporal
     bool lane_groups = false;   // small systems: the row kernels give each row a 16-lane group
+    Buf Rn;       // float [NN][rev_stride]: reverse records of the current layer (two-direction pass)
+    bool two_dir = false;  // reverse pass in one two-direction row kernel (no per-edge arrays, no transpose)
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
-    Buf Ei;       // float [n]
-    Buf red;      // double scratch for reductions
+    Buf Ei;       // double [n]: E_i
+    Buf red;      // double [2 red_blocks(n) + 2]: energy partials, E, kinetic partials, KE
     Buf flag;     // uint64 [4]: displacement flag, max displacement bits
     Buf tmp_a, tmp_b, tmp_c, tmp_d, tmp_scan;  // build scratch
 
@@ -169,7 +171,8 @@ struct Context {
 
     Buf types_caller;             // int32 [n] species in caller order (for rebuilds)
     Buf stage_pos, stage_vel;     // double [n][3] caller-order staging
-    std::vector<float> inv_scale_host;  // 1 / s_t
+    std::vector<float> inv_scale_host;     // 1 / s_t rounded to fp32 (arithmetic modes 0 and 2)
+    std::vector<double> inv_scale64_host;  // 1 / s_t (mode 1)
 
     Status grow(Buf &b, size_t bytes);
     Status grow_keep(Buf &b, size_t bytes, size_t keep);
@@ -204,6 +207,10 @@ Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagno
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
 Status transpose_active(Context &cx);             // t_act alone (T == 1)
 Status force_gather(Context &cx, double *F_caller);
+// two-direction reverse pass (models with K <= 8): the layer's reverse records, then per row the
+// layer's dE/dc and force terms of both directions of every edge
+Status node_grad(Context &cx, int t);
+Status reverse_edges(Context &cx, int t, double *F_caller);
 
 // ---- mlp.hip ----
 Status mlp_forward(Context &cx, int t);           // c^{t+1} from rho^t (t < T-1)
@@ -212,7 +219,9 @@ Status mlp_backward(Context &cx, int t);          // dE/drho^t from dE/dc^{t+1}
 Status pack_weights(Context &cx, const double *mlp);
 
 // ---- integrate.hip ----
-Status energy_sum(Context &cx, double *E_host);
+int64_t red_blocks(int64_t n);                   // partial sums of the fixed-order reductions
+Status energy_reduce(Context &cx);               // E = sum E_i on the device (every evaluation)
+Status energy_sum(Context &cx, double *E_host);  // the last evaluation's E to the host
 Status kick_drift(Context &cx, double dt);       // first half-kick + drift + skin test
 Status kick(Context &cx, double dt);             // second half-kick
 Status skin_check(Context &cx);                  // displacement test only
@@ -221,6 +230,8 @@ Status read_skin_flag(Context &cx, bool *exceeded, double *max_disp);
 Status reset_skin_flag(Context &cx);
 Status unpermute_vec3(Context &cx, const double *sorted, double *caller);
 Status permute_in_vec3(Context &cx, const double *caller, double *sorted);
+// one double per atom, sorted -> caller order
+Status unpermute_scalar(Context &cx, const double *sorted, double *caller);
 // sorted rows of `width` floats (row-major, or column-tiled with row count np when np > 0)
 Status unpermute_float(Context &cx, const float *sorted, int width, int64_t np, double *caller);
 // sorted rows of `width` floats at a row stride of `stride` floats

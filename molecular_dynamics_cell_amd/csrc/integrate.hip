@@ -33,8 +33,8 @@ __device__ double block_sum(F item, int64_t n) {
     return sh[0];
 }
 
-__global__ void k_sum_float(int64_t n, const float *__restrict__ x, double *__restrict__ part) {
-    double s = block_sum([&](int64_t i) { return (double)x[i]; }, n);
+__global__ void k_sum_part(int64_t n, const double *__restrict__ x, double *__restrict__ part) {
+    double s = block_sum([&](int64_t i) { return x[i]; }, n);
     if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
 
@@ -63,8 +63,7 @@ __global__ void k_kinetic(int64_t n, const double *__restrict__ vel, const int32
     if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
 
-Status reduce_to_host(Context &cx, int64_t blocks, double *host) {
-    double *part = cx.red.as<double>();
+Status reduce_to_host(Context &cx, double *part, int64_t blocks, double *host) {
     double *out = part + blocks;
     k_sum_double<<<1, kRedThreads, 0, cx.stream>>>(blocks, part, out);
     MPNN_HIP(hipGetLastError());
@@ -73,11 +72,15 @@ Status reduce_to_host(Context &cx, int64_t blocks, double *host) {
     return Status::ok();
 }
 
+}  // namespace
+
 int64_t red_blocks(int64_t n) {
     const int64_t per = (int64_t)kRedThreads * kRedItems;
     int64_t b = (n + per - 1) / per;
     return b > 0 ? b : 1;
 }
+
+namespace {
 
 // v += (dt/2) a F / m; x += dt v; flag an atom that moved more than skin/2 since the build.
 // First half-kick and drift of every atom, and the largest displacement since the last build
@@ -157,6 +160,12 @@ __global__ void k_permute_in3(int64_t n, const int32_t *__restrict__ perm, const
     for (int a = 0; a < 3; ++a) out[3 * s + a] = in[3 * c + a];
 }
 
+__global__ void k_unpermute1(int64_t n, const int32_t *__restrict__ perm, const double *__restrict__ in,
+                             double *__restrict__ out) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < n) out[perm[s]] = in[s];
+}
+
 __global__ void k_unpermute_float(int64_t n, int width, int64_t np, const int32_t *__restrict__ perm,
                                   const float *__restrict__ in, double *__restrict__ out) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -168,17 +177,32 @@ __global__ void k_unpermute_float(int64_t n, int width, int64_t np, const int32_
 
 }  // namespace
 
-Status energy_sum(Context &cx, double *E_host) {
+// E = sum_i E_i ([JACS] "Parallelization Algorithm", Eq. 3) in a fixed tree, left on the device at
+// red[red_blocks(n)] (no allocation, no host transfer: it runs inside every evaluation, also in a
+// captured graph).  The reduction buffer is sized at the neighbour build.
+Status energy_reduce(Context &cx) {
     ProfScope ps_(cx, kProfReduce);
+    if (cx.n == 0) return Status::ok();
+    const int64_t b = red_blocks(cx.n);
+    if (cx.red.bytes < sizeof(double) * (size_t)(b + 1)) return Status::err(MPNN_E_STATE, "reduction buffer not sized");
+    double *part = cx.red.as<double>();
+    k_sum_part<<<(unsigned)b, kRedThreads, 0, cx.stream>>>(cx.n, cx.Ei.as<double>(), part);
+    MPNN_HIP(hipGetLastError());
+    k_sum_double<<<1, kRedThreads, 0, cx.stream>>>(b, part, part + b);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+// The energy of the last evaluation (energy_reduce's result) copied to the host.
+Status energy_sum(Context &cx, double *E_host) {
     if (cx.n == 0) {
         *E_host = 0.0;
         return Status::ok();
     }
-    const int64_t b = red_blocks(cx.n);
-    MPNN_TRY(cx.grow(cx.red, sizeof(double) * (b + 1)));
-    k_sum_float<<<(unsigned)b, kRedThreads, 0, cx.stream>>>(cx.n, cx.Ei.as<float>(), cx.red.as<double>());
-    MPNN_HIP(hipGetLastError());
-    return reduce_to_host(cx, b, E_host);
+    MPNN_HIP(hipMemcpyAsync(E_host, cx.red.as<double>() + red_blocks(cx.n), sizeof(double), hipMemcpyDeviceToHost,
+                            cx.stream));
+    MPNN_HIP(hipStreamSynchronize(cx.stream));
+    return Status::ok();
 }
 
 Status kinetic_energy(Context &cx, double *ke_host) {
@@ -187,12 +211,14 @@ Status kinetic_energy(Context &cx, double *ke_host) {
         *ke_host = 0.0;
         return Status::ok();
     }
+    // the second half of the reduction buffer (the first holds the potential energy's partials)
     const int64_t b = red_blocks(cx.n);
-    MPNN_TRY(cx.grow(cx.red, sizeof(double) * (b + 1)));
+    if (cx.red.bytes < sizeof(double) * (size_t)(2 * b + 2)) return Status::err(MPNN_E_STATE, "reduction buffer not sized");
+    double *part = cx.red.as<double>() + b + 1;
     k_kinetic<<<(unsigned)b, kRedThreads, 0, cx.stream>>>(cx.n, cx.vel.as<double>(), cx.types.as<int32_t>(),
-                                                          cx.model.as<ModelDev>(), cx.red.as<double>());
+                                                          cx.model.as<ModelDev>(), part);
     MPNN_HIP(hipGetLastError());
-    return reduce_to_host(cx, b, ke_host);
+    return reduce_to_host(cx, part, b, ke_host);
 }
 
 Status kick_drift(Context &cx, double dt) {
@@ -269,6 +295,13 @@ Status unpermute_rows(Context &cx, const float *sorted, int width, int stride, d
     if (cx.n == 0) return Status::ok();
     k_unpermute_rows<<<grid_for(cx.n * width), kBlock, 0, cx.stream>>>(cx.n, width, stride, cx.perm.as<int32_t>(),
                                                                       sorted, caller);
+    MPNN_HIP(hipGetLastError());
+    return Status::ok();
+}
+
+Status unpermute_scalar(Context &cx, const double *sorted, double *caller) {
+    if (cx.n == 0) return Status::ok();
+    k_unpermute1<<<grid_for(cx.n), kBlock, 0, cx.stream>>>(cx.n, cx.perm.as<int32_t>(), sorted, caller);
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

@@ -100,12 +100,13 @@ struct NetArgs {
     int64_t stride;
     int64_t oW1, oW2, oW3, oW1t, oW2t, oW3t, ob1, ob2, ob3;
     int S;
-    float inv_scale, e_scale;
+    float inv_scale, e_scale;   // fp32 parameters (modes 0 and 2)
+    double e_scale64;           // fp64 parameter (mode 1)
     const int32_t *sp_list;
     int64_t sp_off[kMaxSpecies + 1];
     int32_t tile_start[kMaxSpecies + 1];
     float *c_next;         // forward: c^{t+1} of node v at c_next[v * rec_stride(K) + k]
-    float *Ei;             // energy: E_i [n]
+    double *Ei;            // energy: E_i [n]
     const float *Gc;       // backward: dE/dc^{t+1} [*][K]
     float *Grho;           // energy/backward: dE/drho^t, column-tiled [np][DP]
     int64_t np;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
                     if (k < K) a.c_next[me[c] * rec_stride(K) + k] = (float)y[0][c][i];
                 }
             } else {
-                if (grp == 0) a.Ei[me[c]] = (float)((double)a.e_scale * y[0][c][0]);
+                if (grp == 0) a.Ei[me[c]] = (double)a.e_scale * y[0][c][0];
             }
         }
     }
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(64, 2) void k_net64(const NetArgs a) {
                     if (k < K) a.c_next[me * rec_stride(K) + k] = (float)y[0][i];
                 }
             } else {
-                if (grp == 0) a.Ei[me] = (float)((double)a.e_scale * y[0][0]);
+                if (grp == 0) a.Ei[me] = a.e_scale64 * y[0][0];
             }
         }
     }
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(64, 2) void k_net64(const NetArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int k = grp + 4 * i;
-            if constexpr (MODE == kEnergy) gy[i] = (k == 0) ? (double)a.e_scale : 0.0;
+            if constexpr (MODE == kEnergy) gy[i] = (k == 0) ? a.e_scale64 : 0.0;
             else gy[i] = (k < K && me >= 0) ? (double)a.Gc[me * K + k] : 0.0;
         }
         doublex4 g2[HT];
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(64) void k_net16(const NetArgs a) {
                     if (k < K) a.c_next[me[c] * rec_stride(K) + k] = y[0][c][i];
                 }
             } else {
-                if (grp == 0) a.Ei[me[c]] = a.e_scale * y[0][c][0];
+                if (grp == 0) a.Ei[me[c]] = (double)a.e_scale * (double)y[0][c][0];
             }
         }
     }
@@ -780,6 +781,7 @@ NetArgs make_args(Context &cx, int t, int mode) {
     a.F = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
     a.Grho = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
     a.e_scale = (float)cx.e_scale;
+    a.e_scale64 = cx.e_scale;
     a.inv_scale = cx.inv_scale_host[t];
     return a;
 }
@@ -968,7 +970,7 @@ Status mlp_forward(Context &cx, int t) {
 Status mlp_energy(Context &cx) {
     ProfScope ps_(cx, kProfNetEnergy);
     NetArgs a = make_args(cx, cx.T - 1, kEnergy);
-    a.Ei = cx.Ei.as<float>();
+    a.Ei = cx.Ei.as<double>();
     MPNN_DISPATCH_NET(kEnergy, a);
     return Status::ok();
 }

@@ -315,13 +315,17 @@ def _f32(a):
     return np.asarray(a, np.float64).astype(np.float32).astype(np.float64)
 
 
-def random_params(spec: ModelSpec, seed: int, masses, layer_scale=None, e_scale: float = 1.0) -> Params:
+def random_params(spec: ModelSpec, seed: int, masses, layer_scale=None, e_scale: float = 1.0,
+                  round_f32: bool = True) -> Params:
     """Random-init weights: W, b ~ N(0, 1/fan_in); C0 ~ N(0, 1).  Draw order: C0, then for
     t in 0..T-1, for s in 0..S-1: W1, b1, W2, b2, W3, b3.
 
-    Every drawn value (and every radial centre) is rounded to the nearest float32, so an fp32
-    implementation holds exactly the same parameters as an fp64 one; the frozen layer and energy
-    scales are powers of two for the same reason."""
+    With round_f32 (the benchmark models), every drawn value (and every radial centre) is rounded
+    to the nearest float32, so an fp32 implementation holds exactly the same parameters as an fp64
+    one; the frozen layer and energy scales are powers of two for the same reason.  round_f32=False
+    keeps the fp64 draws (the same values before rounding), for checking how each arithmetic mode
+    holds parameters that fp32 cannot represent."""
+    _f32 = globals()["_f32"] if round_f32 else (lambda a: np.asarray(a, np.float64))
     rng = _rng(seed)
     K, L, T, H, S = spec.K, spec.L, spec.T, spec.H, spec.n_species
     D = K * (K + 1) * (L + 1) // 2

@@ -9,7 +9,7 @@ import torch
 from molecular_dynamics_cell_amd import binding
 from molecular_dynamics_cell_amd import inputs as I
 from tests import systems
-from tests.gpu_util import check_ef, gpu_model, oracle_ef, say
+from tests.gpu_util import EI_TOL_BF16, check_ef, check_ei, gpu_model, oracle_ef, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,11 +30,13 @@ def test_bf16_networks(name):
     p.spec.precision = 2
     say(f"[bf16] {name} n={s.n}")
     m = gpu_model(p, s)
-    E, F, _ = m.energy_forces()
+    E, F, Ei = m.energy_forces(atom_energy=True)
     F = F.cpu().numpy()
+    Ei = Ei.cpu().numpy()
     m.close()
     torch.cuda.empty_cache()
-    Eo, Fo, _ = oracle_ef(p, s)
+    Eo, Fo, Eio = oracle_ef(p, s)
+    check_ei(Ei, Eio, tol=EI_TOL_BF16, label=f"{name} bf16 E_i")
     check_ef(E, F, Eo, Fo, e_tol=1e-3, f_tol=2e-3, label=f"{name} bf16")
 
 

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from molecular_dynamics_cell_amd import inputs as I
-from tests.gpu_util import canonical_pairs, check_ef, gpu_model, say
+from tests.gpu_util import canonical_pairs, check_ef, check_ei, gpu_model, say
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,5 @@ def test_full_size_parity(cfg):
     t0 = time.time()
     Eo, Fo, Eio = oracle.energy_forces(oracle.Model(p), pos, s.types, s.box, pair_list=pl)
     say(f"[full cfg{cfg}] oracle E/F in {time.time() - t0:.1f} s ({oracle.num_threads()} threads)")
-    err_i = np.abs(Ei - Eio).max() / np.abs(Eio).max()
-    say(f"[full cfg{cfg}] max per-atom energy error {err_i:.2e} (relative to max |E_i|)")
+    check_ei(Ei, Eio, label=f"full cfg{cfg} E_i")
     check_ef(E, F, Eo, Fo, label=f"full cfg{cfg}")

@@ -7,7 +7,7 @@ import torch
 
 from molecular_dynamics_cell_amd import inputs as I
 from tests import systems
-from tests.gpu_util import canonical_pairs, check_ef, gpu_model, oracle_ef, say
+from tests.gpu_util import canonical_pairs, check_ef, check_ei, gpu_model, oracle_ef, say
 
 import oracle
 
@@ -75,8 +75,7 @@ def test_energy_forces(name):
         err = np.abs(G - dump["GO"][t]).max() / (np.abs(dump["GO"][t]).max() + 1e-30)
         say(f"  dE/dO^{t}: rel max err {err:.2e}")
         assert err < 1e-3
-    err = np.abs(Ei.cpu().numpy() - Eio).max() / np.abs(Eio).max()
-    say(f"  E_i: rel max err {err:.2e}")
+    check_ei(Ei.cpu().numpy(), Eio, label=f"{name} E_i")
     check_ef(E, F.cpu().numpy(), Eo, Fo, label=name)
 
 

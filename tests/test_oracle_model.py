@@ -345,3 +345,17 @@ def test_no_refresh_negative_control(orc, T):
     else:        # ghosts with incomplete neighbour lists give wrong messages
         assert abs(Ed - E) > 1e-6 * abs(E)
         assert np.abs(Fd - F).max() > 1e-6 * np.abs(F).max()
+
+
+def test_fp32_parameter_rounding_is_visible(orc):
+    """The fp64-parameter GPU tests compare arithmetic mode 1 with the oracle on fp64 parameters and
+    modes 0 and 2 with the oracle on the fp32-rounded copy; the two references differ by more than
+    the energy gate's resolution on the 432-atom alloy, so those tests tell the holdings apart."""
+    from tests import systems
+    from tests.params_util import held_fp32, unrounded_params
+    s = systems.hea(6)
+    p = unrounded_params(3)
+    assert not np.array_equal(p.mlp[0][0]["W1"], p.mlp[0][0]["W1"].astype(np.float32))
+    E64, _, _ = _eval(orc, orc.Model(p), s)
+    E32, _, _ = _eval(orc, orc.Model(held_fp32(p)), s)
+    assert abs(E64 - E32) / abs(E64) > 1e-7
