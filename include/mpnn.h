@@ -174,6 +174,23 @@ mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t
 mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
                                double *atom_energy);
 
+/* The energy and forces of mpnn_energy_forces for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results (bitwise) as mpnn_energy_forces, but the call allocates nothing: every
+ * buffer it uses was sized by the last neighbour build, and its one per-call scratch, the partial
+ * sums of the fixed-order energy reduction, is a fixed device array of 16,385 doubles (128 KiB)
+ * that the library holds on each GPU until the process ends.  Limits: at most 16,384 x 2,048 =
+ * 33,554,432 atoms (MPNN_E_CAPACITY beyond); it never rebuilds the neighbour list: when new
+ * positions moved an atom more than skin/2 since the last build it returns MPNN_E_SKIN (the
+ * positions are taken, the forces are not computed, and the next mpnn_energy_forces or
+ * mpnn_md_step rebuilds first); MPNN_E_STATE before a build.  The fixed array is shared by every
+ * context on the GPU and keeps the last call's contents: calls that overlap on one GPU (two
+ * contexts on different streams or threads) race and must be serialised by the caller.
+ * `energy` (host out) synchronises the stream; otherwise the call only enqueues work, except that
+ * new positions are checked against the skin with one stream synchronisation. */
+mpnn_status mpnn_energy_forces_noalloc(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
+                                       double *atom_energy);
+
 /* n_steps velocity-Verlet steps of dt_fs (NVE; [JACS] "Strong Scaling" checks the parallel code by the
  * energy conservation of NVE runs; the integrator itself is not on the pages: half-kick, drift,
  * new forces, half-kick, a = F / m in A/fs^2 with 1 eV/(A amu) = 9.648533212e-3 A/fs^2).  After the

@@ -73,6 +73,7 @@ def lib():
             "mpnn_set_stream": ([p, p], st),
             "mpnn_build_neighbors": ([p, p, p, i64, C.POINTER(C.c_double), d, d], st),
             "mpnn_energy_forces": ([p, p, C.POINTER(C.c_double), p, p], st),
+            "mpnn_energy_forces_noalloc": ([p, p, C.POINTER(C.c_double), p, p], st),
             "mpnn_md_step": ([p, d, i32, i32, C.POINTER(MDStats)], st),
             "mpnn_set_state": ([p, p, p], st),
             "mpnn_get_state": ([p, p, p, C.POINTER(C.c_int64)], st),
@@ -189,6 +190,20 @@ class MPNN:
         self._check(lib().mpnn_energy_forces(self.h, _dptr(pos), C.byref(E) if energy else None,
                                              _dptr(F), _dptr(Ei)))
         return E.value if energy else None, F, Ei
+
+    def energy_forces_noalloc(self, pos: torch.Tensor = None, forces: torch.Tensor = None,
+                              atom_energy: torch.Tensor = None, energy=True):
+        """mpnn_energy_forces_noalloc: the caller passes the output tensors ([n][3] and [n] fp64 on
+        the device, or None); the library allocates nothing."""
+        E = C.c_double(0.0)
+        if pos is not None:
+            pos = pos.to(self.device, torch.float64).contiguous()
+        for t, shape in ((forces, (self.n, 3)), (atom_energy, (self.n,))):
+            if t is not None and (t.dtype != torch.float64 or tuple(t.shape) != shape or not t.is_contiguous()):
+                raise ValueError(f"output must be a contiguous float64 tensor of shape {shape}")
+        self._check(lib().mpnn_energy_forces_noalloc(self.h, _dptr(pos), C.byref(E) if energy else None,
+                                                     _dptr(forces), _dptr(atom_energy)))
+        return E.value if energy else None
 
     def md_step(self, dt, n_steps, rebuild_every=0, stats=True):
         st = MDStats()

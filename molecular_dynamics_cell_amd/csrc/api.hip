@@ -140,7 +140,7 @@ bool supported(int K, int L, int H) {
 
 // One energy/force evaluation on the current (sorted) state: paper Eq. 1-2 forward with the
 // per-layer ghost refresh, then Eq. 3-5 backward with the ghost->owner folds.
-Status evaluate(Context &cx, double *F_caller) {
+Status evaluate(Context &cx, double *F_caller, double *red_part = nullptr) {
     MPNN_TRY(refresh_ghost_positions(cx));
     MPNN_TRY(compact_active(cx));
     for (int t = 0; t < cx.T; ++t) {
@@ -169,7 +169,7 @@ Status evaluate(Context &cx, double *F_caller) {
         if (cx.T == 1) MPNN_TRY(transpose_active(cx));
         MPNN_TRY(force_gather(cx, F_caller));
     }
-    MPNN_TRY(energy_reduce(cx));
+    MPNN_TRY(energy_reduce(cx, red_part));
     cx.forces_valid = true;
     return Status::ok();
 }
@@ -300,7 +300,9 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
             md.C64[q] = held(p->contraction[q]);
             md.C32[q] = (float)p->contraction[q];
         }
-    Status s = cx.grow(cx.model, sizeof md);
+    // the fixed reduction array of mpnn_energy_forces_noalloc, on the device current at create
+    Status s = mpnn::static_scratch(&cx.scratch);
+    if (!s.bad()) s = cx.grow(cx.model, sizeof md);
     if (!s.bad()) {
         if (hipMemcpy(cx.model.p, &md, sizeof md, hipMemcpyHostToDevice) != hipSuccess)
             s = Status::err(MPNN_E_HIP, "upload of model constants failed");
@@ -366,6 +368,8 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
     if (!cx.built) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "mpnn_build_neighbors first"));
     Status s;
     if (pos) s = load_positions(cx, pos);
+    else if (cx.stale) s = mpnn::rebuild_from_state(cx);
+    if (!s.bad()) cx.stale = false;
     if (!s.bad()) s = mpnn::evaluate(cx, forces);
     if (!s.bad() && atom_energy) s = mpnn::unpermute_scalar(cx, cx.Ei.as<double>(), atom_energy);
     if (!s.bad() && energy) {
@@ -377,6 +381,47 @@ mpnn_status mpnn_energy_forces(mpnn_ctx *ctx, const double *pos, double *energy,
         cx.prof_harvest();
     }
     return mpnn::finish(ctx, s);
+}
+
+mpnn_status mpnn_energy_forces_noalloc(mpnn_ctx *ctx, const double *pos, double *energy, double *forces,
+                                       double *atom_energy) {
+    if (!ctx) return MPNN_E_INVALID_ARG;
+    mpnn::Context &cx = ctx->cx;
+    if (!cx.built || cx.stale)
+        return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "needs a current neighbour list (mpnn_build_neighbors)"));
+    if (!cx.scratch) return mpnn::finish(ctx, Status::err(MPNN_E_STATE, "no fixed scratch on this device"));
+    if (mpnn::red_blocks(cx.n) > mpnn::kStaticPartials)
+        return mpnn::finish(ctx, Status::err(MPNN_E_CAPACITY, "more atoms than the fixed scratch holds (" +
+                                                                  std::to_string(mpnn::kStaticPartials * 2048) + ")"));
+    auto run = [&]() -> Status {
+        if (pos && cx.n > 0) {
+            // the caller's array is device memory: permute it straight into the sorted state
+            MPNN_TRY(mpnn::permute_in_vec3(cx, pos, cx.pos.as<double>()));
+            MPNN_TRY(mpnn::reset_skin_flag(cx));
+            MPNN_TRY(mpnn::skin_check(cx));
+            bool ex = false;
+            double md = 0;
+            MPNN_TRY(mpnn::read_skin_flag(cx, &ex, &md));
+            cx.forces_valid = false;
+            if (ex) {
+                cx.stale = true;   // the next allocating call rebuilds first
+                return Status::err(MPNN_E_SKIN, "an atom moved more than skin/2 since the last build: a rebuild "
+                                                "(which may allocate) is needed");
+            }
+        }
+        MPNN_TRY(mpnn::evaluate(cx, forces, cx.scratch));
+        if (atom_energy) MPNN_TRY(mpnn::unpermute_scalar(cx, cx.Ei.as<double>(), atom_energy));
+        if (energy) {
+            MPNN_TRY(mpnn::energy_sum(cx, energy, cx.scratch));
+            if (!std::isfinite(*energy)) return Status::err(MPNN_E_NONFINITE, "non-finite energy");
+        }
+        // the context's own reduction buffer holds the last evaluation's energy for later calls
+        if (cx.n > 0)
+            MPNN_HIP(hipMemcpyAsync(cx.red.as<double>() + mpnn::red_blocks(cx.n), cx.scratch + mpnn::red_blocks(cx.n),
+                                    sizeof(double), hipMemcpyDeviceToDevice, cx.stream));
+        return Status::ok();
+    };
+    return mpnn::finish(ctx, run());
 }
 
 }  // extern "C"
@@ -518,6 +563,11 @@ mpnn_status mpnn_md_step(mpnn_ctx *ctx, double dt_fs, int32_t n_steps, int32_t r
     auto run = [&]() -> Status {
         int64_t rebuilds = 0;
         double max_disp = 0.0;
+        if (cx.stale) {
+            MPNN_TRY(mpnn::rebuild_from_state(cx));
+            cx.stale = false;
+            ++rebuilds;
+        }
         if (!cx.forces_valid) MPNN_TRY(mpnn::evaluate(cx, nullptr));
         MPNN_TRY(mpnn::reset_skin_flag(cx));
         int eager_left = 0;   // after a rolled-back chunk, its steps run eagerly

@@ -129,6 +129,8 @@ struct Context {
     bool lane_groups = false;   // small systems: the row kernels give each row a 16-lane group
     Buf Rn;       // float [NN][rev_stride]: reverse records of the current layer (two-direction pass)
     bool two_dir = false;  // reverse pass in one two-direction row kernel (no per-edge arrays, no transpose)
+    double *scratch = nullptr;  // device address of the fixed reduction array (mpnn_energy_forces_noalloc)
+    bool stale = false;         // positions moved beyond skin/2 without a rebuild: the next call rebuilds
     Buf Frecv;    // double [n][3]
     Buf F;        // double [n][3] (sorted)
     Buf Ei;       // double [n]: E_i
@@ -220,8 +222,13 @@ Status pack_weights(Context &cx, const double *mlp);
 
 // ---- integrate.hip ----
 int64_t red_blocks(int64_t n);                   // partial sums of the fixed-order reductions
-Status energy_reduce(Context &cx);               // E = sum E_i on the device (every evaluation)
-Status energy_sum(Context &cx, double *E_host);  // the last evaluation's E to the host
+// E = sum E_i on the device (every evaluation); part: partials + total, nullptr = the context's buffer
+Status energy_reduce(Context &cx, double *part = nullptr);
+Status energy_sum(Context &cx, double *E_host, const double *part = nullptr);  // last evaluation's E to the host
+// The fixed device array that mpnn_energy_forces_noalloc reduces into (kStaticPartials partials and
+// the total), as a device address for the current device (looked up once per device).
+constexpr int64_t kStaticPartials = 16384;
+Status static_scratch(double **out);
 Status kick_drift(Context &cx, double dt);       // first half-kick + drift + skin test
 Status kick(Context &cx, double dt);             // second half-kick
 Status skin_check(Context &cx);                  // displacement test only

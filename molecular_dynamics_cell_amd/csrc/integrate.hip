@@ -3,6 +3,8 @@
 // skin test that triggers a neighbour rebuild, and caller-order <-> cell-order copies.
 #include <cmath>
 #include <cstring>
+#include <mutex>
+#include <string>
 
 #include <algorithm>
 
@@ -177,15 +179,18 @@ __global__ void k_unpermute_float(int64_t n, int width, int64_t np, const int32_
 
 }  // namespace
 
-// E = sum_i E_i ([JACS] "Parallelization Algorithm", Eq. 3) in a fixed tree, left on the device at
-// red[red_blocks(n)] (no allocation, no host transfer: it runs inside every evaluation, also in a
-// captured graph).  The reduction buffer is sized at the neighbour build.
-Status energy_reduce(Context &cx) {
+// E = sum_i E_i ([JACS] "Parallelization Algorithm", Eq. 3) in a fixed tree: block partials in
+// part[0 .. red_blocks(n)), the total at part[red_blocks(n)] (no allocation, no host transfer: it runs
+// inside every evaluation, also in a captured graph).  part = nullptr: the context's reduction
+// buffer, sized at the neighbour build.
+Status energy_reduce(Context &cx, double *part) {
     ProfScope ps_(cx, kProfReduce);
     if (cx.n == 0) return Status::ok();
     const int64_t b = red_blocks(cx.n);
-    if (cx.red.bytes < sizeof(double) * (size_t)(b + 1)) return Status::err(MPNN_E_STATE, "reduction buffer not sized");
-    double *part = cx.red.as<double>();
+    if (!part) {
+        if (cx.red.bytes < sizeof(double) * (size_t)(b + 1)) return Status::err(MPNN_E_STATE, "reduction buffer not sized");
+        part = cx.red.as<double>();
+    }
     k_sum_part<<<(unsigned)b, kRedThreads, 0, cx.stream>>>(cx.n, cx.Ei.as<double>(), part);
     MPNN_HIP(hipGetLastError());
     k_sum_double<<<1, kRedThreads, 0, cx.stream>>>(b, part, part + b);
@@ -193,15 +198,45 @@ Status energy_reduce(Context &cx) {
     return Status::ok();
 }
 
-// The energy of the last evaluation (energy_reduce's result) copied to the host.
-Status energy_sum(Context &cx, double *E_host) {
+// The energy of the last evaluation (energy_reduce's result in `part`, nullptr = the context's
+// buffer) copied to the host.
+Status energy_sum(Context &cx, double *E_host, const double *part) {
     if (cx.n == 0) {
         *E_host = 0.0;
         return Status::ok();
     }
-    MPNN_HIP(hipMemcpyAsync(E_host, cx.red.as<double>() + red_blocks(cx.n), sizeof(double), hipMemcpyDeviceToHost,
-                            cx.stream));
+    if (!part) part = cx.red.as<double>();
+    MPNN_HIP(hipMemcpyAsync(E_host, part + red_blocks(cx.n), sizeof(double), hipMemcpyDeviceToHost, cx.stream));
     MPNN_HIP(hipStreamSynchronize(cx.stream));
+    return Status::ok();
+}
+
+// ---- fixed device scratch for mpnn_energy_forces_noalloc ----
+// The reduction partials of the evaluations that may not allocate live in this file-scope device
+// array: kStaticPartials block partials and the total, i.e. systems of up to
+// kStaticPartials * 2,048 atoms.  Every GPU holds its own copy until the process ends; host code
+// uses only the address hipGetSymbolAddress reports for the current device (the array's name is a
+// host-side stand-in, not a device address).
+static __device__ __align__(256) double scratch[kStaticPartials + 1];
+namespace {
+constexpr int kMaxDevices = 64;
+double *g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+Status static_scratch(double **out) {
+    int dev = 0;
+    MPNN_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return Status::err(MPNN_E_INVALID_ARG, "device index out of range");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return Status::err(MPNN_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<double *>(p);
+    }
+    *out = g_scratch_ptr[dev];
     return Status::ok();
 }
 

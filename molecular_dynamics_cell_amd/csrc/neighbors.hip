@@ -764,6 +764,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     cx.prof_end(kProfBuildSpecies);
     MPNN_HIP(hipStreamSynchronize(cx.stream));
     cx.built = true;
+    cx.stale = false;
     cx.since_build = 0;
     return Status::ok();
 }
