@@ -57,9 +57,7 @@ def ag2m_alg_bytes(fam, g):
         "net_forward": B["networks_forward"] / T,
         "net_energy": B["networks_forward"] / T + B["networks_vjp"] / T,
         "net_backward": B["networks_vjp"] / T,
-        # the two-direction reverse pass forms every force itself: reverse edges and force gather
-        "reverse_edges": (B["reverse_edges"] + B["force_gather"]) / T,
-        # receiver pass + sender-major gathers (the 12-channel models' reverse pass)
+        # the receiver pass of the reverse edges (its sender-major gathers are inside this budget)
         "backward_layer": B["reverse_edges"] / T,
         "force_gather": B["force_gather"],
     }.get(fam)
@@ -87,17 +85,6 @@ def kernel_model(fam, g):
         # counts, active list, positions and messages (per node); O and feature rows out
         b = 4 * N + 4 * EA + 24 * NN + 4 * K * NN + 4 * KMP * N + 4 * DP * N
         f = EA * (2 * KM + 2 * K)
-        return b, f, "alu"
-    if fam == "node_grad":
-        # dE/drho and O rows in, one dE/dO row out per node (locals and ghosts)
-        b = 4 * DP * N + 4 * KMP * N + 4 * KM * NN
-        f = N * 2 * (2 * D * M)
-        return b, f, "hbm"
-    if fam == "reverse_edges":
-        # per node: position, messages and dE/dO row (gathered per edge, counted once); per atom:
-        # dE/dc and the force out (fp64); active index per edge
-        b = 4 * N + 4 * EA + (24 + 4 * K + 4 * KM) * NN + 4 * K * N + 24 * N
-        f = EA * (8 * KM + 8 * K + 6 * M)
         return b, f, "alu"
     if fam == "backward_layer":
         w_frac = (T - 1) / T                       # layers that emit dE/dc edge terms

@@ -1,7 +1,6 @@
 // C ABI entry points (include/mpnn.h): validation, buffer management and the call sequence
 // of one energy/force evaluation and of the velocity-Verlet loop.
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -58,8 +57,7 @@ Status Context::grow_keep(Buf &b, size_t bytes, size_t keep) {
 const char *const kProfNames[kProfCount] = {
     "build_sort", "build_ghosts", "build_rows", "build_transpose", "build_species", "ghost_positions",
     "compact", "aggregate", "net_forward", "net_energy", "net_backward", "ghost_messages",
-    "backward_layer", "message_grad", "ghost_grad_fold", "force_gather", "kick_drift", "kick", "reduce",
-    "node_grad", "reverse_edges"};
+    "backward_layer", "message_grad", "ghost_grad_fold", "force_gather", "kick_drift", "kick", "reduce"};
 
 void Context::prof_begin(int id) {
     if (!prof_on) return;
@@ -116,7 +114,7 @@ void Context::release(Buf &b) {
 
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
-    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &Rn, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
+    Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
                   &ghost_off, &row_off, &row_len, &slab_off, &nbr, &t_off, &t_recv, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &dact, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
@@ -152,23 +150,15 @@ Status evaluate(Context &cx, double *F_caller, double *red_part = nullptr) {
             MPNN_TRY(mlp_energy(cx));
         }
     }
-    if (cx.two_dir) {
-        for (int t = cx.T - 1; t >= 0; --t) {
-            MPNN_TRY(node_grad(cx, t));
-            MPNN_TRY(reverse_edges(cx, t, F_caller));
-            if (t >= 1) MPNN_TRY(mlp_backward(cx, t - 1));
+    for (int t = cx.T - 1; t >= 0; --t) {
+        MPNN_TRY(backward_layer(cx, t));
+        if (t >= 1) {
+            MPNN_TRY(backward_messages(cx, t));
+            MPNN_TRY(mlp_backward(cx, t - 1));
         }
-    } else {
-        for (int t = cx.T - 1; t >= 0; --t) {
-            MPNN_TRY(backward_layer(cx, t));
-            if (t >= 1) {
-                MPNN_TRY(backward_messages(cx, t));
-                MPNN_TRY(mlp_backward(cx, t - 1));
-            }
-        }
-        if (cx.T == 1) MPNN_TRY(transpose_active(cx));
-        MPNN_TRY(force_gather(cx, F_caller));
     }
+    if (cx.T == 1) MPNN_TRY(transpose_active(cx));
+    MPNN_TRY(force_gather(cx, F_caller));
     MPNN_TRY(energy_reduce(cx, red_part));
     cx.forces_valid = true;
     return Status::ok();
@@ -290,11 +280,6 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out) {
         md.half_pi_over_rc = 0.5 * mpnn::kPi / p->rc;
     }
     cx.contracted = p->contraction != nullptr;
-    // reverse pass: the receiver pass with sender-major gathers; the two-direction row kernel
-    // (K <= 8) only on request (MPNN_TWO_DIR=1): measured 5.5 ms per layer on the 2.05M-atom Ag
-    // subdomain against 2.1 ms + gathers, bound by its 24 scattered 16-byte loads per edge
-    cx.two_dir = false;
-    if (const char *e = std::getenv("MPNN_TWO_DIR")) cx.two_dir = cx.K <= 8 && std::atoi(e) != 0;
     if (cx.contracted)
         for (int q = 0; q < cx.K * cx.K; ++q) {
             md.C64[q] = held(p->contraction[q]);

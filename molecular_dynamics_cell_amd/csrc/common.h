@@ -133,11 +133,6 @@ constexpr int pad16(int w) { return (w + 15) / 16 * 16; }
 // neighbour's position and messages share a cache line in the row kernels' gathers.
 constexpr int rec_stride(int K) { return 8 + (K + 7) / 8 * 8; }
 constexpr int kRecC = 8;   // float offset of c inside a record
-// Reverse records (the two-direction reverse pass, K <= 8): per node and layer, the position (3
-// doubles) and messages c^t as in the node record, then dE/dO^t at float kRevG, padded to whole
-// 128-byte lines (384 bytes for K = 8, L = 2).
-constexpr int kRevG = 16;
-constexpr int rev_stride(int K, int L) { return (kRevG + K * n_mono(L) + 31) / 32 * 32; }
 inline int64_t pad_rows(int64_t n) { return (n + kBlock - 1) / kBlock * kBlock; }
 __host__ __device__ __forceinline__ int64_t tiled(int64_t np, int64_t i, int q) {
     return ((int64_t)(q >> 4) * np + i) * 16 + (q & 15);

@@ -808,6 +808,56 @@ __global__ __launch_bounds__(256) void k_features(int64_t n, int64_t np, const f
 // the node records this pass gathers (4.7 % faster than ordinary stores, measured there); the
 // streamed active indices and the dE/dr_e read back for accumulation are loaded the same way
 // (another 1.2 %).
+// The VJP of one active edge e (see k_backward_layer): writes w_e (WANT_W) and returns dE/dr_e.
+template <int K, int L, bool WANT_W, bool NT, class B>
+__device__ __forceinline__ void edge_vjp(const B &b, const float *cv, const float (&G)[K][n_mono(L)], float ir,
+                                         float *__restrict__ we, float (&g)[3]) {
+    constexpr int M = n_mono(L);
+    constexpr Mono<L> mono;
+    float s = 0.0f, Q[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) Q[m] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        float u = 0.0f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
+        if (WANT_W) st_s<NT>(u * b.Rf[k], &we[k]);
+        s = fmaf(cv[k] * u, b.Rd[k], s);
+        const float P = cv[k] * b.Rf[k];
+#pragma unroll
+        for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
+    }
+    // angular part: dA_m/dx = lx x^(lx-1) y^ly z^lz / rc^lx..., i.e. lx times the monomial
+    // with one power of x fewer, over rc (likewise y, z)
+    float ga[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
+        if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
+        if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
+    }
+    // plus the radial part along r / d
+    const float sd = s * b.inv_d;
+    g[0] = fmaf(sd, b.rx, ga[0] * ir);
+    g[1] = fmaf(sd, b.ry, ga[1] * ir);
+    g[2] = fmaf(sd, b.rz, ga[2] * ir);
+}
+
+// dE/dr_e accumulated over layers: written by the first reverse layer, read-modified-written after.
+template <bool FIRST, bool NT>
+__device__ __forceinline__ void store_gedge(float *__restrict__ ge, const float (&g)[3]) {
+    if (FIRST) {
+        st_s<NT>(g[0], &ge[0]);
+        st_s<NT>(g[1], &ge[1]);
+        st_s<NT>(g[2], &ge[2]);
+    } else {
+        st_s<NT>(ld_s<NT>(&ge[0]) + g[0], &ge[0]);
+        st_s<NT>(ld_s<NT>(&ge[1]) + g[1], &ge[1]);
+        st_s<NT>(ld_s<NT>(&ge[2]) + g[2], &ge[2]);
+    }
+}
+
 template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
@@ -820,7 +870,6 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
                                                         double *__restrict__ Frecv) {
     static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
     constexpr int M = n_mono(L);
-    constexpr Mono<L> mono;
     int64_t i;
     int q = 0;
     if constexpr (LANES == 1) {
@@ -849,43 +898,9 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
         const double *pv = reinterpret_cast<const double *>(rv);
         Basis<K, L, CT> b;
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
-        const float *cv = rv + kRecC;
-        float s = 0.0f, Q[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) Q[m] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            float u = 0.0f;
-#pragma unroll
-            for (int m = 0; m < M; ++m) u += G[k][m] * b.A[m];
-            if (WANT_W) st_s<NT>(u * b.Rf[k], &w[e * K + k]);
-            s = fmaf(cv[k] * u, b.Rd[k], s);
-            const float P = cv[k] * b.Rf[k];
-#pragma unroll
-            for (int m = 0; m < M; ++m) Q[m] += P * G[k][m];
-        }
-        // angular part: dA_m/dx = lx x^(lx-1) y^ly z^lz / rc^lx..., i.e. lx times the monomial
-        // with one power of x fewer, over rc (likewise y, z)
-        float ga[3] = {0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
-            if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
-            if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
-        }
-        // plus the radial part along r / d
-        const float sd = s * b.inv_d;
-        float g[3] = {fmaf(sd, b.rx, ga[0] * ir), fmaf(sd, b.ry, ga[1] * ir), fmaf(sd, b.rz, ga[2] * ir)};
-        float *ge = gedge + 3 * e;
-        if (FIRST) {
-            st_s<NT>(g[0], &ge[0]);
-            st_s<NT>(g[1], &ge[1]);
-            st_s<NT>(g[2], &ge[2]);
-        } else {
-            st_s<NT>(ld_s<NT>(&ge[0]) + g[0], &ge[0]);
-            st_s<NT>(ld_s<NT>(&ge[1]) + g[1], &ge[1]);
-            st_s<NT>(ld_s<NT>(&ge[2]) + g[2], &ge[2]);
-        }
+        float g[3];
+        edge_vjp<K, L, WANT_W, NT>(b, rv + kRecC, G, ir, w + e * K, g);
+        store_gedge<FIRST, NT>(gedge + 3 * e, g);
         F[0] += (double)g[0];
         F[1] += (double)g[1];
         F[2] += (double)g[2];
@@ -990,181 +1005,6 @@ __global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np
         Frecv[3 * i] = F[0]; Frecv[3 * i + 1] = F[1]; Frecv[3 * i + 2] = F[2];
     } else {
         Frecv[3 * i] += F[0]; Frecv[3 * i + 1] += F[1]; Frecv[3 * i + 2] += F[2];
-    }
-}
-
-// ------------------------------------------------------------------------------------------
-// Two-direction reverse pass (models with K <= 8 channels).  The neighbour relation is symmetric:
-// j (or an image of j) is in row i exactly when i (or an image of i) is in row j, with the opposite
-// displacement r_ji = -r_ij and the same radial factors; the monomials change as
-// A_m(-r) = (-1)^l A_m(r) and their gradients as dA_m(-r) = -(-1)^l dA_m(r).  So row i can form, from
-// one basis evaluation per neighbour, both the terms of its own orbital sums (dE/dO_i, received
-// messages c_j) and those of neighbour j's orbital sums that i's message c_i enters (dE/dO_j).  With
-// G = dE/dO, u_k = sum_m G[k,m] A_m and sg_m = (-1)^l:
-//   dE/dc_i[k] = sum_j R_k f_c  sum_m sg_m G_j[k,m] A_m                         (Eq. 4, dE/dc term)
-//   F_i        = sum_j  s r/d + sum_m Q_m dA_m/dr,                                (Eq. 3-4)
-//      s   = sum_k (R'_k f_c + R_k f'_c) (c_j[k] u^i_k + c_i[k] u^j_k)
-//      Q_m = sum_k R_k f_c (c_j[k] G_i[k,m] + c_i[k] sg_m G_j[k,m])
-// Every output is a fixed-order sum over the row: no per-edge arrays, no sender-major gathers, no
-// ghost folds (a ghost's dE/dO is its owner's, refreshed per layer like the messages).
-// ------------------------------------------------------------------------------------------
-
-// dE/dO^t of every node (a ghost takes its owner's) with the node's position and messages: the
-// reverse records that the two-direction pass gathers.
-template <int K, int L>
-__global__ __launch_bounds__(256) void k_node_grad(int64_t NN, int64_t n, int64_t np, const int32_t *__restrict__ owner,
-                                                    const float *__restrict__ Grho, const float *__restrict__ Ot,
-                                                    const float *__restrict__ rec, float *__restrict__ R) {
-    constexpr int M = n_mono(L), RS = rev_stride(K, L);
-    static_assert(K <= kRevG - kRecC, "messages fit before dE/dO");
-    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (v >= NN) return;
-    const int64_t o = v < n ? v : (int64_t)owner[v - n];
-    float G[K][M];
-    assemble_go_row<K, L>(Grho, Ot, np, o, G);
-    const float4 *src = reinterpret_cast<const float4 *>(rec + v * rec_stride(K));
-    float4 *dst = reinterpret_cast<float4 *>(R + v * RS);
-    // header: position and messages (the node's own record: a ghost has its own position)
-#pragma unroll
-    for (int q = 0; q < kRevG / 4; ++q) dst[q] = q < rec_stride(K) / 4 ? src[q] : float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int q = 0; q < (RS - kRevG) / 4; ++q) {
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int f = 4 * q + e;
-            x[e] = f < K * M ? G[f / M][f % M] : 0.0f;
-        }
-        dst[kRevG / 4 + q] = float4{x[0], x[1], x[2], x[3]};
-    }
-}
-
-// The two-direction reverse pass of layer t over one receiver row per lane (LANES = 1) or per
-// 16-lane group (small systems).  WANT_GC: write dE/dc^t_i (t >= 1).  first: the force sum starts
-// (t = T-1), else it accumulates; last (t = 0): the forces are final, written sorted and in the
-// caller's order.
-template <int K, int L, bool WANT_GC, bool CT, bool NT, int LANES>
-__global__ __launch_bounds__(256) void k_reverse_edges(int first, int last, int64_t n, const int64_t *__restrict__ slab_off,
-                                                       const int32_t *__restrict__ nact,
-                                                       const int32_t *__restrict__ act_n, const float *__restrict__ R,
-                                                       const ModelDev *__restrict__ md,
-                                                       const int32_t *__restrict__ row_perm,
-                                                       float *__restrict__ Gc, double *__restrict__ Facc,
-                                                       double *__restrict__ F, const int32_t *__restrict__ perm,
-                                                       double *__restrict__ Fcaller) {
-    static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
-    constexpr int M = n_mono(L), RS = rev_stride(K, L);
-    constexpr Mono<L> mono;
-    int64_t i;
-    int q = 0;
-    if constexpr (LANES == 1) {
-        i = block_row(xcd_block() * blockDim.x, n, row_perm);
-        if (i >= n) return;
-    } else {
-        i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
-        q = (int)(threadIdx.x % LANES);
-    }
-    const bool row = i < n;
-    const int64_t ir_ = row ? i : 0;   // idle groups past the end read row 0 and write nothing
-    float mu[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) mu[k] = md->mu[k];
-    const float ir = md->inv_rc;
-    const float *Ri = R + ir_ * RS;
-    const double *pi = reinterpret_cast<const double *>(Ri);
-    const double xi = pi[0], yi = pi[1], zi = pi[2];
-    float ci[K], Gi[K][M];
-#pragma unroll
-    for (int k = 0; k < K; ++k) ci[k] = Ri[kRecC + k];
-#pragma unroll
-    for (int k = 0; k < K; ++k)
-#pragma unroll
-        for (int m = 0; m < M; ++m) Gi[k][m] = Ri[kRevG + k * M + m];
-    float gc[K];
-#pragma unroll
-    for (int k = 0; k < K; ++k) gc[k] = 0.0f;
-    double Fx = 0.0, Fy = 0.0, Fz = 0.0;
-    const int64_t b0 = sell_base(slab_off, ir_);
-    const int na = row ? nact[ir_] : 0;
-    for (int a = q; a < na; a += LANES) {
-        const int64_t j = ld_s<NT>(&act_n[b0 + kSlab * a]);
-        const float *Rj = R + j * RS;
-        const double *pj = reinterpret_cast<const double *>(Rj);
-        Basis<K, L, CT> b;
-        b.eval(__dsub_rn(pj[0], xi), __dsub_rn(pj[1], yi), __dsub_rn(pj[2], zi), md, mu);
-        float cj[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) cj[k] = Rj[kRecC + k];
-        float s = 0.0f, Q[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) Q[m] = 0.0f;
-        // receiving direction (row i's orbital sums)
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            float u = 0.0f;
-#pragma unroll
-            for (int m = 0; m < M; ++m) u = fmaf(Gi[k][m], b.A[m], u);
-            s = fmaf(cj[k] * u, b.Rd[k], s);
-            const float P = cj[k] * b.Rf[k];
-#pragma unroll
-            for (int m = 0; m < M; ++m) Q[m] = fmaf(P, Gi[k][m], Q[m]);
-        }
-        // sending direction (neighbour j's orbital sums, displacement -r)
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            float g[M];
-#pragma unroll
-            for (int m = 0; m < M; ++m) g[m] = (mono.l[m] & 1) ? -Rj[kRevG + k * M + m] : Rj[kRevG + k * M + m];
-            float u = 0.0f;
-#pragma unroll
-            for (int m = 0; m < M; ++m) u = fmaf(g[m], b.A[m], u);
-            if constexpr (WANT_GC) gc[k] = fmaf(b.Rf[k], u, gc[k]);
-            s = fmaf(ci[k] * u, b.Rd[k], s);
-            const float P = ci[k] * b.Rf[k];
-#pragma unroll
-            for (int m = 0; m < M; ++m) Q[m] = fmaf(P, g[m], Q[m]);
-        }
-        // angular part: dA_m/dx = lx x^(lx-1) y^ly z^lz / rc^lx..., i.e. lx times the monomial
-        // with one power of x fewer, over rc (likewise y, z); then the radial part along r / d
-        float ga[3] = {0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-            if (mono.lx[m]) ga[0] = fmaf((float)mono.lx[m] * Q[m], b.A[mono.mx[m]], ga[0]);
-            if (mono.ly[m]) ga[1] = fmaf((float)mono.ly[m] * Q[m], b.A[mono.my[m]], ga[1]);
-            if (mono.lz[m]) ga[2] = fmaf((float)mono.lz[m] * Q[m], b.A[mono.mz[m]], ga[2]);
-        }
-        const float sd = s * b.inv_d;
-        Fx += (double)fmaf(sd, b.rx, ga[0] * ir);
-        Fy += (double)fmaf(sd, b.ry, ga[1] * ir);
-        Fz += (double)fmaf(sd, b.rz, ga[2] * ir);
-    }
-    if constexpr (LANES > 1) {
-        Fx = group_sum16(Fx);
-        Fy = group_sum16(Fy);
-        Fz = group_sum16(Fz);
-        if constexpr (WANT_GC) {
-#pragma unroll
-            for (int k = 0; k < K; ++k) gc[k] = group_sum16(gc[k]);
-        }
-        if (!row || q != 0) return;
-    }
-    if constexpr (WANT_GC) {
-#pragma unroll
-        for (int k = 0; k < K; ++k) Gc[i * K + k] = gc[k];
-    }
-    if (!first) {
-        Fx += Facc[3 * i];
-        Fy += Facc[3 * i + 1];
-        Fz += Facc[3 * i + 2];
-    }
-    if (last) {
-        F[3 * i] = Fx; F[3 * i + 1] = Fy; F[3 * i + 2] = Fz;
-        if (Fcaller) {
-            const int64_t c = perm[i];
-            Fcaller[3 * c] = Fx; Fcaller[3 * c + 1] = Fy; Fcaller[3 * c + 2] = Fz;
-        }
-    } else {
-        Facc[3 * i] = Fx; Facc[3 * i + 1] = Fy; Facc[3 * i + 2] = Fz;
     }
 }
 
@@ -1492,61 +1332,6 @@ Status backward_layer(Context &cx, int t) {
 #undef MPNN_BWD_NT
 #undef MPNN_BWD_LG
 #undef MPNN_BWD_SPLIT
-    MPNN_HIP(hipGetLastError());
-    return Status::ok();
-}
-
-Status node_grad(Context &cx, int t) {
-    ProfScope ps_(cx, kProfNodeGrad);
-    if (cx.NN == 0) return Status::ok();
-    const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
-    const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
-    const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
-#define MPNN_NG(KK, LL)                                                                                        \
-    k_node_grad<KK, LL><<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cx.n, cx.np, cx.ghost_owner.as<int32_t>(), \
-                                                                    Gt, Ot, ct, cx.Rn.as<float>())
-    if (cx.K == 8 && cx.L == 2) MPNN_NG(8, 2);
-    else if (cx.K == 4 && cx.L == 2) MPNN_NG(4, 2);
-    else if (cx.K == 2 && cx.L == 1) MPNN_NG(2, 1);
-    else return Status::err(MPNN_E_INVALID_ARG, "two-direction reverse pass: unsupported (K, L)");
-#undef MPNN_NG
-    MPNN_HIP(hipGetLastError());
-    return Status::ok();
-}
-
-Status reverse_edges(Context &cx, int t, double *F_caller) {
-    ProfScope ps_(cx, kProfReverseEdges);
-    if (cx.n == 0) return Status::ok();
-    float *Gct = cx.Gc.as<float>() + (int64_t)t * cx.NN * cx.K;
-    const bool gc = t >= 1, first = t == cx.T - 1, last = t == 0;
-    auto launch = [&](auto kl, auto gcf, auto ctf, auto ntf, auto lanes) {
-        constexpr int KK = decltype(kl)::value / 10, LL = decltype(kl)::value % 10;
-        constexpr int LN = decltype(lanes)::value;
-        const unsigned grid = LN == 1 ? grid_xcd(cx.n) : grid_for(cx.n * LN);
-        k_reverse_edges<KK, LL, decltype(gcf)::value, decltype(ctf)::value, decltype(ntf)::value, LN>
-            <<<grid, kBlock, 0, cx.stream>>>(first ? 1 : 0, last ? 1 : 0, cx.n, cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), cx.Rn.as<float>(),
-            cx.model.as<ModelDev>(), LN == 1 ? row_perm(cx) : nullptr, Gct, cx.Frecv.as<double>(), cx.F.as<double>(),
-            cx.perm.as<int32_t>(), F_caller);
-    };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    auto by_lanes = [&](auto kl, auto gcf, auto ctf) {
-        if (cx.lane_groups) launch(kl, gcf, ctf, F_{}, std::integral_constant<int, kGatherLanes>{});
-        else if (cx.nt) launch(kl, gcf, ctf, T_{}, std::integral_constant<int, 1>{});
-        else launch(kl, gcf, ctf, F_{}, std::integral_constant<int, 1>{});
-    };
-    auto by_ct = [&](auto kl, auto gcf) {
-        if (cx.contracted) by_lanes(kl, gcf, T_{});
-        else by_lanes(kl, gcf, F_{});
-    };
-    auto by_gc = [&](auto kl) {
-        if (gc) by_ct(kl, T_{});
-        else by_ct(kl, F_{});
-    };
-    if (cx.K == 8 && cx.L == 2) by_gc(std::integral_constant<int, 82>{});
-    else if (cx.K == 4 && cx.L == 2) by_gc(std::integral_constant<int, 42>{});
-    else if (cx.K == 2 && cx.L == 1) by_gc(std::integral_constant<int, 21>{});
-    else return Status::err(MPNN_E_INVALID_ARG, "two-direction reverse pass: unsupported (K, L)");
     MPNN_HIP(hipGetLastError());
     return Status::ok();
 }

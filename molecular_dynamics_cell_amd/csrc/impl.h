@@ -41,7 +41,7 @@ enum ProfId {
     kProfBuildSort = 0, kProfBuildGhost, kProfBuildRows, kProfBuildTranspose, kProfBuildSpecies,
     kProfGhostPos, kProfCompact, kProfAggregate, kProfNetForward, kProfNetEnergy, kProfNetBackward,
     kProfGhostFeat, kProfBackwardLayer, kProfMessageGrad, kProfGhostFold, kProfForceGather,
-    kProfKickDrift, kProfKick, kProfReduce, kProfNodeGrad, kProfReverseEdges, kProfCount
+    kProfKickDrift, kProfKick, kProfReduce, kProfCount
 };
 extern const char *const kProfNames[kProfCount];
 
@@ -127,8 +127,6 @@ struct Context {
     bool bucket = false;   // row kernels take rows in row_perm order (ragged row lengths)
     bool nt = false;       // per-edge streams far larger than the caches, rows in order: nontemporal
     bool lane_groups = false;   // small systems: the row kernels give each row a 16-lane group
-    Buf Rn;       // float [NN][rev_stride]: reverse records of the current layer (two-direction pass)
-    bool two_dir = false;  // reverse pass in one two-direction row kernel (no per-edge arrays, no transpose)
     double *scratch = nullptr;  // device address of the fixed reduction array (mpnn_energy_forces_noalloc)
     bool stale = false;         // positions moved beyond skin/2 without a rebuild: the next call rebuilds
     Buf Frecv;    // double [n][3]
@@ -209,10 +207,6 @@ Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagno
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
 Status transpose_active(Context &cx);             // t_act alone (T == 1)
 Status force_gather(Context &cx, double *F_caller);
-// two-direction reverse pass (models with K <= 8): the layer's reverse records, then per row the
-// layer's dE/dc and force terms of both directions of every edge
-Status node_grad(Context &cx, int t);
-Status reverse_edges(Context &cx, int t, double *F_caller);
 
 // ---- mlp.hip ----
 Status mlp_forward(Context &cx, int t);           // c^{t+1} from rho^t (t < T-1)

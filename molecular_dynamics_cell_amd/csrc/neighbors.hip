@@ -670,10 +670,8 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_HIP(hipGetLastError());
     cx.prof_end(kProfBuildRows);
 
-    // ---- sender-major transpose: for every node, the edges it sends, in edge order (only the
-    // gather-based reverse pass of the 12-channel models reads it) ----
+    // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
     cx.prof_begin(kProfBuildTranspose);
-    if (!cx.two_dir) {
     MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
     MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
@@ -704,7 +702,6 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         k_tmap_recv<<<grid_for(E), kBlock, 0, cx.stream>>>(E, cx.t_eid.as<int32_t>(), recv, cx.t_recv.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }
-    }   // !two_dir
 
     cx.prof_end(kProfBuildTranspose);
 
@@ -742,18 +739,13 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
     MPNN_TRY(cx.grow(cx.pos32, sizeof(float4) * NN1));
     MPNN_TRY(cx.grow(cx.amask, sizeof(uint32_t) * (size_t)cx.mw * n1));
-    if (cx.two_dir) {
-        MPNN_TRY(cx.grow(cx.Rn, sizeof(float) * NN1 * (size_t)rev_stride(cx.K, cx.L)));
-    } else {
-        MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
-        MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
-    }
+    MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     if (cx.precision == 0 && cx.T > 1)
         MPNN_TRY(cx.grow(cx.dact, sizeof(float) * (size_t)(cx.T - 1) * n1 * 2 * cx.H));
     MPNN_TRY(cx.grow(cx.act_n, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.nact, sizeof(int32_t) * n1));
     MPNN_TRY(cx.grow(cx.row_perm, sizeof(int32_t) * n1));
-    if (cx.T > 1 && !cx.two_dir) MPNN_TRY(cx.grow(cx.w, sizeof(float) * (size_t)E1 * cx.K));
+    if (cx.T > 1) MPNN_TRY(cx.grow(cx.w, sizeof(float) * (size_t)E1 * cx.K));
     MPNN_TRY(cx.grow(cx.Frecv, sizeof(double) * 3 * n1));
     MPNN_TRY(cx.grow(cx.F, sizeof(double) * 3 * n1));
     MPNN_TRY(cx.grow(cx.Ei, sizeof(double) * n1));
