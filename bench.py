@@ -298,22 +298,18 @@ def bandwidth(gib=4, reps=10):
             "sum_read": rate(lambda: a.sum(), nbytes)}
 
 
-def t_sweep(max_t=6, evals=10):
+def t_sweep(cfg=4, max_t=6, evals=10):
     """Cost of one E+F evaluation against the number of message-passing layers T (the pages' claim
-    of a cost linear in T), on the 2.05M-atom Ag subdomain with random-init models of each depth,
-    and the per-layer ghost-refresh volume against subdomain size (surface, not volume, scaling)."""
+    of a cost linear in T) on workload cfg (the 2.05M-atom Ag subdomain or the 4,608-atom water box)
+    with random-init models of each depth (inputs.depth_variant), and, for Ag, the per-layer
+    ghost-refresh volume against subdomain size (surface, not volume, scaling)."""
     import torch
-    from dataclasses import replace
     from molecular_dynamics_cell_amd import binding, inputs as I
     dev = torch.device("cuda:0")
-    s = I.make_system(4)
-    base = I.make_params(4)
-    scales = list(base.layer_scale)
+    s = I.make_system(cfg)
     rows = []
     for T in range(1, max_t + 1):
-        spec = replace(base.spec, T=T)
-        ls = [scales[min(t, len(scales) - 1)] for t in range(T)]
-        p = I.random_params(spec, 1204, base.masses, ls, base.e_scale)
+        p = I.depth_variant(cfg, T)
         m = binding.MPNN(p, dev)
         m.build_neighbors(torch.tensor(s.pos, device=dev), torch.tensor(s.types, device=dev), s.box)
         m.energy_forces(energy=False)
@@ -325,8 +321,8 @@ def t_sweep(max_t=6, evals=10):
             torch.cuda.synchronize()
             ts.append(time.perf_counter() - a0)
         ms = float(np.median(ts)) * 1e3
-        rows.append({"T": T, "ef_ms": round(ms, 3), "atom_steps_per_s": round(s.n / ms * 1e3, 1)})
-        print(f"T={T}: {ms:.3f} ms per E+F", file=sys.stderr, flush=True)
+        rows.append({"T": T, "ef_ms": round(ms, 4), "atom_steps_per_s": round(s.n / ms * 1e3, 1)})
+        print(f"T={T}: {ms:.4f} ms per E+F", file=sys.stderr, flush=True)
         m.close()
         torch.cuda.empty_cache()
     # linear fit ms = a + b T
@@ -335,19 +331,22 @@ def t_sweep(max_t=6, evals=10):
     b, a = np.polyfit(Ts, ys, 1)
     resid = float(np.max(np.abs(ys - (a + b * Ts)) / ys))
     halo = []
-    p = I.make_params(4)
-    for cells in (20, 40, 80):
-        g = I.ag(cells, 1004, 1104, name=f"Ag{cells}")
-        m = binding.MPNN(p, dev)
-        m.build_neighbors(torch.tensor(g.pos, device=dev), torch.tensor(g.types, device=dev), g.box)
-        info = m.info()
-        halo.append({"fcc_cells": cells, "atoms": g.n, "ghosts": info["n_ghost"],
-                     "ghost_fraction": round(info["n_ghost"] / g.n, 4),
-                     "refresh_bytes_per_layer": info["n_ghost"] * p.spec.K * 4})
-        m.close()
-        torch.cuda.empty_cache()
-    return {"sweep": "E+F cost vs layers T, Ag 2,048,000 atoms (random-init models, K=8, L=2, H=64)",
-            "rows": rows, "fit_ms": {"fixed": round(float(a), 3), "per_layer": round(float(b), 3),
+    if cfg == 4:
+        p = I.make_params(4)
+        for cells in (20, 40, 80):
+            g = I.ag(cells, 1004, 1104, name=f"Ag{cells}")
+            m = binding.MPNN(p, dev)
+            m.build_neighbors(torch.tensor(g.pos, device=dev), torch.tensor(g.types, device=dev), g.box)
+            info = m.info()
+            halo.append({"fcc_cells": cells, "atoms": g.n, "ghosts": info["n_ghost"],
+                         "ghost_fraction": round(info["n_ghost"] / g.n, 4),
+                         "refresh_bytes_per_layer": info["n_ghost"] * p.spec.K * 4})
+            m.close()
+            torch.cuda.empty_cache()
+    spec = I.make_params(cfg).spec
+    return {"sweep": f"E+F cost vs layers T, {s.name} ({s.n} atoms; random-init models, K={spec.K}, "
+                     f"L={spec.L}, H={spec.H})",
+            "rows": rows, "fit_ms": {"fixed": round(float(a), 4), "per_layer": round(float(b), 4),
                                      "max_rel_residual": round(resid, 4)},
             "halo": halo}
 
@@ -389,7 +388,7 @@ def main():
         sys.exit(2)
 
     if args.t_sweep:
-        print(json.dumps(t_sweep()))
+        print(json.dumps(t_sweep(args.config)))
         return
     if args.bandwidth:
         print(json.dumps(bandwidth()))

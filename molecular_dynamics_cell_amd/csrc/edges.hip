@@ -149,16 +149,23 @@ struct BasisHalf {
 
 // e^x in fp64 for x <= 709: x = n ln 2 + r with ln 2 in two parts (Cody and Waite), so r is exact
 // to rounding and |r| <= ln 2 / 2; e^r from its Taylor series to r^11 (truncation below 7e-15
-// relative), scaled by 2^n.  Arguments below -745 give 0 (the fp64 result underflows there).
+// relative; SHORT: to r^8, below 3e-10, for factors that are rounded to fp32 afterwards), scaled
+// by 2^n.  Arguments below -745 give 0 (the fp64 result underflows there).
+template <bool SHORT = false>
 __device__ __forceinline__ double exp_fp64(double x) {
     x = fmax(x, -745.0);
     const double n = rint(x * 1.4426950408889634);
     double r = fma(n, -6.93147180369123816490e-01, x);
     r = fma(n, -1.90821492927058770002e-10, r);
-    double p = 1.0 / 39916800.0;          // 1/11!
-    p = fma(p, r, 1.0 / 3628800.0);       // 1/10!
-    p = fma(p, r, 1.0 / 362880.0);
-    p = fma(p, r, 1.0 / 40320.0);
+    double p;
+    if constexpr (SHORT) {
+        p = 1.0 / 40320.0;                // 1/8!
+    } else {
+        p = 1.0 / 39916800.0;             // 1/11!
+        p = fma(p, r, 1.0 / 3628800.0);   // 1/10!
+        p = fma(p, r, 1.0 / 362880.0);
+        p = fma(p, r, 1.0 / 40320.0);
+    }
     p = fma(p, r, 1.0 / 5040.0);
     p = fma(p, r, 1.0 / 720.0);
     p = fma(p, r, 1.0 / 120.0);
@@ -192,11 +199,19 @@ struct BasisHP {
     __device__ __forceinline__ void eval(double dx, double dy, double dz, const CV *__restrict__ cv,
                                          const ModelDev *__restrict__ md) {
         constexpr Mono<L> mono;
+        // factors kept in fp32 (S = float) need series only to ~1e-10: cos to t^14 (truncation below
+        // 7e-11 on [0, pi/2]) and exponentials to r^8; the fp64 orbital sums keep the long series
+        constexpr bool F32 = std::is_same<S, float>::value;
         const double d = sqrt(fma(dx, dx, fma(dy, dy, dz * dz)));
         const double t = d * md->half_pi_over_rc, t2 = t * t;
-        double cs = -1.0 / 6402373705728000.0;                 // -1/18!
-        cs = fma(cs, t2, 1.0 / 20922789888000.0);              // 1/16!
-        cs = fma(cs, t2, -1.0 / 87178291200.0);                // -1/14!
+        double cs;
+        if constexpr (F32) {
+            cs = -1.0 / 87178291200.0;                         // -1/14!
+        } else {
+            cs = -1.0 / 6402373705728000.0;                    // -1/18!
+            cs = fma(cs, t2, 1.0 / 20922789888000.0);          // 1/16!
+            cs = fma(cs, t2, -1.0 / 87178291200.0);            // -1/14!
+        }
         cs = fma(cs, t2, 1.0 / 479001600.0);                   // 1/12!
         cs = fma(cs, t2, -1.0 / 3628800.0);                    // -1/10!
         cs = fma(cs, t2, 1.0 / 40320.0);                       // 1/8!
@@ -209,8 +224,8 @@ struct BasisHP {
             double Rf[K];
             if constexpr (CHAIN) {
                 const double x0 = d - md->mu64[0];
-                double r = exp_fp64(md->g_a0 * x0 * x0) * fc;
-                const double E = exp_fp64(md->g_e * d);
+                double r = exp_fp64<F32>(md->g_a0 * x0 * x0) * fc;
+                const double E = exp_fp64<F32>(md->g_e * d);
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     Rf[k] = r;
@@ -234,8 +249,8 @@ struct BasisHP {
         } else if constexpr (CHAIN) {
             // the chain runs on R_k f_c: P_k = c_k (R_k f_c), next = this E (g_c + g_c g_eps d)
             const double x0 = d - md->mu64[K0];
-            double Rf = exp_fp64(md->g_a0 * x0 * x0) * fc;
-            const double E = exp_fp64(md->g_e * d);
+            double Rf = exp_fp64<F32>(md->g_a0 * x0 * x0) * fc;
+            const double E = exp_fp64<F32>(md->g_e * d);
 #pragma unroll
             for (int j = 0; j < KB; ++j) {
                 const int k = K0 + j;
@@ -251,9 +266,11 @@ struct BasisHP {
                 P[j] = (S)((double)cv[k] * exp(md->g_a0 * x * x) * fc);
             }
         }
-        const double ux = dx * md->inv_rc64, uy = dy * md->inv_rc64, uz = dz * md->inv_rc64;
-        double px[L + 1], py[L + 1], pz[L + 1];
-        px[0] = py[0] = pz[0] = 1.0;
+        // monomials of r / rc: fp32 products of the once-rounded components (S = float), else fp64
+        using U = std::conditional_t<F32, float, double>;
+        const U ux = (U)(dx * md->inv_rc64), uy = (U)(dy * md->inv_rc64), uz = (U)(dz * md->inv_rc64);
+        U px[L + 1], py[L + 1], pz[L + 1];
+        px[0] = py[0] = pz[0] = (U)1;
 #pragma unroll
         for (int q = 1; q <= L; ++q) {
             px[q] = px[q - 1] * ux;

@@ -17,6 +17,8 @@
 #include <algorithm>
 #include <vector>
 
+#include <hipcub/hipcub.hpp>
+
 #include "impl.h"
 
 namespace mpnn {
@@ -121,39 +123,6 @@ __global__ void k_sort_segments(int64_t nseg, const int64_t *__restrict__ off, i
     }
 }
 
-// One wave per segment: every element's rank is the count of smaller keys in the segment
-// (keys are distinct), so the result does not depend on the scatter order.  Segments longer
-// than the LDS tile fall back to the insertion sort on one lane.
-constexpr int kRankTile = 512;
-__global__ __launch_bounds__(64) void k_rank_sort_segments(int64_t nseg, const int64_t *__restrict__ off,
-                                                          int32_t *__restrict__ v) {
-    __shared__ int32_t sh[kRankTile];
-    const int64_t s = blockIdx.x;
-    if (s >= nseg) return;
-    const int64_t b = off[s], len = off[s + 1] - b;
-    if (len <= 1) return;
-    if (len > kRankTile) {
-        if (threadIdx.x == 0)
-            for (int64_t p = b + 1; p < b + len; ++p) {
-                int32_t x = v[p];
-                int64_t q = p - 1;
-                while (q >= b && v[q] > x) {
-                    v[q + 1] = v[q];
-                    --q;
-                }
-                v[q + 1] = x;
-            }
-        return;
-    }
-    for (int j = threadIdx.x; j < len; j += 64) sh[j] = v[b + j];
-    __syncthreads();
-    for (int j = threadIdx.x; j < len; j += 64) {
-        const int32_t x = sh[j];
-        int r = 0;
-        for (int q = 0; q < len; ++q) r += sh[q] < x;
-        v[b + r] = x;
-    }
-}
 
 // Same, carrying a payload along with the key.
 __global__ void k_sort_segments_kv(int64_t nseg, const int64_t *__restrict__ off,
@@ -360,30 +329,35 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
 
 // Entries sent by every node: the count, and each entry's arrival rank at its sender (in an
 // arbitrary order; the segments are sorted by edge afterwards, so the final order is fixed).
-__global__ void k_tcount(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                         const int32_t *__restrict__ nbr, int32_t *__restrict__ cnt, int32_t *__restrict__ rank) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t b = sell_base(slab_off, i);
-    for (int j = 0; j < len[i]; ++j) {
-        const int64_t e = b + kSlab * j;
-        rank[e] = atomicAdd(&cnt[nbr[e]], 1);
-    }
-}
 
-__global__ void k_tfill(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                        const int32_t *__restrict__ nbr, const int64_t *__restrict__ t_off,
-                        const int32_t *__restrict__ rank, int32_t *__restrict__ t_eid) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t b = sell_base(slab_off, i);
-    for (int j = 0; j < len[i]; ++j) {
-        const int64_t e = b + kSlab * j;
-        t_eid[t_off[nbr[e]] + rank[e]] = (int32_t)e;
-    }
-}
 
 // Receiver of every entry.
+// Sort keys of the sender-major transpose: for every neighbour slot (the slab layout, padding slots
+// included) the sender node, or NN for a padding slot past its row's length; values = the slot.
+__global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
+                        const int32_t *__restrict__ nbr, uint32_t NN, uint32_t *__restrict__ keys,
+                        uint32_t *__restrict__ vals) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (slab, lane)
+    if (q >= nslab * kSlab) return;
+    const int64_t s = q / kSlab, r = q % kSlab, i = q;
+    const int64_t b = slab_off[s] + r, w = (slab_off[s + 1] - slab_off[s]) / kSlab;
+    const int nl = i < n ? len[i] : 0;
+    for (int64_t j = 0; j < w; ++j) {
+        const int64_t e = b + kSlab * j;
+        keys[e] = j < nl ? (uint32_t)nbr[e] : NN;
+        vals[e] = (uint32_t)e;
+    }
+}
+
+// Segment starts from the sorted keys: t_off[v] = first position whose key is >= v (t_off[NN] = E).
+__global__ void k_tsegments(int64_t E, const uint32_t *__restrict__ keys, int64_t NN, int64_t *__restrict__ t_off) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p > E) return;
+    const int64_t prev = p > 0 ? (int64_t)keys[p - 1] : -1;
+    const int64_t next = p < E ? (int64_t)keys[p] : NN;
+    for (int64_t v = prev + 1; v <= next; ++v) t_off[v] = p;
+}
+
 __global__ void k_edge_receiver(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
                                 int32_t *__restrict__ recv) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -675,24 +649,33 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
     MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
-    MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)NN1 + 64));
-    // per-entry scratch in the edge-gradient buffer (3 words per slot; it is written per step
-    // later): the arrival ranks in its first E1 words, the receivers in the next E1
+    // a stable radix sort of (sender node, slot) pairs in slot order: each sender's segment lists
+    // its slots in ascending order, so the transposed order (and every sum over it) is fixed.
+    // Scratch: the edge-gradient buffer (3 words per slot, written per step later) holds the keys,
+    // the values and the sorted keys; the sorted values are t_eid
     MPNN_TRY(cx.grow(cx.gedge, sizeof(float) * 3 * E1));
-    int32_t *trank = reinterpret_cast<int32_t *>(cx.gedge.p);
-    cnt = cx.tmp_c.as<int32_t>();
-    MPNN_HIP(hipMemsetAsync(cnt, 0, sizeof(int32_t) * NN1, cx.stream));
-    k_tcount<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-                                                    cx.nbr.as<int32_t>(), cnt, trank);
-    MPNN_HIP(hipGetLastError());
-    MPNN_TRY(exclusive_scan(cx, cnt, cx.NN, cx.t_off.as<int64_t>()));
-    k_tfill<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-                                                   cx.nbr.as<int32_t>(), cx.t_off.as<int64_t>(), trank,
-                                                   cx.t_eid.as<int32_t>());
-    MPNN_HIP(hipGetLastError());
-    if (cx.NN > 0)
-        k_rank_sort_segments<<<(unsigned)cx.NN, 64, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>());
-    MPNN_HIP(hipGetLastError());
+    {
+        uint32_t *keys = reinterpret_cast<uint32_t *>(cx.gedge.p), *vals = keys + E1, *skeys = vals + E1;
+        const int64_t nslab_all = (n + kSlab - 1) / kSlab;
+        if (Es > 0) {
+            k_tkeys<<<grid_for(nslab_all * kSlab), kBlock, 0, cx.stream>>>(
+                nslab_all, n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(),
+                (uint32_t)cx.NN, keys, vals);
+            MPNN_HIP(hipGetLastError());
+            int bits = 1;
+            while (bits < 32 && ((int64_t)1 << bits) <= cx.NN) ++bits;
+            size_t temp = 0;
+            MPNN_HIP(hipcub::DeviceRadixSort::SortPairs(nullptr, temp, keys, skeys, vals,
+                                                        reinterpret_cast<uint32_t *>(cx.t_eid.p), (int)Es, 0, bits,
+                                                        cx.stream));
+            MPNN_TRY(cx.grow(cx.tmp_scan, temp));
+            MPNN_HIP(hipcub::DeviceRadixSort::SortPairs(cx.tmp_scan.p, temp, keys, skeys, vals,
+                                                        reinterpret_cast<uint32_t *>(cx.t_eid.p), (int)Es, 0, bits,
+                                                        cx.stream));
+        }
+        k_tsegments<<<grid_for(E + 1), kBlock, 0, cx.stream>>>(E, skeys, cx.NN, cx.t_off.as<int64_t>());
+        MPNN_HIP(hipGetLastError());
+    }
     {
         // receiver of each edge, then of each transposed entry
         int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p) + E1;

@@ -397,5 +397,16 @@ def make_params(cfg: int, require_scales: bool = True, contraction_seed: int = N
     return p
 
 
+def depth_variant(cfg: int, T: int) -> Params:
+    """Benchmark model cfg rebuilt with T message-passing layers (same seed and draw order; the
+    frozen layer scales of the T-layer model, the last one repeated for deeper layers): the models
+    of the cost-against-depth measurement."""
+    base = make_params(cfg)
+    spec = dataclasses.replace(base.spec, T=T)
+    sc = list(base.layer_scale)
+    ls = [sc[min(t, len(sc) - 1)] for t in range(T)]
+    return random_params(spec, 1200 + cfg, base.masses, ls, base.e_scale)
+
+
 def small_spec(K=2, L=1, T=2, H=8, S=1, rc=4.0, skin=0.5, sigma=0.5) -> ModelSpec:
     return ModelSpec(n_species=S, K=K, L=L, T=T, H=H, rc=rc, sigma=sigma, skin=skin)

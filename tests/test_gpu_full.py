@@ -43,3 +43,4 @@ def test_full_size_parity(cfg):
     say(f"[full cfg{cfg}] oracle E/F in {time.time() - t0:.1f} s ({oracle.num_threads()} threads)")
     check_ei(Ei, Eio, label=f"full cfg{cfg} E_i")
     check_ef(E, F, Eo, Fo, label=f"full cfg{cfg}")
+

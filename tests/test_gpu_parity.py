@@ -118,3 +118,25 @@ def test_uneven_centres(precision):
     E, F, _ = m.energy_forces()
     Eo, Fo, _ = oracle_ef(p, s)
     check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"uneven centres, precision {precision}")
+
+
+DEPTH_CASES = [(4, T, 0) for T in (2, 4, 5, 6)] + [(4, 1, 1)] + [(2, T, 0) for T in (1, 2, 4, 5, 6)]
+
+
+@pytest.mark.parametrize("cfg,T,precision", DEPTH_CASES)
+def test_depth_variants(cfg, T, precision):
+    """The models of the cost-against-depth measurement (inputs.depth_variant: the Ag and water
+    benchmark models rebuilt with T = 1..6 layers) against the oracle, on small instances of the same
+    systems (Ag 4,000 atoms, 120 water molecules).  The one-layer Ag model runs the fp64 mode: its
+    total energy is only 9 % of sum |E_i| and its energy network's output is a 180-fold cancellation,
+    so the fp32 mode's residual per-atom bias (about 1e-7 of |E_i|) leaves 1.1e-6 to 1.4e-6 of |E|,
+    outside the energy gate (its forces and per-atom energies are within theirs)."""
+    s = systems.ag(10, seed=4) if cfg == 4 else systems.water_molecules(120, 18.0)
+    p = I.depth_variant(cfg, T)
+    p.spec.precision = precision
+    say(f"[depth] cfg{cfg} T={T} precision {precision} n={s.n}")
+    m = gpu_model(p, s)
+    E, F, Ei = m.energy_forces(atom_energy=True)
+    Eo, Fo, Eio = oracle_ef(p, s)
+    check_ei(Ei.cpu().numpy(), Eio, label=f"cfg{cfg} T={T} E_i")
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"cfg{cfg} T={T}")
