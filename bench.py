@@ -192,8 +192,9 @@ def roofline_for(fam, ms_avg, g, cfg=4, precision=0, contracted=False):
             out["valu_tflops_at_algorithmic_flops"] = round(flops / t / 1e12, 2)
     v = measured_valu(fam, cfg, precision, contracted)
     if v is not None:
-        out["valu_busy"] = v.get("valu_busy")
-        out["valu_insts_per_unit"] = v.get("valu_insts_per_unit")
+        out["valu_busy"] = v.get("valu_busy")            # % of SIMD cycles issuing VALU (SQ counters)
+        out["valu_insts_per_unit"] = v.get("valu_insts_per_unit")   # per lane-edge
+        out["ta_busy"] = v.get("ta_busy")                # % of cycles the texture-address unit is busy
     return out
 
 
