@@ -665,7 +665,9 @@ __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64
 // LANES = 1: one row per lane, 256-row blocks (row bucketing applies) with LDS-staged tile stores;
 // LANES = 16 (small systems): one row per lane group, the group's partial sums combined by
 // group_sum16 and the row's columns written by its lanes.
-template <int K, int L, bool CHAIN, bool CT, bool NT, int LANES>
+// C0U (layer 0 of a one-species model): every neighbour's message is C0 of the species, taken from
+// the model constants, so only the position part of each node record is gathered.
+template <int K, int L, bool CHAIN, bool CT, bool NT, int LANES, bool C0U = false>
 __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
@@ -693,6 +695,11 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
     // one row per thread: indices staged kIdxStage at a time; lane groups: one span, direct loads
     constexpr int SPAN = LANES == 1 ? kIdxStage : (1 << 24);
     __shared__ int32_t stage[LANES == 1 ? kIdxStage : 1][kBlock];
+    float c0u[K];
+    if constexpr (C0U) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) c0u[k] = md->c0[k];
+    }
     if (i < n) {
         const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
         const int64_t b0 = sell_base(slab_off, i);
@@ -708,7 +715,7 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
                 const double px = pv[0], py = pv[1], pz = pv[2];
                 float cr[K];
 #pragma unroll
-                for (int k = 0; k < K; ++k) cr[k] = rv[kRecC + k];
+                for (int k = 0; k < K; ++k) cr[k] = C0U ? c0u[k] : rv[kRecC + k];
                 __builtin_amdgcn_sched_barrier(0);   // the whole record is requested before the basis starts
                 b.eval(px - xi, py - yi, pz - zi, cr, md);
 #pragma unroll
@@ -875,7 +882,8 @@ __device__ __forceinline__ void store_gedge(float *__restrict__ ge, const float 
     }
 }
 
-template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES>
+// C0U: layer 0 of a one-species model (see k_aggregate): the messages come from the model constants.
+template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES, bool C0U = false>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
@@ -905,6 +913,11 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
     const double xi = pos[3 * ir_], yi = pos[3 * ir_ + 1], zi = pos[3 * ir_ + 2];
     float G[K][M];
     assemble_go_row<K, L>(Grho, Ot, np, ir_, G);
+    float c0u[K];
+    if constexpr (C0U) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) c0u[k] = md->c0[k];
+    }
     double F[3] = {0.0, 0.0, 0.0};
     const int64_t b0 = sell_base(slab_off, ir_);
     const int na = row ? nact[ir_] : 0;
@@ -916,7 +929,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
         Basis<K, L, CT> b;
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
         float g[3];
-        edge_vjp<K, L, WANT_W, NT>(b, rv + kRecC, G, ir, w + e * K, g);
+        edge_vjp<K, L, WANT_W, NT>(b, C0U ? c0u : rv + kRecC, G, ir, w + e * K, g);
         store_gedge<FIRST, NT>(gedge + 3 * e, g);
         F[0] += (double)g[0];
         F[1] += (double)g[1];
@@ -1232,23 +1245,29 @@ Status aggregate(Context &cx, int t) {
     const float *ct = cx.c.as<float>() + (int64_t)t * cx.NN * rec_stride(cx.K);
     float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     float *Ft = cx.feat.as<float>() + (int64_t)t * cx.np * cx.DP;
+    // layer 0 of a one-species model: the messages are the model's C0 (uniform)
+    const bool c0u = t == 0 && cx.S == 1 && !cx.contracted;
     if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
-#define MPNN_AGG32_NT(CH, CT, NT)                                                                               \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT, 1><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(  \
+#define MPNN_AGG32_NT(CH, CT, NT, U)                                                                            \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT, 1, U><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], row_perm(cx), Ot, Ft)))
-#define MPNN_AGG32_LG(CH, CT)                                                                                   \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, false, kGatherLanes><<<grid_for(cx.n * kGatherLanes), \
+#define MPNN_AGG32_LG(CH, CT, U)                                                                                \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, false, kGatherLanes, U><<<grid_for(cx.n * kGatherLanes), \
                                                                                    kBlock, 0, cx.stream>>>(      \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], nullptr, Ot, Ft)))
 #define MPNN_AGG32(CH, CT)                                                                                      \
     do {                                                                                                        \
-        if (cx.lane_groups) MPNN_AGG32_LG(CH, CT);                                                              \
-        else if (cx.nt) MPNN_AGG32_NT(CH, CT, true);                                                            \
-        else MPNN_AGG32_NT(CH, CT, false);                                                                      \
+        if (!(CT) && c0u) {                                                                                     \
+            if (cx.lane_groups) MPNN_AGG32_LG(CH, false, true);                                                 \
+            else if (cx.nt) MPNN_AGG32_NT(CH, false, true, true);                                               \
+            else MPNN_AGG32_NT(CH, false, false, true);                                                         \
+        } else if (cx.lane_groups) MPNN_AGG32_LG(CH, CT, false);                                                \
+        else if (cx.nt) MPNN_AGG32_NT(CH, CT, true, false);                                                     \
+        else MPNN_AGG32_NT(CH, CT, false, false);                                                               \
     } while (0)
         if (cx.contracted) {
             if (cx.chain) MPNN_AGG32(true, true);
@@ -1308,6 +1327,7 @@ Status backward_layer(Context &cx, int t) {
     const float *Gt = cx.grho.as<float>() + (int64_t)t * cx.np * cx.DP;
     const float *Ot = cx.O.as<float>() + (int64_t)t * cx.np * pad16(cx.K * cx.M);
     const bool first = (t == cx.T - 1), want_w = (t >= 1);
+    const bool c0u = t == 0 && cx.S == 1 && !cx.contracted;   // layer-0 messages uniform (see aggregate)
 #define MPNN_BWD(FIRST_, W_)                                                                               \
     do {                                                                                                   \
         if (cx.contracted) MPNN_BWD_CT(FIRST_, W_, true);                                                  \
@@ -1318,24 +1338,28 @@ Status backward_layer(Context &cx, int t) {
         if (!CT_ && cx.K == 12) {                                                                          \
             if (cx.nt) MPNN_BWD_SPLIT(FIRST_, W_, true);                                                   \
             else MPNN_BWD_SPLIT(FIRST_, W_, false);                                                        \
-        } else if (cx.lane_groups) MPNN_BWD_LG(FIRST_, W_, CT_);                                           \
-        else if (cx.nt) MPNN_BWD_NT(FIRST_, W_, CT_, true);                                                \
-        else MPNN_BWD_NT(FIRST_, W_, CT_, false);                                                          \
+        } else if (!(CT_) && !(W_) && c0u) {                                                              \
+            if (cx.lane_groups) MPNN_BWD_LG(FIRST_, false, false, true);                                   \
+            else if (cx.nt) MPNN_BWD_NT(FIRST_, false, false, true, true);                                 \
+            else MPNN_BWD_NT(FIRST_, false, false, false, true);                                           \
+        } else if (cx.lane_groups) MPNN_BWD_LG(FIRST_, W_, CT_, false);                                    \
+        else if (cx.nt) MPNN_BWD_NT(FIRST_, W_, CT_, true, false);                                         \
+        else MPNN_BWD_NT(FIRST_, W_, CT_, false, false);                                                   \
     } while (0)
 #define MPNN_BWD_SPLIT(FIRST_, W_, NT_)                                                                    \
     k_backward_split<12, 3, FIRST_, W_, NT_><<<grid_xcd(2 * cx.n), kBlock, 0, cx.stream>>>(                \
         cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), \
         ct, Gt, Ot, cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(),          \
         cx.Frecv.as<double>())
-#define MPNN_BWD_LG(FIRST_, W_, CT_)                                                                       \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, false, kGatherLanes>           \
+#define MPNN_BWD_LG(FIRST_, W_, CT_, U_)                                                                   \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, false, kGatherLanes, U_>       \
                                   <<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(                 \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), nullptr, cx.w.as<float>(), cx.gedge.as<float>(), \
                                       cx.Frecv.as<double>())))
-#define MPNN_BWD_NT(FIRST_, W_, CT_, NT_)                                                                  \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+#define MPNN_BWD_NT(FIRST_, W_, CT_, NT_, U_)                                                              \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1, U_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
