@@ -124,6 +124,10 @@ Context::~Context() {
     for (hipEvent_t e : cap_ev)
         if (e) (void)hipEventDestroy(e);
     if (cap_stream) (void)hipStreamDestroy(cap_stream);
+    if (side_stream) (void)hipStreamSynchronize(side_stream);
+    for (hipEvent_t e : side_ev)
+        if (e) (void)hipEventDestroy(e);
+    if (side_stream) (void)hipStreamDestroy(side_stream);
     for (Buf *b : all) release(*b);
     prof_harvest();
     for (hipEvent_t e : prof_pool) (void)hipEventDestroy(e);
@@ -141,6 +145,9 @@ bool supported(int K, int L, int H) {
 Status evaluate(Context &cx, double *F_caller, double *red_part = nullptr) {
     MPNN_TRY(refresh_ghost_positions(cx));
     MPNN_TRY(compact_active(cx));
+    // the transposed active map depends only on the compaction: it is built on the side stream
+    // while the forward layers run, and joined before the first sender-major gather
+    MPNN_TRY(fork_transpose(cx));
     for (int t = 0; t < cx.T; ++t) {
         MPNN_TRY(aggregate(cx, t));
         if (t < cx.T - 1) {
@@ -152,12 +159,12 @@ Status evaluate(Context &cx, double *F_caller, double *red_part = nullptr) {
     }
     for (int t = cx.T - 1; t >= 0; --t) {
         MPNN_TRY(backward_layer(cx, t));
+        if (t == cx.T - 1) MPNN_TRY(join_transpose(cx));
         if (t >= 1) {
             MPNN_TRY(backward_messages(cx, t));
             MPNN_TRY(mlp_backward(cx, t - 1));
         }
     }
-    if (cx.T == 1) MPNN_TRY(transpose_active(cx));
     MPNN_TRY(force_gather(cx, F_caller));
     MPNN_TRY(energy_reduce(cx, red_part));
     cx.forces_valid = true;

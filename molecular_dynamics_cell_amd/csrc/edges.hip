@@ -1041,15 +1041,11 @@ __global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np
 // Sender-major gathers use kGatherLanes lanes per node (see group_sum16 above).
 
 // dE/dc^t of every node v (local or ghost): the w_e of the active edges v sends (Eq. 4 first
-// term, gathered without atomics).  The first gather of an evaluation (BUILD) looks up the active
-// slot of each transposed entry through the per-step map and records it in t_act, so the later
-// gathers read it sequentially.
-template <int K, bool BUILD>
-__global__ __launch_bounds__(256) void k_gather_w(int64_t NN, int64_t n, const int64_t *__restrict__ t_off,
-                                                  const int32_t *__restrict__ t_eid, const int32_t *__restrict__ t_recv,
-                                                  const int64_t *__restrict__ slab_off,
-                                                  const uint32_t *__restrict__ amask,
-                                                  int32_t *__restrict__ t_act, const float *__restrict__ w,
+// term, gathered without atomics).  t_act holds the active slot of each transposed entry for this
+// step (k_transpose_active), so the gather reads it sequentially.
+template <int K>
+__global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__restrict__ t_off,
+                                                  const int32_t *__restrict__ t_act, const float *__restrict__ w,
                                                   float *__restrict__ Gc) {
     const int64_t v = (xcd_block() * blockDim.x + threadIdx.x) / kGatherLanes;
     const int q = threadIdx.x % kGatherLanes;
@@ -1062,18 +1058,8 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, int64_t n, const i
         // two entries per lane per step, so both lookups are in flight together
         for (int64_t s = t_off[v] + q; s < s1; s += 2 * kGatherLanes) {
             const bool two = s + kGatherLanes < s1;
-            int32_t a0, a1 = -1;
-            if (BUILD) {
-                const int32_t e0 = t_eid[s], e1 = two ? t_eid[s + kGatherLanes] : 0;
-                const int32_t r0 = t_recv[s], r1 = two ? t_recv[s + kGatherLanes] : 0;
-                a0 = active_slot(r0, e0, slab_off, amask, n);
-                if (two) a1 = active_slot(r1, e1, slab_off, amask, n);
-                t_act[s] = a0;
-                if (two) t_act[s + kGatherLanes] = a1;
-            } else {
-                a0 = t_act[s];
-                if (two) a1 = t_act[s + kGatherLanes];
-            }
+            const int32_t a0 = t_act[s];
+            const int32_t a1 = two ? t_act[s + kGatherLanes] : -1;
             float w0[K], w1[K];
 #pragma unroll
             for (int k = 0; k < K; ++k) w0[k] = w1[k] = 0.0f;
@@ -1098,7 +1084,7 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, int64_t n, const i
         for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
 }
 
-// t_act alone (evaluations without message layers, where no gather builds it).
+// t_act: the active slot (or -1) of every transposed entry under this step's compaction.
 __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, const int32_t *__restrict__ t_eid,
                                                           const int32_t *__restrict__ t_recv,
                                                           const int64_t *__restrict__ slab_off,
@@ -1387,12 +1373,22 @@ Status assemble_go(Context &cx, int t, float *out) {
     return Status::ok();
 }
 
-Status transpose_active(Context &cx) {
-    if (cx.E == 0) return Status::ok();
-    k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.stream>>>(cx.E, cx.n, cx.t_eid.as<int32_t>(),
-                                                                 cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
-                                                                 cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
-    MPNN_HIP(hipGetLastError());
+Status fork_transpose(Context &cx) {
+    if (!cx.side_stream) return Status::err(MPNN_E_STATE, "side stream not created");
+    MPNN_HIP(hipEventRecord(cx.side_ev[0], cx.stream));
+    MPNN_HIP(hipStreamWaitEvent(cx.side_stream, cx.side_ev[0], 0));
+    if (cx.E > 0) {
+        k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.side_stream>>>(
+            cx.E, cx.n, cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
+            cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
+        MPNN_HIP(hipGetLastError());
+    }
+    MPNN_HIP(hipEventRecord(cx.side_ev[1], cx.side_stream));
+    return Status::ok();
+}
+
+Status join_transpose(Context &cx) {
+    MPNN_HIP(hipStreamWaitEvent(cx.stream, cx.side_ev[1], 0));
     return Status::ok();
 }
 
@@ -1402,16 +1398,9 @@ Status backward_messages(Context &cx, int t) {
     {
         ProfScope ps_(cx, kProfMessageGrad);
         const unsigned gg = grid_xcd(cx.NN * kGatherLanes);
-        const bool build = (t == cx.T - 1);
-#define MPNN_GW(KK)                                                                                           \
-    if (build)                                                                                                \
-        k_gather_w<KK, true><<<gg, kBlock, 0, cx.stream>>>(                                                   \
-            cx.NN, cx.n, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(),               \
-            cx.slab_off.as<int64_t>(), cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>(), cx.w.as<float>(), Gct);  \
-    else                                                                                                      \
-        k_gather_w<KK, false><<<gg, kBlock, 0, cx.stream>>>(                                                  \
-            cx.NN, cx.n, cx.t_off.as<int64_t>(), cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(),               \
-            cx.slab_off.as<int64_t>(), cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>(), cx.w.as<float>(), Gct)
+#define MPNN_GW(KK)                                                                                 \
+    k_gather_w<KK><<<gg, kBlock, 0, cx.stream>>>(cx.NN, cx.t_off.as<int64_t>(), cx.t_act.as<int32_t>(), \
+                                                 cx.w.as<float>(), Gct)
         switch (cx.K) {
             case 2: MPNN_GW(2); break;
             case 4: MPNN_GW(4); break;

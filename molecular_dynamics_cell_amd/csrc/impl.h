@@ -159,6 +159,10 @@ struct Context {
     hipStream_t cap_stream = nullptr;    // own (non-default, default-priority) stream: graphs are
                                          // captured and replayed there, ordered by events
     hipEvent_t cap_ev[2] = {nullptr, nullptr};
+    // second stream (default priority) on which the transposed active map of each evaluation is
+    // built while the forward layers run; events fork it from and join it to the context's stream
+    hipStream_t side_stream = nullptr;
+    hipEvent_t side_ev[2] = {nullptr, nullptr};
     double prof_ms[kProfCount] = {};
     int64_t prof_launches[kProfCount] = {};
     std::vector<hipEvent_t> prof_pool;
@@ -205,7 +209,10 @@ Status refresh_ghost_features(Context &cx, int t);
 Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
 Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagnostics)
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
-Status transpose_active(Context &cx);             // t_act alone (T == 1)
+// t_act (the active slot of every transposed entry) for this step, on the side stream, forked from
+// the context's stream after the compaction; join_transpose makes the context's stream wait for it
+Status fork_transpose(Context &cx);
+Status join_transpose(Context &cx);
 Status force_gather(Context &cx, double *F_caller);
 
 // ---- mlp.hip ----

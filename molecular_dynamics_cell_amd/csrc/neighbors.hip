@@ -738,6 +738,9 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_HIP(hipGetLastError());
     cx.prof_end(kProfBuildSpecies);
     MPNN_HIP(hipStreamSynchronize(cx.stream));
+    if (!cx.side_stream) MPNN_HIP(hipStreamCreateWithFlags(&cx.side_stream, hipStreamNonBlocking));
+    for (hipEvent_t &e : cx.side_ev)
+        if (!e) MPNN_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     cx.built = true;
     cx.stale = false;
     cx.since_build = 0;
