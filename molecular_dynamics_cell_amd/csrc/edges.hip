@@ -1374,21 +1374,25 @@ Status assemble_go(Context &cx, int t, float *out) {
 }
 
 Status fork_transpose(Context &cx) {
-    if (!cx.side_stream) return Status::err(MPNN_E_STATE, "side stream not created");
-    MPNN_HIP(hipEventRecord(cx.side_ev[0], cx.stream));
-    MPNN_HIP(hipStreamWaitEvent(cx.side_stream, cx.side_ev[0], 0));
+    hipStream_t s = cx.stream;
+    if (cx.side) {
+        if (!cx.side_stream) return Status::err(MPNN_E_STATE, "side stream not created");
+        MPNN_HIP(hipEventRecord(cx.side_ev[0], cx.stream));
+        MPNN_HIP(hipStreamWaitEvent(cx.side_stream, cx.side_ev[0], 0));
+        s = cx.side_stream;
+    }
     if (cx.E > 0) {
-        k_transpose_active<<<grid_for(cx.E), kBlock, 0, cx.side_stream>>>(
-            cx.E, cx.n, cx.t_eid.as<int32_t>(), cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
-            cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
+        k_transpose_active<<<grid_for(cx.E), kBlock, 0, s>>>(cx.E, cx.n, cx.t_eid.as<int32_t>(),
+                                                           cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
+                                                           cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }
-    MPNN_HIP(hipEventRecord(cx.side_ev[1], cx.side_stream));
+    if (cx.side) MPNN_HIP(hipEventRecord(cx.side_ev[1], cx.side_stream));
     return Status::ok();
 }
 
 Status join_transpose(Context &cx) {
-    MPNN_HIP(hipStreamWaitEvent(cx.stream, cx.side_ev[1], 0));
+    if (cx.side) MPNN_HIP(hipStreamWaitEvent(cx.stream, cx.side_ev[1], 0));
     return Status::ok();
 }
 

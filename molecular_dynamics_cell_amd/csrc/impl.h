@@ -163,6 +163,7 @@ struct Context {
     // built while the forward layers run; events fork it from and join it to the context's stream
     hipStream_t side_stream = nullptr;
     hipEvent_t side_ev[2] = {nullptr, nullptr};
+    bool side = false;   // transposed map on the side stream (large lists), else inline after the compaction
     double prof_ms[kProfCount] = {};
     int64_t prof_launches[kProfCount] = {};
     std::vector<hipEvent_t> prof_pool;
@@ -209,8 +210,9 @@ Status refresh_ghost_features(Context &cx, int t);
 Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
 Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagnostics)
 Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
-// t_act (the active slot of every transposed entry) for this step, on the side stream, forked from
-// the context's stream after the compaction; join_transpose makes the context's stream wait for it
+// t_act (the active slot of every transposed entry) for this step: on the side stream, forked from
+// the context's stream after the compaction, for long lists (Context::side), else on the context's
+// stream; join_transpose makes the context's stream wait for the side stream
 Status fork_transpose(Context &cx);
 Status join_transpose(Context &cx);
 Status force_gather(Context &cx, double *F_caller);

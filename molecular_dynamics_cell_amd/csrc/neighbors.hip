@@ -738,9 +738,12 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_HIP(hipGetLastError());
     cx.prof_end(kProfBuildSpecies);
     MPNN_HIP(hipStreamSynchronize(cx.stream));
-    if (!cx.side_stream) MPNN_HIP(hipStreamCreateWithFlags(&cx.side_stream, hipStreamNonBlocking));
+    // a second stream pays where the map's build is long enough to hide (measured: the fork and join
+    // cost Ag108 a third of its step inside replayed graphs)
+    cx.side = cx.E >= ((int64_t)1 << 22);
+    if (cx.side && !cx.side_stream) MPNN_HIP(hipStreamCreateWithFlags(&cx.side_stream, hipStreamNonBlocking));
     for (hipEvent_t &e : cx.side_ev)
-        if (!e) MPNN_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        if (cx.side && !e) MPNN_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
     cx.built = true;
     cx.stale = false;
     cx.since_build = 0;
