@@ -1084,14 +1084,18 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
         for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
 }
 
-// t_act: the active slot (or -1) of every transposed entry under this step's compaction.
+// t_act: the active slot (or -1) of every transposed entry under this step's compaction; the
+// entry's receiver row follows from its slot (the slab of its 64-slot run, and the slot mod 64).
 __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, const int32_t *__restrict__ t_eid,
-                                                          const int32_t *__restrict__ t_recv,
+                                                          const int32_t *__restrict__ blk_slab,
                                                           const int64_t *__restrict__ slab_off,
                                                           const uint32_t *__restrict__ amask,
                                                           int32_t *__restrict__ t_act) {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < E) t_act[s] = active_slot(t_recv[s], t_eid[s], slab_off, amask, n);
+    if (s >= E) return;
+    const int32_t e = t_eid[s];
+    const int64_t r = (int64_t)blk_slab[e / kSlab] * kSlab + e % kSlab;
+    t_act[s] = active_slot(r, e, slab_off, amask, n);
 }
 
 // Ghost -> owner sum of dE/dc (the reverse ghost exchange), ghosts of an owner in order.
@@ -1383,7 +1387,7 @@ Status fork_transpose(Context &cx) {
     }
     if (cx.E > 0) {
         k_transpose_active<<<grid_for(cx.E), kBlock, 0, s>>>(cx.E, cx.n, cx.t_eid.as<int32_t>(),
-                                                           cx.t_recv.as<int32_t>(), cx.slab_off.as<int64_t>(),
+                                                           cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
                                                            cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }

@@ -327,11 +327,6 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
     if (!FILL) cnt[i] = c;
 }
 
-// Entries sent by every node: the count, and each entry's arrival rank at its sender (in an
-// arbitrary order; the segments are sorted by edge afterwards, so the final order is fixed).
-
-
-// Receiver of every entry.
 // Sort keys of the sender-major transpose: for every neighbour slot (the slab layout, padding slots
 // included) the sender node, or NN for a padding slot past its row's length; values = the slot.
 __global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
@@ -358,12 +353,12 @@ __global__ void k_tsegments(int64_t E, const uint32_t *__restrict__ keys, int64_
     for (int64_t v = prev + 1; v <= next; ++v) t_off[v] = p;
 }
 
-__global__ void k_edge_receiver(int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                                int32_t *__restrict__ recv) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int64_t b = sell_base(slab_off, i);
-    for (int j = 0; j < len[i]; ++j) recv[b + kSlab * j] = (int32_t)i;
+// Slab of every run of 64 slots: slab s owns the runs slab_off[s]/64 .. slab_off[s+1]/64 - 1, and
+// slot e of it belongs to row 64 s + e % 64 (slab offsets are multiples of 64).
+__global__ void k_blk_slab(int64_t nslab, const int64_t *__restrict__ slab_off, int32_t *__restrict__ blk_slab) {
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nslab) return;
+    for (int64_t q = slab_off[s] / kSlab; q < slab_off[s + 1] / kSlab; ++q) blk_slab[q] = (int32_t)s;
 }
 
 // Width of each 64-row slab (its longest row), times 64.
@@ -375,11 +370,6 @@ __global__ void k_slab_width(int64_t n, int64_t nslab, const int32_t *__restrict
     sw[s] = w * kSlab;
 }
 
-__global__ void k_tmap_recv(int64_t E, const int32_t *__restrict__ t_eid, const int32_t *__restrict__ recv_of_edge,
-                            int32_t *__restrict__ t_recv) {
-    int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < E) t_recv[s] = recv_of_edge[t_eid[s]];
-}
 
 __global__ void k_flag_species(int64_t n, const int32_t *__restrict__ types, int s, int32_t *__restrict__ f) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -647,7 +637,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
     cx.prof_begin(kProfBuildTranspose);
     MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
-    MPNN_TRY(cx.grow(cx.t_recv, sizeof(int32_t) * E1));
+    MPNN_TRY(cx.grow(cx.blk_slab, sizeof(int32_t) * (size_t)(E1 / kSlab + 1)));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
     // a stable radix sort of (sender node, slot) pairs in slot order: each sender's segment lists
     // its slots in ascending order, so the transposed order (and every sum over it) is fixed.
@@ -677,13 +667,12 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         MPNN_HIP(hipGetLastError());
     }
     {
-        // receiver of each edge, then of each transposed entry
-        int32_t *recv = reinterpret_cast<int32_t *>(cx.gedge.p) + E1;
-        k_edge_receiver<<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.slab_off.as<int64_t>(),
-                                                               cx.row_len.as<int32_t>(), recv);
-        MPNN_HIP(hipGetLastError());
-        k_tmap_recv<<<grid_for(E), kBlock, 0, cx.stream>>>(E, cx.t_eid.as<int32_t>(), recv, cx.t_recv.as<int32_t>());
-        MPNN_HIP(hipGetLastError());
+        const int64_t nslab_all = (n + kSlab - 1) / kSlab;
+        if (nslab_all > 0) {
+            k_blk_slab<<<grid_for(nslab_all), kBlock, 0, cx.stream>>>(nslab_all, cx.slab_off.as<int64_t>(),
+                                                                      cx.blk_slab.as<int32_t>());
+            MPNN_HIP(hipGetLastError());
+        }
     }
 
     cx.prof_end(kProfBuildTranspose);
