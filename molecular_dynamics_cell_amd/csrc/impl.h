@@ -107,6 +107,7 @@ struct Context {
     Buf row_len;                    // int32 [n] Verlet entries per row
     Buf slab_off;                   // int64 [n/64+2] start of each 64-row slab
     Buf nbr;                        // int32 [E_sell] sender node of each entry (sliced ELLPACK)
+    Buf cellpos;                    // float4 [NN]: fp32 node positions in grid-cell order (build only)
     Buf t_off, t_eid;               // int64 [NN+1], int32 [E]: sender-major segments, slot of each entry
     Buf blk_slab;                   // int32 [E_sell/64]: slab of each run of 64 slots (slot -> receiver row)
     Buf sp_list, sp_off;            // int32 [n], int64 [S+1]

@@ -276,17 +276,30 @@ __global__ void k_ext_key(int64_t NN, int64_t n, const double *__restrict__ pos,
     key[v] = (int32_t)ext_key(x, q, g);
 }
 
+// Node positions in grid-cell order (the order of cnodes) in fp32, with the node's index in the
+// fourth word: the row search reads each cell's candidates as one contiguous run.
+__global__ void k_cell_pos(int64_t NN, const int32_t *__restrict__ cnodes, const double *__restrict__ pos,
+                           float4 *__restrict__ cp) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= NN) return;
+    const int64_t v = cnodes[p];
+    cp[p] = float4{(float)pos[3 * v], (float)pos[3 * v + 1], (float)pos[3 * v + 2], __int_as_float((int32_t)v)};
+}
+
 // Receiver rows: every node v != i of the 27 extended cells around local atom i with
 // (dx*dx + dy*dy) + dz*dz < rcut^2 in fp64.  Cells in fixed (dx, dy, dz) order, nodes of a cell
-// in ascending id, so rows are deterministic.
+// in ascending id, so rows are deterministic.  The test runs first on the fp32 positions: d^2 from
+// them is within `band` of the fp64 value (the bound of the per-step compaction, with rcut), so
+// only candidates with d^2 in [lo, hi] = rcut^2 -/+ band repeat it in fp64.
 template <bool FILL>
 __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
-                       const int64_t *__restrict__ coff, const int32_t *__restrict__ cnodes,
-                       double rcut2, int32_t *__restrict__ cnt, const int64_t *__restrict__ slab_off,
-                       int32_t *__restrict__ nbr) {
+                       const int64_t *__restrict__ coff, const float4 *__restrict__ cp,
+                       double rcut2, float lo, float hi, int32_t *__restrict__ cnt,
+                       const int64_t *__restrict__ slab_off, int32_t *__restrict__ nbr) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const double xi = pos[3 * i], yi = pos[3 * i + 1], zi = pos[3 * i + 2];
+    const float xf = (float)xi, yf = (float)yi, zf = (float)zi;
     // the stencil lives in the receiver's own subdomain grid, which holds only its nodes
     const double xv[3] = {xi, yi, zi};
     const int q = own_sub(xv, g);
@@ -311,12 +324,16 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
                 if (z < 0 || z > g.n[2] + 1) continue;
                 int64_t cell = cell0 + ((int64_t)x * ny + y) * nz + z;
                 for (int64_t p = coff[cell]; p < coff[cell + 1]; ++p) {
-                    int32_t v = cnodes[p];
+                    const float4 c4 = cp[p];
+                    const int32_t v = __float_as_int(c4.w);
                     if (v == (int32_t)i) continue;
-                    double d2 = d2_exact(__dsub_rn(pos[3 * (int64_t)v], xi),
-                                         __dsub_rn(pos[3 * (int64_t)v + 1], yi),
-                                         __dsub_rn(pos[3 * (int64_t)v + 2], zi));
-                    if (d2 < rcut2) {
+                    const float dx = c4.x - xf, dy = c4.y - yf, dz = c4.z - zf;
+                    const float d2f = dx * dx + dy * dy + dz * dz;
+                    bool in = d2f < lo;
+                    if (!in && d2f < hi)
+                        in = d2_exact(__dsub_rn(pos[3 * (int64_t)v], xi), __dsub_rn(pos[3 * (int64_t)v + 1], yi),
+                                      __dsub_rn(pos[3 * (int64_t)v + 2], zi)) < rcut2;
+                    if (in) {
                         if (FILL) nbr[base + kSlab * (o++)] = v;
                         else ++c;
                     }
@@ -575,11 +592,22 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
 
     // ---- receiver rows ----
     const double rcut2 = w * w;
+    // fp32 pre-test band (as in the per-step compaction, with rcut): coordinates within [-c, c]
+    const double cmax = std::max(cx.box[0], std::max(cx.box[1], cx.box[2])) + cx.rc + 2.0 * skin;
+    const double eps32 = cmax * std::ldexp(1.0, -24);
+    const double band = 2.0 * (4.0 * std::sqrt(3.0) * eps32 * w + 4.0 * std::ldexp(1.0, -23) * w * w) + 1e-9;
+    const float lo = (float)(rcut2 - band), hi = (float)(rcut2 + band);
+    MPNN_TRY(cx.grow(cx.cellpos, sizeof(float4) * NN1));
+    if (cx.NN > 0) {
+        k_cell_pos<<<grid_for(cx.NN), kBlock, 0, cx.stream>>>(cx.NN, cnodes, cx.pos.as<double>(),
+                                                               cx.cellpos.as<float4>());
+        MPNN_HIP(hipGetLastError());
+    }
     MPNN_TRY(cx.grow(cx.tmp_c, sizeof(int32_t) * (size_t)(n1 > next ? n1 : next) + 64));
     cnt = cx.tmp_c.as<int32_t>();
     MPNN_TRY(cx.grow(cx.row_off, sizeof(int64_t) * (n1 + 1)));
-    k_rows<false><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, cnt,
-                                                         nullptr, nullptr);
+    k_rows<false><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cx.cellpos.as<float4>(),
+                                                         rcut2, lo, hi, cnt, nullptr, nullptr);
     MPNN_HIP(hipGetLastError());
     MPNN_TRY(cx.grow(cx.row_len, sizeof(int32_t) * n1));
     if (n > 0)
@@ -629,8 +657,9 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     cx.E_sell = Es;
     const int64_t E1 = Es > 0 ? Es : 1;
     MPNN_TRY(cx.grow(cx.nbr, sizeof(int32_t) * E1));
-    k_rows<true><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cnodes, rcut2, nullptr,
-                                                        cx.slab_off.as<int64_t>(), cx.nbr.as<int32_t>());
+    k_rows<true><<<grid_for(n), kBlock, 0, cx.stream>>>(n, cx.pos.as<double>(), g, off, cx.cellpos.as<float4>(),
+                                                        rcut2, lo, hi, nullptr, cx.slab_off.as<int64_t>(),
+                                                        cx.nbr.as<int32_t>());
     MPNN_HIP(hipGetLastError());
     cx.prof_end(kProfBuildRows);
 
