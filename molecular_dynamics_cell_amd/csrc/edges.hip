@@ -312,6 +312,7 @@ __device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], SC 
 // combined by a fixed butterfly, after which every lane of the group holds the same bits (each
 // step adds two operands in either order), so the result is reproducible.
 constexpr int kGatherLanes = 16;
+constexpr int kRecWin = 512;   // nodes per staged record window of the row kernels
 
 template <class T>
 __device__ __forceinline__ T group_sum16(T x) {
@@ -667,8 +668,12 @@ __device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64
 // group_sum16 and the row's columns written by its lanes.
 // C0U (layer 0 of a one-species model): every neighbour's message is C0 of the species, taken from
 // the model constants, so only the position part of each node record is gathered.
-template <int K, int L, bool CHAIN, bool CT, bool NT, int LANES, bool C0U = false>
-__global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const double *__restrict__ pos,
+// WIN > 0 (one row per lane): the records of nodes lo .. lo + WIN - 1, a window of node indices
+// centred on the block's rows, are staged in LDS once per block, and the edges whose sender falls
+// in it read the record there; the rest read it from global memory.  Rows are in cell order, so
+// most senders of a block lie in such a window.
+template <int K, int L, bool CHAIN, bool CT, bool NT, int LANES, bool C0U = false, int WIN = 0>
+__global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t NN, int64_t np, const double *__restrict__ pos,
                                                    const int64_t *__restrict__ slab_off,
                                                    const int32_t *__restrict__ nact,
                                                    const int32_t *__restrict__ act_n, const float *__restrict__ c,
@@ -676,13 +681,27 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
                                                    const int32_t *__restrict__ row_perm,
                                                    float *__restrict__ O, float *__restrict__ feat) {
     static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
+    static_assert(WIN == 0 || LANES == 1, "record window with one row per lane only");
     constexpr int M = n_mono(L), KMT = pad16(K * M) / 16, DT = pad16(n_feat(K, L)) / 16;
-    int64_t i, i0 = 0;
+    constexpr int RQ = rec_stride(K) / 4;       // float4 per record
+    constexpr int RQL = C0U ? 2 : RQ;           // staged per record: the position part, or all
+    constexpr int SHQ = WIN * RQL > 5 * kBlock ? WIN * RQL : 5 * kBlock;
+    __shared__ float4 shm[LANES == 1 ? SHQ : 1];   // the window, then the tile stores' staging
+    int64_t i, i0 = 0, lo = 0, nwin = 0;
     int q = 0;
     if constexpr (LANES == 1) {
         i0 = xcd_block() * kBlock;
         if (i0 >= n) return;                       // whole block past the end (grid rounded to 8 XCDs)
         i = block_row(i0, n, row_perm);
+        if constexpr (WIN > 0) {
+            lo = i0 + kBlock / 2 - WIN / 2;
+            lo = lo < 0 ? 0 : lo;
+            nwin = NN - lo < WIN ? NN - lo : WIN;
+            const float4 *src = reinterpret_cast<const float4 *>(c) + lo * RQ;
+            for (int64_t p = threadIdx.x; p < nwin * RQL; p += kBlock)
+                shm[p] = RQL == RQ ? src[p] : src[(p / RQL) * RQ + p % RQL];
+            __syncthreads();
+        }
     } else {
         i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
         q = (int)(threadIdx.x % LANES);
@@ -710,7 +729,10 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
             for (int a = a0; a < a1; a += LANES) {
                 const int64_t v = LANES == 1 ? stage[a - a0][threadIdx.x] : ld_s<NT>(&act_n[b0 + kSlab * a]);
                 BasisHP<K, L, float, 0, K, CHAIN, CT> b;
-                const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+                const int64_t wv = v - lo;
+                const float *rv = (WIN > 0 && wv >= 0 && wv < nwin)
+                                      ? reinterpret_cast<const float *>(shm + wv * RQL)   // staged record
+                                      : c + v * rec_stride(K);   // node record: position, then messages
                 const double *pv = reinterpret_cast<const double *>(rv);
                 const double px = pv[0], py = pv[1], pz = pv[2];
                 float cr[K];
@@ -726,10 +748,10 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t np, const 
         }
     }
     if constexpr (LANES == 1) {
-        __shared__ float4 lds[5 * kBlock];
+        if constexpr (WIN > 0) __syncthreads();   // every thread is done with the window
         // rows n..np-1 of the last block are padding: written, never read
-        store_o_rows<K, L>(acc, lds, O + i0 * 16, np, (int)(i - i0), std::make_integer_sequence<int, KMT>{});
-        store_feature_rows<K, L>(acc, inv_scale, lds, feat + i0 * 16, np, (int)(i - i0),
+        store_o_rows<K, L>(acc, shm, O + i0 * 16, np, (int)(i - i0), std::make_integer_sequence<int, KMT>{});
+        store_feature_rows<K, L>(acc, inv_scale, shm, feat + i0 * 16, np, (int)(i - i0),
                                  std::make_integer_sequence<int, DT>{});
     } else {
 #pragma unroll
@@ -883,8 +905,9 @@ __device__ __forceinline__ void store_gedge(float *__restrict__ ge, const float 
 }
 
 // C0U: layer 0 of a one-species model (see k_aggregate): the messages come from the model constants.
-template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES, bool C0U = false>
-__global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, const double *__restrict__ pos,
+// WIN > 0: a window of node records staged in LDS per block, as in k_aggregate.
+template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES, bool C0U = false, int WIN = 0>
+__global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, int64_t np, const double *__restrict__ pos,
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ nact,
                                                         const int32_t *__restrict__ act_n, const float *__restrict__ c,
@@ -894,11 +917,25 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
                                                         float *__restrict__ w, float *__restrict__ gedge,
                                                         double *__restrict__ Frecv) {
     static_assert(LANES == 1 || LANES == kGatherLanes, "one lane or one lane group per row");
+    static_assert(WIN == 0 || LANES == 1, "record window with one row per lane only");
     constexpr int M = n_mono(L);
-    int64_t i;
+    constexpr int RQ = rec_stride(K) / 4, RQL = C0U ? 2 : RQ;
+    __shared__ float4 shm[WIN > 0 ? WIN * RQL : 1];
+    int64_t i, lo = 0, nwin = 0;
     int q = 0;
     if constexpr (LANES == 1) {
-        i = block_row(xcd_block() * blockDim.x, n, row_perm);
+        const int64_t i0 = xcd_block() * blockDim.x;
+        if (i0 >= n) return;   // whole block past the end
+        if constexpr (WIN > 0) {
+            lo = i0 + kBlock / 2 - WIN / 2;
+            lo = lo < 0 ? 0 : lo;
+            nwin = NN - lo < WIN ? NN - lo : WIN;
+            const float4 *src = reinterpret_cast<const float4 *>(c) + lo * RQ;
+            for (int64_t p = threadIdx.x; p < nwin * RQL; p += kBlock)
+                shm[p] = RQL == RQ ? src[p] : src[(p / RQL) * RQ + p % RQL];
+            __syncthreads();
+        }
+        i = block_row(i0, n, row_perm);
         if (i >= n) return;
     } else {   // lane group per row (small systems); the group's force partials meet below
         i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / LANES;
@@ -924,7 +961,10 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t np, c
     for (int a = q; a < na; a += LANES) {
         const int64_t e = b0 + kSlab * a;   // active slot: per-edge outputs are stored here
         const int64_t v = ld_s<NT>(&act_n[e]);
-        const float *rv = c + v * rec_stride(K);   // node record: position, then messages
+        const int64_t wv = v - lo;
+        const float *rv = (WIN > 0 && wv >= 0 && wv < nwin)
+                              ? reinterpret_cast<const float *>(shm + wv * RQL)   // staged record
+                              : c + v * rec_stride(K);   // node record: position, then messages
         const double *pv = reinterpret_cast<const double *>(rv);
         Basis<K, L, CT> b;
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
@@ -1239,14 +1279,14 @@ Status aggregate(Context &cx, int t) {
     const bool c0u = t == 0 && cx.S == 1 && !cx.contracted;
     if (cx.precision != 1) {   // fp32 orbital sums (fp32 and bf16 networks)
 #define MPNN_AGG32_NT(CH, CT, NT, U)                                                                            \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT, 1, U><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
-                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, NT, 1, U, NT ? (U ? 2 * kRecWin : kRecWin) : 0><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+                                      cx.n, cx.NN, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),          \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], row_perm(cx), Ot, Ft)))
 #define MPNN_AGG32_LG(CH, CT, U)                                                                                \
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_aggregate<KK, LL, CH, CT, false, kGatherLanes, U><<<grid_for(cx.n * kGatherLanes), \
                                                                                    kBlock, 0, cx.stream>>>(      \
-                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),                 \
+                                      cx.n, cx.NN, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(),          \
                                       cx.nact.as<int32_t>(), cx.act_n.as<int32_t>(), ct, cx.model.as<ModelDev>(), \
                                       cx.inv_scale_host[t], nullptr, Ot, Ft)))
 #define MPNN_AGG32(CH, CT)                                                                                      \
@@ -1344,13 +1384,13 @@ Status backward_layer(Context &cx, int t) {
 #define MPNN_BWD_LG(FIRST_, W_, CT_, U_)                                                                   \
     MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, false, kGatherLanes, U_>       \
                                   <<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(                 \
-                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
+                                      cx.n, cx.NN, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), nullptr, cx.w.as<float>(), cx.gedge.as<float>(), \
                                       cx.Frecv.as<double>())))
 #define MPNN_BWD_NT(FIRST_, W_, CT_, NT_, U_)                                                              \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1, U_><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
-                                      cx.n, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1, U_, NT_ && !U_ ? kRecWin : 0><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+                                      cx.n, cx.NN, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
                                       cx.Frecv.as<double>())))
