@@ -517,13 +517,15 @@ __device__ __forceinline__ int64_t block_row(int64_t i0, int64_t n, const int32_
     return (row_perm && i < n) ? (int64_t)row_perm[i] : i;
 }
 
-// Compaction of row i (see k_compact below); returns its active count.
+// Compaction of row i (see k_compact below); returns its active count.  win: the fp32 positions of
+// nodes wlo .. wlo + nwin - 1 staged in LDS (nwin = 0: none).
 template <bool NT>
 __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *__restrict__ pos,
                                            const float4 *__restrict__ pos32, const int64_t *__restrict__ slab_off,
                                            const int32_t *__restrict__ len, const int32_t *__restrict__ nbr,
                                            double rc2, float lo, float hi, uint32_t *__restrict__ amask,
-                                           int32_t *__restrict__ act_n, int32_t (*stage)[kBlock]) {
+                                           int32_t *__restrict__ act_n, int32_t (*stage)[kBlock],
+                                           const float4 *win, int64_t wlo, int64_t nwin) {
     const float4 pi = pos32[i];
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
@@ -541,7 +543,10 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = j0 + u < nl ? stage[j0 % kIdxStage + u][threadIdx.x] : (int32_t)i;
 #pragma unroll
-        for (int u = 0; u < U; ++u) pv[u] = pos32[v[u]];
+        for (int u = 0; u < U; ++u) {
+            const int64_t wv = v[u] - wlo;
+            pv[u] = (wv >= 0 && wv < nwin) ? win[wv] : pos32[v[u]];
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int j = j0 + u;
@@ -570,7 +575,7 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
 }
 
 template <bool NT>
-__global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__restrict__ pos,
+__global__ __launch_bounds__(256) void k_compact(int64_t n, int64_t NN, const double *__restrict__ pos,
                                                  const float4 *__restrict__ pos32,
                                                  const int64_t *__restrict__ slab_off,
                                                  const int32_t *__restrict__ len,
@@ -579,7 +584,17 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, const double *__rest
                                                  int32_t *__restrict__ nact, int32_t *__restrict__ row_perm) {
     const int64_t i0 = xcd_block() * blockDim.x, i = i0 + threadIdx.x;
     __shared__ int32_t stage[kIdxStage][kBlock];
-    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n, stage) : -1;
+    // the fp32 positions of a node window around the block's rows (see k_aggregate)
+    constexpr int WIN = 2 * kRecWin;
+    __shared__ float4 win[WIN];
+    int64_t wlo = i0 + kBlock / 2 - WIN / 2;
+    wlo = wlo < 0 ? 0 : wlo;
+    const int64_t nwin = NN - wlo < WIN ? (NN - wlo > 0 ? NN - wlo : 0) : WIN;
+    for (int64_t p = threadIdx.x; p < nwin; p += kBlock) win[p] = pos32[wlo + p];
+    __syncthreads();
+    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n, stage,
+                                           win, wlo, nwin)
+                         : -1;
     if (i < n) nact[i] = na;
     if (row_perm) {
         // the block's rows by descending active count (ties by row), so the waves of the row
@@ -1255,7 +1270,7 @@ Status compact_active(Context &cx) {
     const float lo = (float)(rc2 - band), hi = (float)(rc2 + band);
     auto launch = [&](auto nt) {
         k_compact<decltype(nt)::value><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
-            cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(), cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
+            cx.n, cx.NN, cx.pos.as<double>(), cx.pos32.as<float4>(), cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
             cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(), cx.nact.as<int32_t>(),
             cx.bucket ? cx.row_perm.as<int32_t>() : nullptr);
     };
