@@ -905,20 +905,6 @@ __device__ __forceinline__ void edge_vjp(const B &b, const float *cv, const floa
     g[2] = fmaf(sd, b.rz, ga[2] * ir);
 }
 
-// dE/dr_e accumulated over layers: written by the first reverse layer, read-modified-written after.
-template <bool FIRST, bool NT>
-__device__ __forceinline__ void store_gedge(float *__restrict__ ge, const float (&g)[3]) {
-    if (FIRST) {
-        st_s<NT>(g[0], &ge[0]);
-        st_s<NT>(g[1], &ge[1]);
-        st_s<NT>(g[2], &ge[2]);
-    } else {
-        st_s<NT>(ld_s<NT>(&ge[0]) + g[0], &ge[0]);
-        st_s<NT>(ld_s<NT>(&ge[1]) + g[1], &ge[1]);
-        st_s<NT>(ld_s<NT>(&ge[2]) + g[2], &ge[2]);
-    }
-}
-
 // C0U: layer 0 of a one-species model (see k_aggregate): the messages come from the model constants.
 // WIN > 0: a window of node records staged in LDS per block, as in k_aggregate.
 template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES, bool C0U = false, int WIN = 0>
@@ -976,6 +962,13 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
     for (int a = q; a < na; a += LANES) {
         const int64_t e = b0 + kSlab * a;   // active slot: per-edge outputs are stored here
         const int64_t v = ld_s<NT>(&act_n[e]);
+        // dE/dr_e accumulates over layers (written by the first reverse layer, added to after); the
+        // earlier layers' value is requested before the edge's arithmetic
+        float gp[3] = {0.0f, 0.0f, 0.0f};
+        if constexpr (!FIRST) {
+#pragma unroll
+            for (int d = 0; d < 3; ++d) gp[d] = ld_s<NT>(&gedge[3 * e + d]);
+        }
         const int64_t wv = v - lo;
         const float *rv = (WIN > 0 && wv >= 0 && wv < nwin)
                               ? reinterpret_cast<const float *>(shm + wv * RQL)   // staged record
@@ -985,7 +978,8 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
         b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
         float g[3];
         edge_vjp<K, L, WANT_W, NT>(b, C0U ? c0u : rv + kRecC, G, ir, w + e * K, g);
-        store_gedge<FIRST, NT>(gedge + 3 * e, g);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) st_s<NT>(gp[d] + g[d], &gedge[3 * e + d]);
         F[0] += (double)g[0];
         F[1] += (double)g[1];
         F[2] += (double)g[2];
