@@ -979,7 +979,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
         float g[3];
         edge_vjp<K, L, WANT_W, NT>(b, C0U ? c0u : rv + kRecC, G, ir, w + e * K, g);
 #pragma unroll
-        for (int d = 0; d < 3; ++d) st_s<NT>(gp[d] + g[d], &gedge[3 * e + d]);
+        for (int d = 0; d < 3; ++d) st_s<NT>(FIRST ? g[d] : gp[d] + g[d], &gedge[3 * e + d]);
         F[0] += (double)g[0];
         F[1] += (double)g[1];
         F[2] += (double)g[2];
@@ -1033,6 +1033,12 @@ __global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np
     for (int a = 0; a < na; ++a) {
         const int64_t e = b0 + kSlab * a;
         const int64_t v = ld_s<NT>(&act_n[e]);
+        // the earlier layers' dE/dr_e (lane h = 0 accumulates), requested before the arithmetic
+        float gp[3] = {0.0f, 0.0f, 0.0f};
+        if (!FIRST && h == 0) {
+#pragma unroll
+            for (int d = 0; d < 3; ++d) gp[d] = ld_s<NT>(&gedge[3 * e + d]);
+        }
         const float *rv = c + v * rec_stride(K);
         const double *pv = reinterpret_cast<const double *>(rv);
         BasisHalf<K, L> b;
@@ -1064,16 +1070,8 @@ __global__ __launch_bounds__(256, 2) void k_backward_split(int64_t n, int64_t np
 #pragma unroll
         for (int q = 0; q < 3; ++q) g[q] += __shfl_xor(g[q], 1);   // the other channel half
         if (h == 0) {
-            float *ge = gedge + 3 * e;
-            if (FIRST) {
-                st_s<NT>(g[0], &ge[0]);
-                st_s<NT>(g[1], &ge[1]);
-                st_s<NT>(g[2], &ge[2]);
-            } else {
-                st_s<NT>(ld_s<NT>(&ge[0]) + g[0], &ge[0]);
-                st_s<NT>(ld_s<NT>(&ge[1]) + g[1], &ge[1]);
-                st_s<NT>(ld_s<NT>(&ge[2]) + g[2], &ge[2]);
-            }
+#pragma unroll
+            for (int d = 0; d < 3; ++d) st_s<NT>(FIRST ? g[d] : gp[d] + g[d], &gedge[3 * e + d]);
         }
         F[0] += (double)g[0];
         F[1] += (double)g[1];
