@@ -22,6 +22,9 @@ CASES = {
     "HEA432_K12L3": (3, lambda: systems.hea(6), 0, 1e-4),
     "CHON4002_K12L3_fp64": (5, lambda: I.make_system(5, reduced=True), 1, 1e-4),
     "Ag108_bf16": (1, lambda: I.make_system(1), 2, 2e-3),
+    # 500,000 atoms: per-edge streams of 1.7 GB, so the row kernels take their streaming path (with
+    # the staged record windows), which the smaller cases do not reach
+    "Ag500000_cfg4model": (4, lambda: systems.ag(50, seed=5), 0, 1e-4),
 }
 
 
