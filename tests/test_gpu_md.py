@@ -90,6 +90,8 @@ def test_nve_energy_conservation():
     (1, lambda: I.make_system(1), 12, 0, None),                 # no rebuild: whole chunks
     (3, lambda: systems.hea(8), 13, 5, None),                   # chunks end before scheduled rebuilds
     (1, lambda: I.make_system(1), 12, 0, 0.02),                 # displacement rebuilds: chunks roll back
+    (4, lambda: systems.ag(24, seed=3), 10, 0, None),           # 4.4M list entries: the transposed map
+                                                                # is built on the second stream
 ])
 def test_graph_replay_matches_eager(cfg, make, steps, rebuild, skin):
     """MD replayed in captured chunks gives the same state, bit for bit, as eager steps; each run
