@@ -139,7 +139,10 @@ mpnn_status mpnn_create(const mpnn_params *p, mpnn_ctx **out);
 void mpnn_destroy(mpnn_ctx *ctx);
 
 /* Stream for every later call (a hipStream_t, e.g. torch.cuda.current_stream().cuda_stream);
- * NULL selects the null stream. */
+ * NULL selects the null stream.  On long neighbour lists (4M entries or more) an evaluation also
+ * runs one kernel on a second, library-owned stream of default priority, forked from and joined
+ * back to this stream with events inside the same call, so work ordered on this stream before
+ * and after a call stays ordered with all of it (also under graph capture). */
 mpnn_status mpnn_set_stream(mpnn_ctx *ctx, void *hip_stream);
 
 /* Device memory source for the buffers allocated from now on: alloc(bytes, user) returns device
@@ -229,7 +232,8 @@ mpnn_status mpnn_get_info(mpnn_ctx *ctx, mpnn_info *info);
 
 /* Event profiler: enable != 0 resets the counters and records a hipEvent pair on the context's
  * stream around every kernel family launched afterwards; 0 stops recording.  Durations are
- * collected at the library's own synchronisation points. */
+ * collected at the library's own synchronisation points.  The kernel on the second stream (see
+ * mpnn_set_stream) is not among the families. */
 mpnn_status mpnn_set_profiling(mpnn_ctx *ctx, int32_t enable);
 
 /* Accumulated device time and launch count of kernel family idx (0 <= idx < number of families;
