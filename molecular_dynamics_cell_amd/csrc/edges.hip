@@ -314,6 +314,22 @@ __device__ __forceinline__ void feature_tile(const float (&O)[K][n_mono(L)], SC 
 constexpr int kGatherLanes = 16;
 constexpr int kRecWin = 512;   // nodes per staged record window of the row kernels
 
+// A node record (position, then K messages when WANT_C) from src, an LDS window slot or the record
+// array; the row kernels call it on two separate paths so that each compiles to loads of its own
+// memory space (one pointer into either space would make generic loads, which are slower for both).
+template <int K, bool WANT_C, class P>
+__device__ __forceinline__ void read_record(const P *src, double &px, double &py, double &pz, float (&cr)[K]) {
+    const double2 xy = reinterpret_cast<const double2 *>(src)[0];
+    px = xy.x;
+    py = xy.y;
+    pz = reinterpret_cast<const double *>(src)[2];
+    if constexpr (WANT_C) {
+        const float *cv = reinterpret_cast<const float *>(src) + kRecC;
+#pragma unroll
+        for (int k = 0; k < K; ++k) cr[k] = cv[k];
+    }
+}
+
 template <class T>
 __device__ __forceinline__ T group_sum16(T x) {
 #pragma unroll
@@ -544,8 +560,10 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
         for (int u = 0; u < U; ++u) v[u] = j0 + u < nl ? stage[j0 % kIdxStage + u][threadIdx.x] : (int32_t)i;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            // two paths, so each load is of its own memory space (see read_record)
             const int64_t wv = v[u] - wlo;
-            pv[u] = (wv >= 0 && wv < nwin) ? win[wv] : pos32[v[u]];
+            if (wv >= 0 && wv < nwin) pv[u] = win[wv];
+            else pv[u] = pos32[v[u]];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -745,14 +763,16 @@ __global__ __launch_bounds__(256) void k_aggregate(int64_t n, int64_t NN, int64_
                 const int64_t v = LANES == 1 ? stage[a - a0][threadIdx.x] : ld_s<NT>(&act_n[b0 + kSlab * a]);
                 BasisHP<K, L, float, 0, K, CHAIN, CT> b;
                 const int64_t wv = v - lo;
-                const float *rv = (WIN > 0 && wv >= 0 && wv < nwin)
-                                      ? reinterpret_cast<const float *>(shm + wv * RQL)   // staged record
-                                      : c + v * rec_stride(K);   // node record: position, then messages
-                const double *pv = reinterpret_cast<const double *>(rv);
-                const double px = pv[0], py = pv[1], pz = pv[2];
+                double px, py, pz;
                 float cr[K];
+                if (WIN > 0 && wv >= 0 && wv < nwin)
+                    read_record<K, !C0U>(shm + wv * RQL, px, py, pz, cr);   // staged record
+                else
+                    read_record<K, !C0U>(c + v * rec_stride(K), px, py, pz, cr);   // the record array
+                if constexpr (C0U) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) cr[k] = C0U ? c0u[k] : rv[kRecC + k];
+                    for (int k = 0; k < K; ++k) cr[k] = c0u[k];
+                }
                 __builtin_amdgcn_sched_barrier(0);   // the whole record is requested before the basis starts
                 b.eval(px - xi, py - yi, pz - zi, cr, md);
 #pragma unroll
@@ -970,14 +990,20 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
             for (int d = 0; d < 3; ++d) gp[d] = ld_s<NT>(&gedge[3 * e + d]);
         }
         const int64_t wv = v - lo;
-        const float *rv = (WIN > 0 && wv >= 0 && wv < nwin)
-                              ? reinterpret_cast<const float *>(shm + wv * RQL)   // staged record
-                              : c + v * rec_stride(K);   // node record: position, then messages
-        const double *pv = reinterpret_cast<const double *>(rv);
+        double px, py, pz;
+        float cv[K];
+        if (WIN > 0 && wv >= 0 && wv < nwin)
+            read_record<K, !C0U>(shm + wv * RQL, px, py, pz, cv);   // staged record
+        else
+            read_record<K, !C0U>(c + v * rec_stride(K), px, py, pz, cv);   // the record array
+        if constexpr (C0U) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) cv[k] = c0u[k];
+        }
         Basis<K, L, CT> b;
-        b.eval(__dsub_rn(pv[0], xi), __dsub_rn(pv[1], yi), __dsub_rn(pv[2], zi), md, mu);
+        b.eval(__dsub_rn(px, xi), __dsub_rn(py, yi), __dsub_rn(pz, zi), md, mu);
         float g[3];
-        edge_vjp<K, L, WANT_W, NT>(b, C0U ? c0u : rv + kRecC, G, ir, w + e * K, g);
+        edge_vjp<K, L, WANT_W, NT>(b, cv, G, ir, w + e * K, g);
 #pragma unroll
         for (int d = 0; d < 3; ++d) st_s<NT>(FIRST ? g[d] : gp[d] + g[d], &gedge[3 * e + d]);
         F[0] += (double)g[0];
