@@ -1422,7 +1422,7 @@ Status backward_layer(Context &cx, int t) {
                                       cx.model.as<ModelDev>(), nullptr, cx.w.as<float>(), cx.gedge.as<float>(), \
                                       cx.Frecv.as<double>())))
 #define MPNN_BWD_NT(FIRST_, W_, CT_, NT_, U_)                                                              \
-    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1, U_, NT_ && !U_ ? kRecWin : 0><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
+    MPNN_DISPATCH_KL(cx.K, cx.L, (k_backward_layer<KK, LL, FIRST_, W_, CT_, NT_, 1, U_, NT_ ? (U_ ? 2 * kRecWin : 3 * kRecWin / 2) : 0><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>( \
                                       cx.n, cx.NN, cx.np, cx.pos.as<double>(), cx.slab_off.as<int64_t>(), cx.nact.as<int32_t>(), \
                                       cx.act_n.as<int32_t>(), ct, Gt, Ot,                                          \
                                       cx.model.as<ModelDev>(), row_perm(cx), cx.w.as<float>(), cx.gedge.as<float>(), \
