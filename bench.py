@@ -94,9 +94,9 @@ def kernel_model(fam, g):
         f = EA * (4 * KM + 6 * K + 6 * M)
         return b, f, "alu"
     if fam == "message_grad":
-        build = 4 * EL + 4 * EL + EL / 8 + 4 * EL  # transposed ids and receivers, activity bits, t_act out
-        rest = 4 * EL                              # t_act in
-        b = 8 * NN + (build + (T - 2) * rest) / max(T - 1, 1) + 4 * K * EA + 4 * K * NN
+        # segment offsets (per node), the transposed active map (per Verlet entry; built once per
+        # evaluation by its own kernel), w_e (per active edge), dE/dc rows out (per node)
+        b = 8 * NN + 4 * EL + 4 * K * EA + 4 * K * NN
         return b, K * EA, "hbm"
     if fam == "force_gather":
         b = 8 * NN + 4 * EL + 12 * EA + 8 * N + 24 * N + 48 * N
