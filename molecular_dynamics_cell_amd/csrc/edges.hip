@@ -520,8 +520,9 @@ __device__ __forceinline__ void stage_indices(int32_t (*stage)[kBlock], const in
 // expression as the build), compacted in row order into the row's leading slots (sender node of
 // active entry a at slot base + 64 a), plus one activity bit per Verlet entry (word j/32, bit j%32
 // of the row's mask).  Per-edge outputs live in active slots, so the row kernels write them
-// coalesced; a sender-major gather finds the active slot of an entry by counting the set bits
-// before it (the masks are 32x smaller than a per-entry slot map and stay in cache).  The test
+// coalesced; the transposed active map (k_transpose_active, once per evaluation) finds the active
+// slot of an entry by counting the set bits before it (the masks are 32x smaller than a per-entry
+// slot map and stay in cache).  The test
 // first uses the fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of
 // the fp64 value (a bound from the coordinate range, see compact_active), so only entries inside
 // rc^2 -/+ band, a vanishing fraction, repeat it in fp64.
