@@ -45,6 +45,19 @@ __device__ __forceinline__ float sigmoid(float z) {
 // fp32 sum runs over more than 16 products (long fp32 chains lose several 1e-7 relative on
 // these products).
 template <int RT, int CT>
+__device__ __forceinline__ void gemm_chunk(const float4 &w, const float (&x)[CT][4], double (&acc)[CT][4]) {
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+        floatx4 t = mfma4(w.x, x[c][0], floatx4{0.f, 0.f, 0.f, 0.f});
+        t = mfma4(w.y, x[c][1], t);
+        t = mfma4(w.z, x[c][2], t);
+        t = mfma4(w.w, x[c][3], t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] += (double)t[i];
+    }
+}
+
+template <int RT, int CT>
 __device__ __forceinline__ void gemm_step(const float4 *__restrict__ W, int KT, int kt, const float (&x)[CT][4],
                                           double (&acc)[RT][CT][4], int lane) {
     // 128-wide networks: one scheduling region per chunk column, which keeps the compiler from
@@ -52,18 +65,7 @@ __device__ __forceinline__ void gemm_step(const float4 *__restrict__ W, int KT, 
     // ones may prefetch the next column's weights
     if constexpr (RT >= 8) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const float4 w = W[(rt * KT + kt) * 64 + lane];
-#pragma unroll
-        for (int c = 0; c < CT; ++c) {
-            floatx4 t = mfma4(w.x, x[c][0], floatx4{0.f, 0.f, 0.f, 0.f});
-            t = mfma4(w.y, x[c][1], t);
-            t = mfma4(w.z, x[c][2], t);
-            t = mfma4(w.w, x[c][3], t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rt][c][i] += (double)t[i];
-        }
-    }
+    for (int rt = 0; rt < RT; ++rt) gemm_chunk<RT, CT>(W[(rt * KT + kt) * 64 + lane], x, acc[rt]);
 }
 
 // accumulators start from the bias of their output row (row 16 rt + 4 grp + i)
@@ -144,16 +146,52 @@ __global__ __launch_bounds__(64, 2) void k_net(const NetArgs a) {
     init_bias(z1, b1, grp);
     {
         const float4 *W1 = reinterpret_cast<const float4 *>(W + a.oW1);
-#pragma unroll 1
-        for (int kt = 0; kt < DT; ++kt) {
-            float x[CT][4];
+        auto load_x = [&](int kt, float (&x)[CT][4]) {
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
                 float4 f = float4{0.f, 0.f, 0.f, 0.f};
                 if (me[c] >= 0) f = *reinterpret_cast<const float4 *>(a.F + tiled(a.np, me[c], 16 * kt + 4 * grp));
                 x[c][0] = f.x; x[c][1] = f.y; x[c][2] = f.z; x[c][3] = f.w;
             }
-            gemm_step<HT, CT>(W1, DT, kt, x, z1, lane);
+        };
+        if constexpr (HT < 8) {
+            // 64-wide networks on one atom tile: the next column's features (from HBM) are
+            // requested after this column's weights (from L2), so the products wait for the
+            // weights only (with two tiles the registers would cost a wave per SIMD).  The loads
+            // are unconditional (padding lanes read row 0 and drop it, the last step re-reads its
+            // own column), so the wait counts stay exact
+            auto load_all = [&](int kt, float (&x)[CT][4]) {
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    const int64_t r = me[c] >= 0 ? me[c] : 0;
+                    float4 f = *reinterpret_cast<const float4 *>(a.F + tiled(a.np, r, 16 * kt + 4 * grp));
+                    if (me[c] < 0) f = float4{0.f, 0.f, 0.f, 0.f};
+                    x[c][0] = f.x; x[c][1] = f.y; x[c][2] = f.z; x[c][3] = f.w;
+                }
+            };
+            float x[CT][4];
+            load_all(0, x);
+#pragma unroll 1
+            for (int kt = 0; kt < DT; ++kt) {
+                float4 w[HT];
+#pragma unroll
+                for (int rt = 0; rt < HT; ++rt) w[rt] = W1[(rt * DT + kt) * 64 + lane];
+                float xn[CT][4];
+                load_all(kt + 1 < DT ? kt + 1 : kt, xn);
+#pragma unroll
+                for (int rt = 0; rt < HT; ++rt) gemm_chunk<HT, CT>(w[rt], x, z1[rt]);
+#pragma unroll
+                for (int c = 0; c < CT; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[c][i] = xn[c][i];
+            }
+        } else {
+#pragma unroll 1
+            for (int kt = 0; kt < DT; ++kt) {
+                float x[CT][4];
+                load_x(kt, x);
+                gemm_step<HT, CT>(W1, DT, kt, x, z1, lane);
+            }
         }
     }
     // H1 = silu(Z1); the backward pass keeps only silu'(Z1) = s (1 + z (1 - s))
