@@ -681,20 +681,6 @@ __global__ __launch_bounds__(256) void k_compact_groups(int64_t n, const double 
     if (q == 0) nact[i] = o;
 }
 
-// Active slot of Verlet slot e of receiver row i this step (-1: d >= rc): the row's slab base
-// plus 64 times the number of active entries before entry j = (e - base) / 64.
-__device__ __forceinline__ int32_t active_slot(int64_t i, int32_t e, const int64_t *__restrict__ slab_off,
-                                               const uint32_t *__restrict__ amask, int64_t n) {
-    const int64_t b = sell_base(slab_off, i);
-    const int j = (int)((e - b) / kSlab);
-    const int w = j >> 5, bit = j & 31;
-    const uint32_t word = amask[(int64_t)w * n + i];
-    if (!((word >> bit) & 1u)) return -1;
-    int a = __popc(word & ((1u << bit) - 1u));
-    for (int q = 0; q < w; ++q) a += __popc(amask[(int64_t)q * n + i]);
-    return (int32_t)(b + (int64_t)kSlab * a);
-}
-
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
 // atom's density features from it; both leave through LDS-staged, column-tiled stores.
 // LANES = 1: one row per lane, 256-row blocks (row bucketing applies) with LDS-staged tile stores;
@@ -1158,18 +1144,56 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
         for (int k = 0; k < K; ++k) Gc[v * K + k] = acc[k];
 }
 
-// t_act: the active slot (or -1) of every transposed entry under this step's compaction; the
-// entry's receiver row follows from its slot (the slab of its 64-slot run, and the slot mod 64).
-__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, const int32_t *__restrict__ t_eid,
+// t_act: the active slot (or -1) of every transposed entry under this step's compaction.  Each
+// entry holds its receiver row and column, packed as (row << jb) | column (jb > 0), or its slot,
+// whose row follows from the slab of its 64-slot run (jb = 0).  Each thread takes kTPer entries a
+// block apart and requests all their lookups (row base, activity words) before using any, so the
+// build keeps few waves busy while it runs beside the forward layers.
+constexpr int kTPer = 4;
+__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, int jb,
+                                                          const uint32_t *__restrict__ t_ent,
                                                           const int32_t *__restrict__ blk_slab,
                                                           const int64_t *__restrict__ slab_off,
                                                           const uint32_t *__restrict__ amask,
                                                           int32_t *__restrict__ t_act) {
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= E) return;
-    const int32_t e = t_eid[s];
-    const int64_t r = (int64_t)blk_slab[e / kSlab] * kSlab + e % kSlab;
-    t_act[s] = active_slot(r, e, slab_off, amask, n);
+    const int64_t s0 = (int64_t)blockIdx.x * (kBlock * kTPer) + threadIdx.x;
+    uint32_t ent[kTPer];
+#pragma unroll
+    for (int p = 0; p < kTPer; ++p) {
+        const int64_t s = s0 + (int64_t)p * kBlock;
+        ent[p] = s < E ? t_ent[s] : 0u;   // past the end: row 0, column 0, not stored
+    }
+    int64_t r[kTPer], b[kTPer];
+    int j[kTPer];
+#pragma unroll
+    for (int p = 0; p < kTPer; ++p) {
+        if (jb > 0) {
+            r[p] = ent[p] >> jb;
+            j[p] = (int)(ent[p] & ((1u << jb) - 1u));
+            b[p] = sell_base(slab_off, r[p]);
+        } else {
+            const int64_t e = ent[p];
+            r[p] = (int64_t)blk_slab[e / kSlab] * kSlab + e % kSlab;
+            b[p] = sell_base(slab_off, r[p]);
+            j[p] = (int)((e - b[p]) / kSlab);
+        }
+    }
+    uint32_t word[kTPer];
+#pragma unroll
+    for (int p = 0; p < kTPer; ++p) word[p] = amask[(int64_t)(j[p] >> 5) * n + r[p]];
+#pragma unroll
+    for (int p = 0; p < kTPer; ++p) {
+        const int64_t s = s0 + (int64_t)p * kBlock;
+        if (s >= E) continue;
+        const int bit = j[p] & 31;
+        int32_t slot = -1;
+        if ((word[p] >> bit) & 1u) {
+            int a = __popc(word[p] & ((1u << bit) - 1u));
+            for (int q = 0; q < (j[p] >> 5); ++q) a += __popc(amask[(int64_t)q * n + r[p]]);
+            slot = (int32_t)(b[p] + (int64_t)kSlab * a);
+        }
+        t_act[s] = slot;
+    }
 }
 
 // Ghost -> owner sum of dE/dc (the reverse ghost exchange), ghosts of an owner in order.
@@ -1460,9 +1484,9 @@ Status fork_transpose(Context &cx) {
         s = cx.side_stream;
     }
     if (cx.E > 0) {
-        k_transpose_active<<<grid_for(cx.E), kBlock, 0, s>>>(cx.E, cx.n, cx.t_eid.as<int32_t>(),
-                                                           cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
-                                                           cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
+        k_transpose_active<<<grid_for((cx.E + kTPer - 1) / kTPer), kBlock, 0, s>>>(
+            cx.E, cx.n, cx.tjb, cx.t_eid.as<uint32_t>(), cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
+            cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }
     if (cx.side) MPNN_HIP(hipEventRecord(cx.side_ev[1], cx.side_stream));

@@ -84,6 +84,7 @@ struct Context {
     int64_t n = 0, G = 0, NN = 0, E = 0, E_sell = 0;
     int64_t np = 0;             // n rounded up to whole 256-row blocks (column-tiled vectors)
     int mw = 1;                 // activity-mask words per row (longest row / 32, rounded up)
+    int tjb = 0;                // transposed entries hold (row << tjb | column) when > 0, else the slot
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
     int sub[3] = {1, 1, 1};     // virtual subdomains per axis (the next build applies them)

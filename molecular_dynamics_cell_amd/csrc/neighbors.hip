@@ -346,8 +346,11 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
 
 // Sort keys of the sender-major transpose: for every neighbour slot (the slab layout, padding slots
 // included) the sender node, or NN for a padding slot past its row's length; values = the slot.
+// Sort keys and values of every slab slot: key = the sender (NN for padding), value = the slot
+// itself, or, when jb > 0, the receiver row and the slot's column packed as (row << jb) | column, so
+// that the per-step map build (k_transpose_active) reads the row without a lookup.
 __global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
-                        const int32_t *__restrict__ nbr, uint32_t NN, uint32_t *__restrict__ keys,
+                        const int32_t *__restrict__ nbr, uint32_t NN, int jb, uint32_t *__restrict__ keys,
                         uint32_t *__restrict__ vals) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (slab, lane)
     if (q >= nslab * kSlab) return;
@@ -357,7 +360,7 @@ __global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ sl
     for (int64_t j = 0; j < w; ++j) {
         const int64_t e = b + kSlab * j;
         keys[e] = j < nl ? (uint32_t)nbr[e] : NN;
-        vals[e] = (uint32_t)e;
+        vals[e] = jb > 0 ? ((uint32_t)i << jb) | (uint32_t)j : (uint32_t)e;
     }
 }
 
@@ -635,6 +638,11 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
             slots += w;
         }
         cx.mw = (int)std::max<int64_t>(1, (longest + 31) / 32);
+        // transposed entries as (row, column) in 32 bits when both fit (2.05M rows of at most
+        // 128 columns: 21 + 7 bits)
+        int jb = 1;
+        while (((int64_t)1 << jb) < longest) ++jb;
+        cx.tjb = n <= ((int64_t)1 << (32 - jb)) ? jb : 0;
         // ragged rows (slabs less than 85 % full, e.g. a gas with clusters): the row kernels take
         // each block's rows by descending active count, so a wave's rows have similar lengths.  The
         // reordering scatters the rows' per-edge stores and spreads a wave over four slabs, so it
@@ -679,7 +687,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         if (Es > 0) {
             k_tkeys<<<grid_for(nslab_all * kSlab), kBlock, 0, cx.stream>>>(
                 nslab_all, n, cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(), cx.nbr.as<int32_t>(),
-                (uint32_t)cx.NN, keys, vals);
+                (uint32_t)cx.NN, cx.tjb, keys, vals);
             MPNN_HIP(hipGetLastError());
             int bits = 1;
             while (bits < 32 && ((int64_t)1 << bits) <= cx.NN) ++bits;
@@ -697,7 +705,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     }
     {
         const int64_t nslab_all = (n + kSlab - 1) / kSlab;
-        if (nslab_all > 0) {
+        if (nslab_all > 0 && cx.tjb == 0) {   // slot -> slab of its run, for unpacked entries
             k_blk_slab<<<grid_for(nslab_all), kBlock, 0, cx.stream>>>(nslab_all, cx.slab_off.as<int64_t>(),
                                                                       cx.blk_slab.as<int32_t>());
             MPNN_HIP(hipGetLastError());
