@@ -146,10 +146,12 @@ Status evaluate(Context &cx, double *F_caller, double *red_part = nullptr) {
     MPNN_TRY(refresh_ghost_positions(cx));
     MPNN_TRY(compact_active(cx));
     // the transposed active map depends only on the compaction: it is built on the side stream
-    // while the forward layers run, and joined before the first sender-major gather
-    MPNN_TRY(fork_transpose(cx));
+    // beside the forward layers after the first aggregation (which then runs alone: 0.04 ms per
+    // step better on the 2.05M-atom Ag subdomain than beside it), and joined before the first
+    // sender-major gather
     for (int t = 0; t < cx.T; ++t) {
         MPNN_TRY(aggregate(cx, t));
+        if (t == 0) MPNN_TRY(fork_transpose(cx));
         if (t < cx.T - 1) {
             MPNN_TRY(mlp_forward(cx, t));
             MPNN_TRY(refresh_ghost_features(cx, t + 1));

@@ -521,8 +521,9 @@ __device__ __forceinline__ void stage_indices(int32_t (*stage)[kBlock], const in
 // active entry a at slot base + 64 a), plus one activity bit per Verlet entry (word j/32, bit j%32
 // of the row's mask).  Per-edge outputs live in active slots, so the row kernels write them
 // coalesced; the transposed active map (k_transpose_active, once per evaluation) finds the active
-// slot of an entry by counting the set bits before it (the masks are 32x smaller than a per-entry
-// slot map and stay in cache).  The test
+// slot of an entry by counting the set bits before it, with the active counts of the row's first
+// words in one extra word per row (the masks are 32x smaller than a per-entry slot map and stay in
+// cache).  The test
 // first uses the fp32 positions (one 16-byte load per entry): d^2 from them is within `band` of
 // the fp64 value (a bound from the coordinate range, see compact_active), so only entries inside
 // rc^2 -/+ band, a vanishing fraction, repeat it in fp64.
@@ -540,14 +541,14 @@ template <bool NT>
 __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *__restrict__ pos,
                                            const float4 *__restrict__ pos32, const int64_t *__restrict__ slab_off,
                                            const int32_t *__restrict__ len, const int32_t *__restrict__ nbr,
-                                           double rc2, float lo, float hi, uint32_t *__restrict__ amask,
+                                           double rc2, float lo, float hi, int mw, uint32_t *__restrict__ amask,
                                            int32_t *__restrict__ act_n, int32_t (*stage)[kBlock],
                                            const float4 *win, int64_t wlo, int64_t nwin) {
     const float4 pi = pos32[i];
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
     int o = 0;
-    uint32_t bits = 0;
+    uint32_t bits = 0, pre = 0;
     // eight entries per step: their index and position loads are all in flight together (four:
     // 16 % slower; sixteen: 2.2x slower)
     constexpr int U = 8;
@@ -587,9 +588,11 @@ __device__ __forceinline__ int compact_row(int64_t i, int64_t n, const double *_
             if ((j & 31) == 31 || j == nl - 1) {
                 amask[(int64_t)(j >> 5) * n + i] = bits;
                 bits = 0;
+                if ((j >> 5) < 3) pre |= (uint32_t)o << (8 * (j >> 5));   // active entries before the next word
             }
         }
     }
+    amask[(int64_t)mw * n + i] = pre;
     return o;
 }
 
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, int64_t NN, const do
                                                  const int64_t *__restrict__ slab_off,
                                                  const int32_t *__restrict__ len,
                                                  const int32_t *__restrict__ nbr, double rc2, float lo, float hi,
-                                                 uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
+                                                 int mw, uint32_t *__restrict__ amask, int32_t *__restrict__ act_n,
                                                  int32_t *__restrict__ nact, int32_t *__restrict__ row_perm) {
     const int64_t i0 = xcd_block() * blockDim.x, i = i0 + threadIdx.x;
     __shared__ int32_t stage[kIdxStage][kBlock];
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(256) void k_compact(int64_t n, int64_t NN, const do
     const int64_t nwin = NN - wlo < WIN ? (NN - wlo > 0 ? NN - wlo : 0) : WIN;
     for (int64_t p = threadIdx.x; p < nwin; p += kBlock) win[p] = pos32[wlo + p];
     __syncthreads();
-    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, amask, act_n, stage,
+    const int na = i < n ? compact_row<NT>(i, n, pos, pos32, slab_off, len, nbr, rc2, lo, hi, mw, amask, act_n, stage,
                                            win, wlo, nwin)
                          : -1;
     if (i < n) nact[i] = na;
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(256) void k_compact_groups(int64_t n, const double 
                                                         const int64_t *__restrict__ slab_off,
                                                         const int32_t *__restrict__ len,
                                                         const int32_t *__restrict__ nbr, double rc2, float lo,
-                                                        float hi, uint32_t *__restrict__ amask,
+                                                        float hi, int mw, uint32_t *__restrict__ amask,
                                                         int32_t *__restrict__ act_n, int32_t *__restrict__ nact) {
     const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kGatherLanes;
     const int q = (int)(threadIdx.x % kGatherLanes);
@@ -650,7 +653,7 @@ __global__ __launch_bounds__(256) void k_compact_groups(int64_t n, const double 
     const int64_t b = sell_base(slab_off, i);
     const int nl = len[i];
     int o = 0;
-    uint32_t lo_bits = 0;
+    uint32_t lo_bits = 0, pre = 0;
     for (int j0 = 0; j0 < nl; j0 += kGatherLanes) {
         const int j = j0 + q;
         bool act = false;
@@ -677,8 +680,13 @@ __global__ __launch_bounds__(256) void k_compact_groups(int64_t n, const double 
         } else if (q == 0) {
             amask[(int64_t)(j0 >> 5) * n + i] = lo_bits | (bits << 16);
         }
+        // a word ends with its second half or with the row
+        if (((j0 & 31) == 16 || j0 + kGatherLanes >= nl) && (j0 >> 5) < 3) pre |= (uint32_t)o << (8 * (j0 >> 5));
     }
-    if (q == 0) nact[i] = o;
+    if (q == 0) {
+        nact[i] = o;
+        amask[(int64_t)mw * n + i] = pre;
+    }
 }
 
 // O^t_i[k,m] = sum over active neighbours v of c^t_v[k] R_k f_c A_m (Eq. 1 inner sum), and the
@@ -1146,11 +1154,14 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
 
 // t_act: the active slot (or -1) of every transposed entry under this step's compaction.  Each
 // entry holds its receiver row and column, packed as (row << jb) | column (jb > 0), or its slot,
-// whose row follows from the slab of its 64-slot run (jb = 0).  Each thread takes kTPer entries a
-// block apart and requests all their lookups (row base, activity words) before using any, so the
-// build keeps few waves busy while it runs beside the forward layers.
+// whose row follows from the slab of its 64-slot run (jb = 0).  The active slot is the row base plus
+// 64 times the active entries before the entry: the set bits below it in its activity word plus,
+// for rows of at most four words, the count of the earlier words that the compaction stores in the
+// row's extra mask word (longer rows add the earlier words' bits up).  Each thread takes kTPer
+// entries a block apart and requests all their lookups (row base, activity and count words) before
+// using any, so the build keeps few waves busy while it runs beside the forward layers.
 constexpr int kTPer = 4;
-__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, int jb,
+__global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, int jb, int mw,
                                                           const uint32_t *__restrict__ t_ent,
                                                           const int32_t *__restrict__ blk_slab,
                                                           const int64_t *__restrict__ slab_off,
@@ -1178,9 +1189,12 @@ __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, 
             j[p] = (int)((e - b[p]) / kSlab);
         }
     }
-    uint32_t word[kTPer];
+    uint32_t word[kTPer], pre[kTPer];
 #pragma unroll
-    for (int p = 0; p < kTPer; ++p) word[p] = amask[(int64_t)(j[p] >> 5) * n + r[p]];
+    for (int p = 0; p < kTPer; ++p) {
+        word[p] = amask[(int64_t)(j[p] >> 5) * n + r[p]];
+        pre[p] = mw <= 4 ? amask[(int64_t)mw * n + r[p]] : 0u;
+    }
 #pragma unroll
     for (int p = 0; p < kTPer; ++p) {
         const int64_t s = s0 + (int64_t)p * kBlock;
@@ -1189,7 +1203,13 @@ __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, 
         int32_t slot = -1;
         if ((word[p] >> bit) & 1u) {
             int a = __popc(word[p] & ((1u << bit) - 1u));
-            for (int q = 0; q < (j[p] >> 5); ++q) a += __popc(amask[(int64_t)q * n + r[p]]);
+            if (j[p] >= 32) {
+                if (mw <= 4) {
+                    a += (int)((pre[p] >> (8 * ((j[p] >> 5) - 1))) & 0xFFu);
+                } else {
+                    for (int q = 0; q < (j[p] >> 5); ++q) a += __popc(amask[(int64_t)q * n + r[p]]);
+                }
+            }
             slot = (int32_t)(b[p] + (int64_t)kSlab * a);
         }
         t_act[s] = slot;
@@ -1314,13 +1334,14 @@ Status compact_active(Context &cx) {
     auto launch = [&](auto nt) {
         k_compact<decltype(nt)::value><<<grid_xcd(cx.n), kBlock, 0, cx.stream>>>(
             cx.n, cx.NN, cx.pos.as<double>(), cx.pos32.as<float4>(), cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-            cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(), cx.nact.as<int32_t>(),
-            cx.bucket ? cx.row_perm.as<int32_t>() : nullptr);
+            cx.nbr.as<int32_t>(), rc2, lo, hi, cx.mw, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(),
+            cx.nact.as<int32_t>(), cx.bucket ? cx.row_perm.as<int32_t>() : nullptr);
     };
     if (cx.lane_groups)
         k_compact_groups<<<grid_for(cx.n * kGatherLanes), kBlock, 0, cx.stream>>>(
             cx.n, cx.pos.as<double>(), cx.pos32.as<float4>(), cx.slab_off.as<int64_t>(), cx.row_len.as<int32_t>(),
-            cx.nbr.as<int32_t>(), rc2, lo, hi, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(), cx.nact.as<int32_t>());
+            cx.nbr.as<int32_t>(), rc2, lo, hi, cx.mw, cx.amask.as<uint32_t>(), cx.act_n.as<int32_t>(),
+            cx.nact.as<int32_t>());
     else if (cx.nt) launch(std::true_type{});
     else launch(std::false_type{});
     MPNN_HIP(hipGetLastError());
@@ -1485,7 +1506,7 @@ Status fork_transpose(Context &cx) {
     }
     if (cx.E > 0) {
         k_transpose_active<<<grid_for((cx.E + kTPer - 1) / kTPer), kBlock, 0, s>>>(
-            cx.E, cx.n, cx.tjb, cx.t_eid.as<uint32_t>(), cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
+            cx.E, cx.n, cx.tjb, cx.mw, cx.t_eid.as<uint32_t>(), cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
             cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }

@@ -121,7 +121,8 @@ struct Context {
     Buf Gc;       // float [T][NN][K]  dE/dc^t (layers 1..T-1)
     Buf gedge;    // float [E][3]  dE/dr_e summed over layers
     Buf w;        // float [E][K]  per-edge dE/dc contribution of the current layer
-    Buf amask;    // uint32 [mw][n]: bit j%32 of word j/32 = entry j of the row is active (d < rc)
+    Buf amask;    // uint32 [mw + 1][n]: bit j%32 of word j/32 = entry j of the row is active (d < rc);
+                  // word mw: byte w - 1 = active entries in words 0 .. w - 1 (w = 1, 2, 3)
     Buf act_n;    // int32 [E]: sender node of each active slot
     Buf t_act;    // int32 [E]: active slot of each transposed entry this step (-1: d >= rc)
     Buf dact;     // float [T-1][n][2H]: silu' of both hidden layers of each message network (fp32 mode)

@@ -747,7 +747,7 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     MPNN_TRY(cx.grow(cx.grho, sizeof(float) * (size_t)cx.T * np1 * cx.DP));
     MPNN_TRY(cx.grow(cx.Gc, sizeof(float) * (size_t)cx.T * NN1 * cx.K));
     MPNN_TRY(cx.grow(cx.pos32, sizeof(float4) * NN1));
-    MPNN_TRY(cx.grow(cx.amask, sizeof(uint32_t) * (size_t)cx.mw * n1));
+    MPNN_TRY(cx.grow(cx.amask, sizeof(uint32_t) * (size_t)(cx.mw + 1) * n1));
     MPNN_TRY(cx.grow(cx.t_act, sizeof(int32_t) * E1));
     if (cx.precision == 0 && cx.T > 1)
         MPNN_TRY(cx.grow(cx.dact, sizeof(float) * (size_t)(cx.T - 1) * n1 * 2 * cx.H));
