@@ -31,11 +31,13 @@ __device__ __forceinline__ void sincos_half_pi(float v, float &s, float &c) {
                                                  1.0f / 40320.0f), -1.0f / 720.0f), 1.0f / 24.0f), -0.5f), 1.0f);
 }
 
-// Edge basis of one edge, fp32, from the fp64 displacement: hardware exp2 of a pre-scaled
-// argument for the Gaussians, correctly rounded sqrt and 1/d, and the cutoff written as
+// Edge basis of one edge for the reverse pass (forces only), fp32, from the fp64 displacement:
+// hardware exp2 of a pre-scaled argument for the Gaussians, the hardware square root and reciprocal
+// for d and 1/d (one ulp each, about 1e-7 relative in an edge's force terms; the correctly rounded
+// forms cost 1.2 % more time in the reverse pass), and the cutoff written as
 // f_c = (1 + cos(pi v))/2 = cos^2(pi v/2), f_c' = -(pi/rc) sin(pi v/2) cos(pi v/2), which has no
-// cancellation near rc.  (The hardware sqrt and cos/sin shifted the total energy by several
-// 1e-6 relative.)
+// cancellation near rc.  (In the orbital sums, which set the energy, the hardware sqrt and cos/sin
+// shifted the total energy by several 1e-6 relative; those use BasisHP below.)
 // CT: the contraction variant, orbital n from sum_k C[n][k] R_k (and its derivative), in fp32.
 template <int K, int L, bool CT = false>
 struct Basis {
@@ -47,8 +49,8 @@ struct Basis {
                                          const float *mu) {
         constexpr Mono<L> mono;
         rx = (float)dx; ry = (float)dy; rz = (float)dz;
-        const float d = sqrtf(rx * rx + ry * ry + rz * rz);
-        inv_d = 1.0f / d;
+        const float d = __builtin_amdgcn_sqrtf(rx * rx + ry * ry + rz * rz);
+        inv_d = __builtin_amdgcn_rcpf(d);
         // x / rc as a refined quotient (no bias from rounding 1/rc)
         const float rc = md->rc, ir = md->inv_rc;
         auto div_rc = [rc, ir](float x) {
