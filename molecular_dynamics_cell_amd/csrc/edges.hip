@@ -922,7 +922,8 @@ __device__ __forceinline__ void edge_vjp(const B &b, const float *cv, const floa
     g[2] = fmaf(sd, b.rz, ga[2] * ir);
 }
 
-// C0U: layer 0 of a one-species model (see k_aggregate): the messages come from the model constants.
+// C0U: layer 0 of a one-species model (see k_aggregate): the messages come from the model constants,
+// folded into the row's dE/dO (no per-edge message products).
 // WIN > 0: a window of node records staged in LDS per block, as in k_aggregate.
 template <int K, int L, bool FIRST, bool WANT_W, bool CT, bool NT, int LANES, bool C0U = false, int WIN = 0>
 __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, int64_t np, const double *__restrict__ pos,
@@ -968,10 +969,14 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
     const double xi = pos[3 * ir_], yi = pos[3 * ir_ + 1], zi = pos[3 * ir_ + 2];
     float G[K][M];
     assemble_go_row<K, L>(Grho, Ot, np, ir_, G);
-    float c0u[K];
     if constexpr (C0U) {
+        // uniform messages: C0[k] folds into the row's dE/dO once, and every edge takes c_v = 1
 #pragma unroll
-        for (int k = 0; k < K; ++k) c0u[k] = md->c0[k];
+        for (int k = 0; k < K; ++k) {
+            const float c0k = md->c0[k];
+#pragma unroll
+            for (int m = 0; m < M; ++m) G[k][m] *= c0k;
+        }
     }
     double F[3] = {0.0, 0.0, 0.0};
     const int64_t b0 = sell_base(slab_off, ir_);
@@ -995,7 +1000,7 @@ __global__ __launch_bounds__(256) void k_backward_layer(int64_t n, int64_t NN, i
             read_record<K, !C0U>(c + v * rec_stride(K), px, py, pz, cv);   // the record array
         if constexpr (C0U) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) cv[k] = c0u[k];
+            for (int k = 0; k < K; ++k) cv[k] = 1.0f;
         }
         Basis<K, L, CT> b;
         b.eval(__dsub_rn(px, xi), __dsub_rn(py, yi), __dsub_rn(pz, zi), md, mu);
