@@ -162,7 +162,9 @@ mpnn_status mpnn_set_allocator(mpnn_ctx *ctx, void *(*alloc)(size_t bytes, void 
  * Verlet list of every pair with d^2 < (rc + skin)^2 evaluated in fp64 as
  * (dx*dx + dy*dy) + dz*dz, its sender-major transpose, and the per-species atom groups.
  * rc must equal the model's rc.  Velocities are reset to zero (see mpnn_set_state).
- * Errors: E_INVALID_ARG, E_BOX (box edge <= rc + skin), E_CAPACITY, E_OOM, E_HIP. */
+ * Errors: E_INVALID_ARG, E_BOX (box edge <= rc + skin), E_CAPACITY (more than 2^31 - 1 list entries
+ * or slots, or more than 2^(32-b) atoms when the longest row holds up to 2^b entries: 33,554,432
+ * atoms for rows of at most 128), E_OOM, E_HIP. */
 mpnn_status mpnn_build_neighbors(mpnn_ctx *ctx, const double *pos, const int32_t *types,
                                  int64_t n, const double box[3], double rc, double skin);
 

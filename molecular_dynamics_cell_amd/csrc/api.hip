@@ -115,7 +115,7 @@ void Context::release(Buf &b) {
 Context::~Context() {
     if (stream) (void)hipStreamSynchronize(stream);
     Buf *all[] = {&weights, &weights64, &weights16, &ghost_sub, &row_perm, &model, &perm, &inv_perm, &pos, &pos32, &vel, &ref, &types, &ghost_owner, &ghost_code,
-                  &ghost_off, &row_off, &row_len, &slab_off, &nbr, &cellpos, &t_off, &blk_slab, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
+                  &ghost_off, &row_off, &row_len, &slab_off, &nbr, &cellpos, &t_off, &t_eid, &sp_list, &sp_off, &c, &O, &feat, &grho, &Gc,
                   &gedge, &w, &amask, &act_n, &t_act, &dact, &nact, &Frecv, &F, &Ei, &red, &flag, &tmp_a, &tmp_b, &tmp_c,
                   &tmp_d, &tmp_scan,
                   &types_caller, &stage_pos, &stage_vel, &bak_pos, &bak_vel, &bak_F};

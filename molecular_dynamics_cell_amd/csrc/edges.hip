@@ -1160,8 +1160,7 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
 }
 
 // t_act: the active slot (or -1) of every transposed entry under this step's compaction.  Each
-// entry holds its receiver row and column, packed as (row << jb) | column (jb > 0), or its slot,
-// whose row follows from the slab of its 64-slot run (jb = 0).  The active slot is the row base plus
+// entry holds its receiver row and column, packed as (row << jb) | column.  The active slot is the row base plus
 // 64 times the active entries before the entry: the set bits below it in its activity word plus,
 // for rows of at most four words, the count of the earlier words that the compaction stores in the
 // row's extra mask word (longer rows add the earlier words' bits up).  Each thread takes kTPer
@@ -1170,7 +1169,6 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
 constexpr int kTPer = 4;
 __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, int jb, int mw,
                                                           const uint32_t *__restrict__ t_ent,
-                                                          const int32_t *__restrict__ blk_slab,
                                                           const int64_t *__restrict__ slab_off,
                                                           const uint32_t *__restrict__ amask,
                                                           int32_t *__restrict__ t_act) {
@@ -1185,16 +1183,9 @@ __global__ __launch_bounds__(256) void k_transpose_active(int64_t E, int64_t n, 
     int j[kTPer];
 #pragma unroll
     for (int p = 0; p < kTPer; ++p) {
-        if (jb > 0) {
-            r[p] = ent[p] >> jb;
-            j[p] = (int)(ent[p] & ((1u << jb) - 1u));
-            b[p] = sell_base(slab_off, r[p]);
-        } else {
-            const int64_t e = ent[p];
-            r[p] = (int64_t)blk_slab[e / kSlab] * kSlab + e % kSlab;
-            b[p] = sell_base(slab_off, r[p]);
-            j[p] = (int)((e - b[p]) / kSlab);
-        }
+        r[p] = ent[p] >> jb;
+        j[p] = (int)(ent[p] & ((1u << jb) - 1u));
+        b[p] = sell_base(slab_off, r[p]);
     }
     uint32_t word[kTPer], pre[kTPer];
 #pragma unroll
@@ -1513,7 +1504,7 @@ Status fork_transpose(Context &cx) {
     }
     if (cx.E > 0) {
         k_transpose_active<<<grid_for((cx.E + kTPer - 1) / kTPer), kBlock, 0, s>>>(
-            cx.E, cx.n, cx.tjb, cx.mw, cx.t_eid.as<uint32_t>(), cx.blk_slab.as<int32_t>(), cx.slab_off.as<int64_t>(),
+            cx.E, cx.n, cx.tjb, cx.mw, cx.t_eid.as<uint32_t>(), cx.slab_off.as<int64_t>(),
             cx.amask.as<uint32_t>(), cx.t_act.as<int32_t>());
         MPNN_HIP(hipGetLastError());
     }

@@ -84,7 +84,7 @@ struct Context {
     int64_t n = 0, G = 0, NN = 0, E = 0, E_sell = 0;
     int64_t np = 0;             // n rounded up to whole 256-row blocks (column-tiled vectors)
     int mw = 1;                 // activity-mask words per row (longest row / 32, rounded up)
-    int tjb = 0;                // transposed entries hold (row << tjb | column) when > 0, else the slot
+    int tjb = 1;                // transposed entries hold (row << tjb) | column
     double box[3] = {0, 0, 0};
     double skin = 0, rcut = 0;
     int sub[3] = {1, 1, 1};     // virtual subdomains per axis (the next build applies them)
@@ -110,7 +110,6 @@ struct Context {
     Buf nbr;                        // int32 [E_sell] sender node of each entry (sliced ELLPACK)
     Buf cellpos;                    // float4 [NN]: fp32 node positions in grid-cell order (build only)
     Buf t_off, t_eid;               // int64 [NN+1], int32 [E]: sender-major segments, slot of each entry
-    Buf blk_slab;                   // int32 [E_sell/64]: slab of each run of 64 slots (slot -> receiver row)
     Buf sp_list, sp_off;            // int32 [n], int64 [S+1]
 
     // per-evaluation buffers

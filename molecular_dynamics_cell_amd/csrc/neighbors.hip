@@ -346,9 +346,9 @@ __global__ void k_rows(int64_t n, const double *__restrict__ pos, Grid g,
 
 // Sort keys of the sender-major transpose: for every neighbour slot (the slab layout, padding slots
 // included) the sender node, or NN for a padding slot past its row's length; values = the slot.
-// Sort keys and values of every slab slot: key = the sender (NN for padding), value = the slot
-// itself, or, when jb > 0, the receiver row and the slot's column packed as (row << jb) | column, so
-// that the per-step map build (k_transpose_active) reads the row without a lookup.
+// Sort keys and values of every slab slot: key = the sender (NN for padding), value = the receiver
+// row and the slot's column packed as (row << jb) | column, so that the per-step map build
+// (k_transpose_active) reads the row without a lookup.
 __global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ slab_off, const int32_t *__restrict__ len,
                         const int32_t *__restrict__ nbr, uint32_t NN, int jb, uint32_t *__restrict__ keys,
                         uint32_t *__restrict__ vals) {
@@ -360,7 +360,7 @@ __global__ void k_tkeys(int64_t nslab, int64_t n, const int64_t *__restrict__ sl
     for (int64_t j = 0; j < w; ++j) {
         const int64_t e = b + kSlab * j;
         keys[e] = j < nl ? (uint32_t)nbr[e] : NN;
-        vals[e] = jb > 0 ? ((uint32_t)i << jb) | (uint32_t)j : (uint32_t)e;
+        vals[e] = ((uint32_t)i << jb) | (uint32_t)j;
     }
 }
 
@@ -371,14 +371,6 @@ __global__ void k_tsegments(int64_t E, const uint32_t *__restrict__ keys, int64_
     const int64_t prev = p > 0 ? (int64_t)keys[p - 1] : -1;
     const int64_t next = p < E ? (int64_t)keys[p] : NN;
     for (int64_t v = prev + 1; v <= next; ++v) t_off[v] = p;
-}
-
-// Slab of every run of 64 slots: slab s owns the runs slab_off[s]/64 .. slab_off[s+1]/64 - 1, and
-// slot e of it belongs to row 64 s + e % 64 (slab offsets are multiples of 64).
-__global__ void k_blk_slab(int64_t nslab, const int64_t *__restrict__ slab_off, int32_t *__restrict__ blk_slab) {
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= nslab) return;
-    for (int64_t q = slab_off[s] / kSlab; q < slab_off[s + 1] / kSlab; ++q) blk_slab[q] = (int32_t)s;
 }
 
 // Width of each 64-row slab (its longest row), times 64.
@@ -638,11 +630,14 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
             slots += w;
         }
         cx.mw = (int)std::max<int64_t>(1, (longest + 31) / 32);
-        // transposed entries as (row, column) in 32 bits when both fit (2.05M rows of at most
-        // 128 columns: 21 + 7 bits)
+        // transposed entries hold (row, column) in 32 bits (2.05M rows of at most 128 columns:
+        // 21 + 7 bits; at most 2^25 rows of 128 columns, 2^24 of 256)
         int jb = 1;
         while (((int64_t)1 << jb) < longest) ++jb;
-        cx.tjb = n <= ((int64_t)1 << (32 - jb)) ? jb : 0;
+        if (n > ((int64_t)1 << (32 - jb)))
+            return Status::err(MPNN_E_CAPACITY, "too many atoms for the longest neighbour row (" + std::to_string(longest) +
+                                                    " entries): at most " + std::to_string((int64_t)1 << (32 - jb)));
+        cx.tjb = jb;
         // ragged rows (slabs less than 85 % full, e.g. a gas with clusters): the row kernels take
         // each block's rows by descending active count, so a wave's rows have similar lengths.  The
         // reordering scatters the rows' per-edge stores and spreads a wave over four slabs, so it
@@ -674,7 +669,6 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
     // ---- sender-major transpose: for every node, the edges it sends, in edge order ----
     cx.prof_begin(kProfBuildTranspose);
     MPNN_TRY(cx.grow(cx.t_off, sizeof(int64_t) * (NN1 + 1)));
-    MPNN_TRY(cx.grow(cx.blk_slab, sizeof(int32_t) * (size_t)(E1 / kSlab + 1)));
     MPNN_TRY(cx.grow(cx.t_eid, sizeof(int32_t) * E1));
     // a stable radix sort of (sender node, slot) pairs in slot order: each sender's segment lists
     // its slots in ascending order, so the transposed order (and every sum over it) is fixed.
@@ -702,14 +696,6 @@ Status build_neighbors(Context &cx, const double *pos_caller, const int32_t *typ
         }
         k_tsegments<<<grid_for(E + 1), kBlock, 0, cx.stream>>>(E, skeys, cx.NN, cx.t_off.as<int64_t>());
         MPNN_HIP(hipGetLastError());
-    }
-    {
-        const int64_t nslab_all = (n + kSlab - 1) / kSlab;
-        if (nslab_all > 0 && cx.tjb == 0) {   // slot -> slab of its run, for unpacked entries
-            k_blk_slab<<<grid_for(nslab_all), kBlock, 0, cx.stream>>>(nslab_all, cx.slab_off.as<int64_t>(),
-                                                                      cx.blk_slab.as<int32_t>());
-            MPNN_HIP(hipGetLastError());
-        }
     }
 
     cx.prof_end(kProfBuildTranspose);
