@@ -1160,10 +1160,10 @@ __global__ __launch_bounds__(256) void k_gather_w(int64_t NN, const int64_t *__r
 }
 
 // t_act: the active slot (or -1) of every transposed entry under this step's compaction.  Each
-// entry holds its receiver row and column, packed as (row << jb) | column.  The active slot is the row base plus
-// 64 times the active entries before the entry: the set bits below it in its activity word plus,
-// for rows of at most four words, the count of the earlier words that the compaction stores in the
-// row's extra mask word (longer rows add the earlier words' bits up).  Each thread takes kTPer
+// entry holds its receiver row and column, packed as (row << jb) | column.  The active slot is the
+// row base plus 64 times the active entries before the entry: the set bits below it in its
+// activity word plus, for rows of at most four words, the count of the earlier words that the
+// compaction stores in the row's extra mask word (longer rows add the earlier words' bits up).  Each thread takes kTPer
 // entries a block apart and requests all their lookups (row base, activity and count words) before
 // using any, so the build keeps few waves busy while it runs beside the forward layers.
 constexpr int kTPer = 4;
