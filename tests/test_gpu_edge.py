@@ -205,3 +205,31 @@ def test_row_bucketing_decision():
     assert inf["row_bucketing"] == 0 and inf["n_edges"] / inf["n_slots"] >= 0.85, inf
     inf = gpu_model(I.make_params(5), I.make_system(5, reduced=True)).info()
     assert inf["row_bucketing"] == 0, inf
+
+
+def test_long_rows_one_row_per_lane():
+    """Dense rows on the large-system path: liquid water at 1 g/cm3 in a doubled box (36,864 atoms,
+    about 147 list entries per row within rc + skin).  Above 32,768 atoms every row takes one lane;
+    rows longer than 128 entries need more than four activity words (the per-step transposed map
+    then counts the earlier words' bits instead of reading the row's stored counts) and eight bits
+    of column in each transposed entry; with 4M entries or more the map is built on the second
+    stream.  Pair sets bit-exact and the energy, forces and per-atom energies within their gates
+    against the oracle; a second evaluation gives the same bits."""
+    from tests.gpu_util import check_ei
+    s = I.water(24, 12288, 71.6, seed=1002)
+    p = I.make_params(2)
+    m = gpu_model(p, s)
+    inf = m.info()
+    assert inf["n_local"] == 36864 and inf["n_edges"] >= 4_000_000, inf
+    gi, gj, gs = (t.cpu().numpy() for t in m.get_pairs())
+    longest = int(np.bincount(gi, minlength=s.n).max())
+    assert longest > 128, longest
+    pos = oracle.wrap(s.pos, s.box)
+    pl = oracle.pairs(pos, s.box, p.spec.rc + p.spec.skin)
+    assert np.array_equal(canonical_pairs(gi, gj, gs, s.n), canonical_pairs(*pl, s.n))
+    E, F, Ei = m.energy_forces(atom_energy=True)
+    E2, F2, _ = m.energy_forces()
+    assert E2 == E and torch.equal(F2, F)
+    Eo, Fo, Eio = oracle.energy_forces(oracle.Model(p), pos, s.types, s.box, pair_list=pl)
+    check_ei(Ei.cpu().numpy(), Eio, label=f"water36864 (longest row {longest}) E_i")
+    check_ef(E, F.cpu().numpy(), Eo, Fo, label=f"water36864 (longest row {longest})")
