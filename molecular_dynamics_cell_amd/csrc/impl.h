@@ -109,7 +109,7 @@ struct Context {
     Buf slab_off;                   // int64 [n/64+2] start of each 64-row slab
     Buf nbr;                        // int32 [E_sell] sender node of each entry (sliced ELLPACK)
     Buf cellpos;                    // float4 [NN]: fp32 node positions in grid-cell order (build only)
-    Buf t_off, t_eid;               // int64 [NN+1], int32 [E]: sender-major segments, slot of each entry
+    Buf t_off, t_eid;               // int64 [NN+1], uint32 [E]: sender-major segments, (row << tjb) | column of each entry
     Buf sp_list, sp_off;            // int32 [n], int64 [S+1]
 
     // per-evaluation buffers
@@ -212,10 +212,10 @@ Status aggregate(Context &cx, int t);
 Status refresh_ghost_features(Context &cx, int t);
 Status backward_layer(Context &cx, int t);        // per-edge w_e and dE/dr_e of layer t
 Status assemble_go(Context &cx, int t, float *out);  // dE/dO^t [n][K*M] (diagnostics)
-Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (t = T-1 builds t_act)
+Status backward_messages(Context &cx, int t);     // dE/dc^t of all nodes + ghost fold (reads t_act)
 // t_act (the active slot of every transposed entry) for this step: on the side stream, forked from
-// the context's stream after the compaction, for long lists (Context::side), else on the context's
-// stream; join_transpose makes the context's stream wait for the side stream
+// the context's stream after the first aggregation, for long lists (Context::side), else on the
+// context's stream; join_transpose makes the context's stream wait for the side stream
 Status fork_transpose(Context &cx);
 Status join_transpose(Context &cx);
 Status force_gather(Context &cx, double *F_caller);
